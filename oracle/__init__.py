@@ -1,0 +1,189 @@
+"""CPU oracle for the tree draft-and-verify step -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and its
+Python binding) never imports, loads or calls anything here, and this package
+imports nothing from the product.
+
+The arithmetic lives in ``jt_oracle.c`` (plain single-threaded C11, fp64); this
+module compiles it with gcc and marshals numpy arrays to it.  bfloat16 tensors
+travel as raw ``uint16`` words.
+
+Pins (tests that hold the oracle to something other than itself) are in
+``tests/test_oracle_*.py``.  No oracle function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "jt_oracle.c")
+_LIB = os.path.join(_HERE, "libjt_oracle.so")
+
+# per-sequence flags, restated from the C file
+BAD_PARENT = 1
+DEPTH_GT_N = 2
+BAD_BLOCK = 4
+NAN = 8
+BAD_PREFIX = 16
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile jt_oracle.c into libjt_oracle.so with gcc (no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off",
+                        "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle takes float32 or bf16-as-uint16, got {a.dtype}")
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def build_mask(parent: np.ndarray):
+    """parent int32 [S,B] -> (vis uint8 [S,B,B], depth int32 [S,B], err int32 [S])."""
+    parent = _c(parent, np.int32)
+    S, B = parent.shape
+    vis = np.zeros((S, B, B), np.uint8)
+    depth = np.zeros((S, B), np.int32)
+    err = np.zeros(S, np.int32)
+    rc = _load().jto_build_mask(_p(parent), S, B, _p(vis), _p(depth), _p(err))
+    if rc:
+        raise ValueError(f"jto_build_mask rc={rc}")
+    return vis, depth, err
+
+
+def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, prefix_len, parent, *,
+                   block_table=None, block_size=16, num_blocks=0, max_prefix=None,
+                   scale=0.0, sel=None):
+    """Tree-causal GQA attention in fp64.
+
+    q [S,B,Hq,d]; k_tree, v_tree [S,B,Hkv,d]; contiguous prefix [S,Pmax,Hkv,d] or,
+    with ``block_table`` [S,maxblk], a pool [nblk,block_size,Hkv,d].
+    ``sel``: optional int array [n,3] of (s, v, h) rows to compute.
+    Returns (out float64, lse float64, err int32[S]); out is [S,B,Hq,d] or [n,d].
+    """
+    dt = _dtype_code(q)
+    for a in (k_tree, v_tree, k_prefix, v_prefix):
+        if a.dtype != q.dtype:
+            raise TypeError("all tensors must share one dtype")
+    q, k_tree, v_tree = _c(q, q.dtype), _c(k_tree, q.dtype), _c(v_tree, q.dtype)
+    k_prefix, v_prefix = _c(k_prefix, q.dtype), _c(v_prefix, q.dtype)
+    S, B, Hq, d = q.shape
+    Hkv = k_tree.shape[2]
+    prefix_len = _c(prefix_len, np.int32)
+    parent = _c(parent, np.int32)
+    if block_table is None:
+        bt, maxblk = None, 0
+        Pmax = k_prefix.shape[1] if max_prefix is None else max_prefix
+        nblk = 0
+    else:
+        bt = _c(block_table, np.int32)
+        maxblk = bt.shape[1]
+        Pmax = maxblk * block_size if max_prefix is None else max_prefix
+        nblk = num_blocks if num_blocks else k_prefix.shape[0]
+    if sel is None:
+        nsel, selp = 0, None
+        out = np.zeros((S, B, Hq, d), np.float64)
+        lse = np.zeros((S, B, Hq), np.float64)
+    else:
+        sel = _c(sel, np.int32).reshape(-1, 3)
+        nsel, selp = sel.shape[0], sel
+        out = np.zeros((nsel, d), np.float64)
+        lse = np.zeros(nsel, np.float64)
+    err = np.zeros(S, np.int32)
+    lib = _load()
+    lib.jto_tree_attention.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 3 + [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 6 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]
+    rc = lib.jto_tree_attention(_p(q), _p(k_tree), _p(v_tree), _p(k_prefix), _p(v_prefix),
+                                _p(bt), maxblk, block_size, nblk, _p(prefix_len), Pmax,
+                                _p(parent), S, B, Hq, Hkv, d, dt, float(scale), nsel,
+                                _p(selp), _p(out), _p(lse), _p(err))
+    if rc:
+        raise ValueError(f"jto_tree_attention rc={rc}")
+    return out, lse, err
+
+
+def topw(logits, W: int, rows: int | None = None, V: int | None = None, row_stride=None):
+    """Per-row top-W ids (value desc, id asc), fp64 log-probs and row LSE.
+
+    ``logits`` is a 2-D array [rows, row_stride]; ``V`` defaults to its width.
+    """
+    dt = _dtype_code(logits)
+    logits = np.ascontiguousarray(logits)
+    R, stride = logits.shape
+    rows = R if rows is None else rows
+    V = stride if V is None else V
+    row_stride = stride if row_stride is None else row_stride
+    ids = np.zeros((rows, W), np.int32)
+    lp = np.zeros((rows, W), np.float64)
+    lse = np.zeros(rows, np.float64)
+    lib = _load()
+    lib.jto_topw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p]
+    rc = lib.jto_topw(_p(logits), row_stride, rows, V, W, dt, _p(ids), _p(lp), _p(lse))
+    if rc:
+        raise ValueError(f"jto_topw rc={rc}")
+    return ids, lp, lse
+
+
+def verify_greedy(target_logits, parent, tokens, N: int, V=None):
+    """Greedy verification.  target_logits [S*B, stride] (or [S,B,stride]); parent,
+    tokens [S,B]; the first ``V`` entries of each row are the vocabulary.
+
+    Returns dict(accept_len [S], accept_path [S,N+1], bonus [S], argmax [S,B], err [S]).
+    """
+    parent = _c(parent, np.int32)
+    tokens = _c(tokens, np.int32)
+    S, B = parent.shape
+    dt = _dtype_code(target_logits)
+    tl = np.ascontiguousarray(target_logits).reshape(S * B, -1)
+    row_stride = tl.shape[1]
+    V = row_stride if V is None else V
+    out = dict(accept_len=np.zeros(S, np.int32), accept_path=np.zeros((S, N + 1), np.int32),
+               bonus=np.zeros(S, np.int32), argmax=np.zeros((S, B), np.int32),
+               err=np.zeros(S, np.int32))
+    lib = _load()
+    lib.jto_verify_greedy.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int] + \
+        [ctypes.c_void_p] * 5
+    rc = lib.jto_verify_greedy(_p(tl), row_stride, V, dt, _p(parent), _p(tokens), S, B, N,
+                               _p(out["accept_len"]), _p(out["accept_path"]),
+                               _p(out["bonus"]), _p(out["argmax"]), _p(out["err"]))
+    if rc:
+        raise ValueError(f"jto_verify_greedy rc={rc}")
+    return out

@@ -1,0 +1,420 @@
+/*
+ * jt_oracle.c -- CPU oracle for one draft-and-verify step over a token tree.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Plain, slow, single-threaded C11.  Every floating-point input is widened to
+ * double (bf16 -> float is exact, float -> double is exact) and every result is
+ * computed and returned in double.  Masks are dense, sorts are full sorts, and
+ * softmax is the two-pass max-subtracted textbook form.  No blocking, fusion or
+ * reordering beyond what the definitions state.
+ *
+ * Sources (the JetSpec pages):
+ *  - tree-causal mask: M[v,u] = 0 iff u is an ancestor of v or v itself,
+ *    -inf otherwise ("How it works", mask equation, startedourmission.github.io
+ *    review of JetSpec); nodes see the prefix, their ancestors and themselves,
+ *    never siblings or descendants (paperlayer.ai JetSpec summary, section 2
+ *    "Architecture").
+ *  - verification uses parent indices, depths and the tree mask in one pass
+ *    (paperlayer.ai JetSpec summary, appendix E "Verification").
+ *  - per-position top-k tokens and log-probabilities (same page, appendix E
+ *    "Drafting"); top-W per depth (paper.rainbus.top summary, method steps).
+ *  - acceptance of the longest valid prefix plus a bonus token (paperlayer.ai
+ *    JetSpec summary section 2; JetSpec++ summary section 3); at temperature 0
+ *    the min(1, p/q) rule of the review's inference section reduces to
+ *    "draft token equals the target argmax" (point-mass proposal, JetSpec++
+ *    summary appendix F.3).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - node 0 is the tree root and is counted in B; parent[0] = -1 and
+ *    0 <= parent[i] < i for i >= 1, anything else is a bad parent array;
+ *  - softmax scale 1/sqrt(d) when the caller passes scale <= 0;
+ *  - query head h reads KV head h / (Hq/Hkv) (contiguous GQA groups);
+ *  - top-W order is value descending, token id ascending; -0 equals +0;
+ *    NaN ranks below -inf;
+ *  - argmax ties go to the lowest token id; NaN entries are skipped and flagged;
+ *  - among accepted nodes the deepest wins, ties to the lowest node index.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* device-style per-sequence flags (same meaning as the library's, values
+ * restated here on purpose: the oracle includes no library header) */
+#define ORA_BAD_PARENT 1
+#define ORA_DEPTH_GT_N 2
+#define ORA_BAD_BLOCK 4
+#define ORA_NAN 8
+#define ORA_BAD_PREFIX 16
+
+/* element types: 0 = IEEE float32, 1 = bfloat16 stored as raw 16-bit words */
+static double elem(const void *base, int64_t i, int dtype)
+{
+    if (dtype == 0)
+        return (double)((const float *)base)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int jto_version(void) { return 1; }
+
+/* ---------------------------------------------------------------- mask -- */
+
+/* Checks the parent-array layout of one sequence.  Returns 1 when valid. */
+static int parents_valid(const int32_t *par, int B)
+{
+    if (B < 1 || par[0] != -1)
+        return 0;
+    for (int i = 1; i < B; i++)
+        if (par[i] < 0 || par[i] >= i)
+            return 0;
+    return 1;
+}
+
+/*
+ * Dense tree-causal visibility and depths.
+ *   vis[s][v][u] = 1 iff u in Anc(v) or u == v (walk parents up to the root),
+ *   depth[s][v]  = number of parent steps from v to the root.
+ * A sequence with a bad parent array gets ORA_BAD_PARENT in err[s], an
+ * all-zero vis block and depth -1 everywhere.
+ */
+int jto_build_mask(const int32_t *parent, int S, int B, uint8_t *vis,
+                   int32_t *depth, int32_t *err)
+{
+    if (S < 0 || B < 1)
+        return 2;
+    for (int s = 0; s < S; s++) {
+        const int32_t *par = parent + (int64_t)s * B;
+        uint8_t *V = vis + (int64_t)s * B * B;
+        int32_t *dep = depth + (int64_t)s * B;
+        memset(V, 0, (size_t)B * B);
+        if (!parents_valid(par, B)) {
+            err[s] = ORA_BAD_PARENT;
+            for (int v = 0; v < B; v++)
+                dep[v] = -1;
+            continue;
+        }
+        err[s] = 0;
+        for (int v = 0; v < B; v++) {
+            int steps = 0;
+            for (int u = v; u != -1; u = par[u]) {
+                V[(int64_t)v * B + u] = 1;
+                steps++;
+            }
+            dep[v] = steps - 1;
+        }
+    }
+    return 0;
+}
+
+/* ----------------------------------------------------------- attention -- */
+
+/*
+ * Tree-causal GQA attention of all B tree nodes of each sequence against that
+ * sequence's prefix KV and the tree's own KV.
+ *
+ * For sequence s, node v, query head h (KV head g = h / (Hq/Hkv)):
+ *   score_j = scale * <q[s,v,h], k_prefix[s,j,g]>            j < prefix_len[s]
+ *   score_u = scale * <q[s,v,h], k_tree[s,u,g]> + M[v,u]     u < B
+ *   out     = sum_j softmax(score)_j * value_j,  lse = log sum_j exp(score_j)
+ * with M from jto_build_mask (0 visible, -inf hidden, exp(-inf) = 0 exactly).
+ *
+ * Prefix layout: block_table == NULL -> contiguous [S, max_prefix, Hkv, d];
+ * otherwise a pool [num_blocks, block_size, Hkv, d] where logical key j of
+ * sequence s lives in block block_table[s*max_blocks + j/block_size], slot
+ * j % block_size.  Keys of a block id outside [0, num_blocks) are skipped and
+ * flagged ORA_BAD_BLOCK; prefix_len outside [0, max_prefix] is flagged
+ * ORA_BAD_PREFIX and clamped.
+ *
+ * Rows: n_sel == 0 -> every (s, v, h) in that order, out is [S,B,Hq,d];
+ * otherwise the n_sel (s, v, h) triples in sel[], out is [n_sel, d].
+ * Returns 0, or 2 on a shape error.
+ */
+int jto_tree_attention(const void *q, const void *k_tree, const void *v_tree,
+                       const void *k_prefix, const void *v_prefix,
+                       const int32_t *block_table, int max_blocks, int block_size,
+                       int num_blocks, const int32_t *prefix_len, int max_prefix,
+                       const int32_t *parent, int S, int B, int Hq, int Hkv, int d,
+                       int dtype, double scale, int n_sel, const int32_t *sel,
+                       double *out, double *lse, int32_t *err)
+{
+    if (S < 1 || B < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv != 0 || max_prefix < 0)
+        return 2;
+    if (block_table && (block_size < 1 || max_blocks < 0))
+        return 2;
+    const int G = Hq / Hkv;
+    if (scale <= 0.0)
+        scale = 1.0 / sqrt((double)d);
+
+    uint8_t *vis = (uint8_t *)malloc((size_t)S * B * B);
+    int32_t *dep = (int32_t *)malloc(sizeof(int32_t) * (size_t)S * B);
+    int32_t *merr = (int32_t *)malloc(sizeof(int32_t) * (size_t)S);
+    double *sc = (double *)malloc(sizeof(double) * ((size_t)max_prefix + B));
+    int32_t *kpos = (int32_t *)malloc(sizeof(int32_t) * ((size_t)max_prefix + 1));
+    if (!vis || !dep || !merr || !sc || !kpos) {
+        free(vis); free(dep); free(merr); free(sc); free(kpos);
+        return 3;
+    }
+    jto_build_mask(parent, S, B, vis, dep, merr);
+    for (int s = 0; s < S; s++) {
+        int32_t e = merr[s];
+        int P = prefix_len[s];
+        if (P < 0 || P > max_prefix)
+            e |= ORA_BAD_PREFIX;
+        if (block_table) {
+            int P2 = P < 0 ? 0 : (P > max_prefix ? max_prefix : P);
+            for (int j = 0; j < P2; j += block_size) {
+                int lb = j / block_size;
+                int blk = lb < max_blocks ? block_table[(int64_t)s * max_blocks + lb] : -1;
+                if (blk < 0 || blk >= num_blocks)
+                    e |= ORA_BAD_BLOCK;
+            }
+        }
+        err[s] = e;
+    }
+
+    int64_t nrows = n_sel > 0 ? n_sel : (int64_t)S * B * Hq;
+    for (int64_t r = 0; r < nrows; r++) {
+        int s, v, h;
+        if (n_sel > 0) {
+            s = sel[3 * r]; v = sel[3 * r + 1]; h = sel[3 * r + 2];
+        } else {
+            s = (int)(r / ((int64_t)B * Hq));
+            v = (int)((r / Hq) % B);
+            h = (int)(r % Hq);
+        }
+        int g = h / G;
+        int P = prefix_len[s];
+        if (P < 0) P = 0;
+        if (P > max_prefix) P = max_prefix;
+        const int64_t qoff = (((int64_t)s * B + v) * Hq + h) * d;
+
+        /* physical row index of each logical prefix key, -1 when skipped */
+        for (int j = 0; j < P; j++) {
+            if (!block_table) {
+                kpos[j] = j;
+            } else {
+                int lb = j / block_size;
+                int blk = lb < max_blocks ? block_table[(int64_t)s * max_blocks + lb] : -1;
+                kpos[j] = (blk < 0 || blk >= num_blocks) ? -1 : blk * block_size + j % block_size;
+            }
+        }
+        /* pass 0: scores */
+        int nk = P + B;
+        for (int j = 0; j < P; j++) {
+            if (kpos[j] < 0) { sc[j] = -INFINITY; continue; }
+            int64_t koff = block_table ? ((int64_t)kpos[j] * Hkv + g) * d
+                                       : (((int64_t)s * max_prefix + j) * Hkv + g) * d;
+            double acc = 0.0;
+            for (int c = 0; c < d; c++)
+                acc += elem(q, qoff + c, dtype) * elem(k_prefix, koff + c, dtype);
+            sc[j] = scale * acc;
+        }
+        const uint8_t *mrow = vis + ((int64_t)s * B + v) * B;
+        for (int u = 0; u < B; u++) {
+            int64_t koff = (((int64_t)s * B + u) * Hkv + g) * d;
+            double acc = 0.0;
+            for (int c = 0; c < d; c++)
+                acc += elem(q, qoff + c, dtype) * elem(k_tree, koff + c, dtype);
+            sc[P + u] = mrow[u] ? scale * acc : -INFINITY;
+        }
+        /* pass 1: max; pass 2: exp and normaliser */
+        double m = -INFINITY;
+        for (int j = 0; j < nk; j++)
+            if (sc[j] > m) m = sc[j];
+        double Z = 0.0;
+        for (int j = 0; j < nk; j++) {
+            sc[j] = (sc[j] == -INFINITY) ? 0.0 : exp(sc[j] - m);
+            Z += sc[j];
+        }
+        /* pass 3: weighted sum of values */
+        double *o = out + r * d;
+        for (int c = 0; c < d; c++)
+            o[c] = 0.0;
+        for (int j = 0; j < P; j++) {
+            if (sc[j] == 0.0) continue;
+            int64_t voff = block_table ? ((int64_t)kpos[j] * Hkv + g) * d
+                                       : (((int64_t)s * max_prefix + j) * Hkv + g) * d;
+            for (int c = 0; c < d; c++)
+                o[c] += sc[j] * elem(v_prefix, voff + c, dtype);
+        }
+        for (int u = 0; u < B; u++) {
+            if (sc[P + u] == 0.0) continue;
+            int64_t voff = (((int64_t)s * B + u) * Hkv + g) * d;
+            for (int c = 0; c < d; c++)
+                o[c] += sc[P + u] * elem(v_tree, voff + c, dtype);
+        }
+        if (Z > 0.0) {
+            for (int c = 0; c < d; c++)
+                o[c] /= Z;
+            lse[r] = m + log(Z);
+        } else {
+            lse[r] = -INFINITY;
+        }
+    }
+    free(vis); free(dep); free(merr); free(sc); free(kpos);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- top-W -- */
+
+typedef struct { double x; int32_t i; } ora_item;
+
+/* total order: non-NaN before NaN; larger value first; lower id first */
+static int item_cmp(const void *pa, const void *pb)
+{
+    const ora_item *a = (const ora_item *)pa, *b = (const ora_item *)pb;
+    int an = isnan(a->x), bn = isnan(b->x);
+    if (an != bn)
+        return an ? 1 : -1;
+    if (!an) {
+        if (a->x > b->x) return -1;
+        if (a->x < b->x) return 1;
+    }
+    return (a->i > b->i) - (a->i < b->i);
+}
+
+/*
+ * Per row: the W largest logits in (value desc, id asc) order, by a full sort
+ * of the row; lse = m + log(sum exp(x - m)) over the whole row (m = row max);
+ * logprob = x - lse.  Row r starts at logits + r*row_stride elements.
+ * A row whose finite maximum is -inf has lse = -inf.
+ */
+int jto_topw(const void *logits, int64_t row_stride, int rows, int V, int W,
+             int dtype, int32_t *ids, double *logprob, double *lse)
+{
+    if (rows < 0 || V < 1 || W < 1 || W > V || row_stride < V)
+        return 2;
+    ora_item *it = (ora_item *)malloc(sizeof(ora_item) * (size_t)V);
+    if (!it)
+        return 3;
+    for (int r = 0; r < rows; r++) {
+        const int64_t base = (int64_t)r * row_stride;
+        double m = -INFINITY;
+        int has_nan = 0;
+        for (int t = 0; t < V; t++) {
+            it[t].x = elem(logits, base + t, dtype);
+            it[t].i = t;
+            if (isnan(it[t].x)) has_nan = 1;
+            else if (it[t].x > m) m = it[t].x;
+        }
+        double L;
+        if (has_nan) {
+            L = NAN;
+        } else if (m == -INFINITY) {
+            L = -INFINITY;
+        } else {
+            double Z = 0.0;
+            for (int t = 0; t < V; t++)
+                Z += exp(it[t].x - m);
+            L = m + log(Z);
+        }
+        if (lse)
+            lse[r] = L;
+        qsort(it, (size_t)V, sizeof(ora_item), item_cmp);
+        for (int w = 0; w < W; w++) {
+            ids[(int64_t)r * W + w] = it[w].i;
+            logprob[(int64_t)r * W + w] = it[w].x - L;
+        }
+    }
+    free(it);
+    return 0;
+}
+
+/* --------------------------------------------------------------- verify -- */
+
+/* first index of the row maximum by a linear scan; NaN entries are skipped */
+static int32_t row_argmax(const void *logits, int64_t base, int V, int dtype, int *saw_nan)
+{
+    int32_t best_i = -1;
+    double best = 0.0;
+    for (int t = 0; t < V; t++) {
+        double x = elem(logits, base + t, dtype);
+        if (isnan(x)) { *saw_nan = 1; continue; }
+        if (best_i < 0 || x > best) { best = x; best_i = t; }
+    }
+    return best_i < 0 ? 0 : best_i;
+}
+
+/*
+ * Greedy tree verification.
+ *   am[s,v]   = argmax_t target_logits[s,v,t] (lowest id on ties);
+ *   v accepted iff every node u != root on the root path of v has
+ *              tokens[s,u] == am[s,parent[u]];
+ *   v*        = deepest accepted node, lowest index on ties (root is always
+ *              accepted);
+ *   accept_len[s] = depth(v*), accept_path[s,0..N] = root..v* padded with -1,
+ *   bonus[s]  = am[s,v*].
+ * Row (s, v) of the logits starts at (s*B + v)*row_stride elements.
+ * err[s]: ORA_BAD_PARENT, ORA_DEPTH_GT_N (some node deeper than N), ORA_NAN.
+ * A sequence with a bad parent array or a node deeper than N gets
+ * accept_len 0, path [0, -1, ...] and bonus am[s,0].
+ */
+int jto_verify_greedy(const void *target_logits, int64_t row_stride, int V, int dtype,
+                      const int32_t *parent, const int32_t *tokens, int S, int B, int N,
+                      int32_t *accept_len, int32_t *accept_path, int32_t *bonus,
+                      int32_t *argmax, int32_t *err)
+{
+    if (S < 0 || B < 1 || V < 1 || N < 0 || row_stride < V)
+        return 2;
+    for (int s = 0; s < S; s++) {
+        const int32_t *par = parent + (int64_t)s * B;
+        const int32_t *tok = tokens + (int64_t)s * B;
+        int32_t *am = argmax + (int64_t)s * B;
+        int32_t *path = accept_path + (int64_t)s * (N + 1);
+        int flags = 0, saw_nan = 0;
+        for (int v = 0; v < B; v++)
+            am[v] = row_argmax(target_logits, ((int64_t)s * B + v) * row_stride, V, dtype, &saw_nan);
+        if (saw_nan)
+            flags |= ORA_NAN;
+        for (int k = 0; k <= N; k++)
+            path[k] = -1;
+        path[0] = 0;
+        accept_len[s] = 0;
+        bonus[s] = am[0];
+        if (!parents_valid(par, B)) {
+            err[s] = flags | ORA_BAD_PARENT;
+            continue;
+        }
+        int too_deep = 0;
+        for (int v = 0; v < B; v++) {
+            int dv = 0;
+            for (int u = v; par[u] != -1; u = par[u])
+                dv++;
+            if (dv > N)
+                too_deep = 1;
+        }
+        if (too_deep) {
+            err[s] = flags | ORA_DEPTH_GT_N;
+            continue;
+        }
+        int best_v = 0, best_d = 0;
+        for (int v = 0; v < B; v++) {
+            int ok = 1, dv = 0;
+            for (int u = v; par[u] != -1; u = par[u]) {
+                if (tok[u] != am[par[u]])
+                    ok = 0;
+                dv++;
+            }
+            if (ok && dv > best_d) {
+                best_d = dv;
+                best_v = v;
+            }
+        }
+        accept_len[s] = best_d;
+        for (int u = best_v; u != -1; u = par[u]) {
+            int du = 0;
+            for (int w = u; par[w] != -1; w = par[w])
+                du++;
+            path[du] = u;
+        }
+        bonus[s] = am[best_v];
+        err[s] = flags;
+    }
+    return 0;
+}

@@ -1,0 +1,141 @@
+"""Pins for the oracle's greedy tree verification (CPU only).
+
+Verification accepts the longest prefix whose drafted tokens satisfy the
+target's acceptance condition and commits it plus a bonus token (paperlayer.ai
+JetSpec summary, section 2; JetSpec++ summary, section 3; paper.rainbus.top,
+prerequisites).  At temperature 0 the min(1, p/q) rule (JetSpec review,
+startedourmission.github.io, inference) with a point-mass draft (paperlayer.ai
+JetSpec++ summary, appendix F.3) accepts a node iff its token is the target
+argmax at its parent.  With i.i.d. per-token acceptance alpha over N drafted
+tokens the expected number of committed tokens is (1 - alpha^(N+1))/(1 - alpha)
+(review, background; paper.rainbus.top, prerequisites).
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_causal_draft_amd import workload as wl
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _logits_with_argmax(am, V, dtype="f32"):
+    x = np.zeros((len(am), V), np.float32)
+    x[np.arange(len(am)), am] = 1.0
+    return wl.to_dtype(x, dtype)
+
+
+def test_hand_worked_tree7():
+    g = json.load(open(os.path.join(GOLD, "tree7_hand.json")))
+    e = g["expected"]
+    tl = _logits_with_argmax(np.array(g["target_argmax"]), g["vocab"])
+    r = oracle.verify_greedy(tl, np.array([g["parent"]]), np.array([g["tokens"]]), e["N"])
+    assert r["err"][0] == 0
+    assert r["argmax"][0].tolist() == g["target_argmax"]
+    assert r["accept_len"][0] == e["accept_len"]
+    assert r["accept_path"][0].tolist() == e["accept_path"]
+    assert r["bonus"][0] == e["bonus"]
+
+
+def _enumerate(parent, ok, am):
+    """Independent set-based enumeration: accepted nodes grow from the root in index order."""
+    B = len(parent)
+    acc = {0}
+    depth = [0] * B
+    for u in range(1, B):
+        depth[u] = depth[parent[u]] + 1
+        if parent[u] in acc and ok[u]:
+            acc.add(u)
+    best = min(acc, key=lambda v: (-depth[v], v))
+    path = []
+    u = best
+    while u != -1:
+        path.append(u)
+        u = parent[u] if u else -1
+    return depth[best], path[::-1], am[best]
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7])
+def test_exhaustive_tiny_trees_all_patterns(B):
+    """Every parent array (B <= 7) x every accept pattern (2^(B-1)), duplicates allowed."""
+    V = 2 * B + 2
+    pats = list(itertools.product([0, 1], repeat=B - 1))
+    for tail in itertools.product(*[range(i) for i in range(1, B)]):
+        parent = [-1] + list(tail)
+        S = len(pats)
+        par = np.tile(np.array(parent, np.int32), (S, 1))
+        am = np.array([2 * v for v in range(B)])               # target argmax at node v
+        tok = np.zeros((S, B), np.int32)
+        for s, pat in enumerate(pats):
+            for u in range(1, B):
+                tok[s, u] = am[parent[u]] + (0 if pat[u - 1] else 1)
+        tl = np.tile(_logits_with_argmax(am, V), (S, 1))
+        r = oracle.verify_greedy(tl, par, tok, B)
+        assert not r["err"].any()
+        for s, pat in enumerate(pats):
+            L, path, bonus = _enumerate(parent, (1,) + pat, am)
+            assert r["accept_len"][s] == L
+            assert r["accept_path"][s, :L + 1].tolist() == path
+            assert (r["accept_path"][s, L + 1:] == -1).all()
+            assert r["bonus"][s] == bonus
+
+
+@pytest.mark.parametrize("alpha,N", [(0.8, 16), (0.6, 5), (0.95, 12)])
+def test_chain_closed_form_expected_tokens(alpha, N):
+    """Monte Carlo over a chain: E[accept_len + 1] = (1-a^(N+1))/(1-a), P(len>=k) = a^k."""
+    n = 20000
+    rng = np.random.default_rng(int(alpha * 100) + N)
+    ok = rng.random((n, N)) < alpha
+    par = np.tile(wl.chain_tree(N + 1)[0], (n, 1))
+    V = 3
+    am = np.zeros((n, N + 1), np.int64)                      # target argmax: token 0 everywhere
+    tok = np.where(ok, 0, 1).astype(np.int32)                # draft token 0 accepted, 1 rejected
+    tok = np.concatenate([np.full((n, 1), 2, np.int32), tok], 1)
+    tl = _logits_with_argmax(am.reshape(-1), V)
+    r = oracle.verify_greedy(tl, par, tok, N)
+    committed = r["accept_len"] + 1.0
+    expect = (1 - alpha ** (N + 1)) / (1 - alpha)
+    assert abs(committed.mean() - expect) <= 4 * committed.std() / np.sqrt(n)
+    for k in (1, 2, 4):
+        p = (r["accept_len"] >= k).mean()
+        assert abs(p - alpha ** k) <= 4 * np.sqrt(alpha ** k * (1 - alpha ** k) / n)
+
+
+def test_all_none_and_star():
+    B, V = 10, 8
+    par, dep, _ = wl.random_tree(B, 5, 3, np.random.default_rng(2))
+    am = np.arange(B) % V
+    tok_all = np.array([0] + [am[par[u]] for u in range(1, B)], np.int32)
+    tok_none = np.array([0] + [(am[par[u]] + 1) % V for u in range(1, B)], np.int32)
+    tl = _logits_with_argmax(am, V)
+    r = oracle.verify_greedy(tl, par[None], tok_all[None], 5)
+    assert r["accept_len"][0] == dep.max()
+    assert r["accept_path"][0, dep.max()] == int(np.nonzero(dep == dep.max())[0][0])
+    r = oracle.verify_greedy(tl, par[None], tok_none[None], 5)
+    assert r["accept_len"][0] == 0 and r["bonus"][0] == am[0]
+    star = wl.star_tree(B)[0]
+    r = oracle.verify_greedy(tl, star[None], tok_all[None] * 0 + am[0], 5)
+    assert r["accept_len"][0] == 1 and r["accept_path"][0, :2].tolist() == [0, 1]
+
+
+def test_argmax_ties_lowest_id_and_flags():
+    V = 16
+    x = np.zeros((3, V), np.float32)
+    x[0, [3, 9, 12]] = 2.0          # tie: lowest id 3
+    x[1, 5] = np.nan                 # NaN is skipped and flagged
+    x[1, 7] = 1.0
+    x[2, 15] = 1.0
+    par = np.array([[-1, 0, 1]], np.int32)
+    tok = np.array([[0, 3, 7]], np.int32)
+    r = oracle.verify_greedy(x, par, tok, 2)
+    assert r["argmax"][0].tolist() == [3, 7, 15]
+    assert r["err"][0] == oracle.NAN
+    assert r["accept_len"][0] == 2 and r["bonus"][0] == 15
+    r = oracle.verify_greedy(x, par, tok, 1)                 # depth 2 > N = 1
+    assert r["err"][0] & oracle.DEPTH_GT_N
+    r = oracle.verify_greedy(x, np.array([[-1, 0, 2]], np.int32), tok, 2)
+    assert r["err"][0] & oracle.BAD_PARENT
