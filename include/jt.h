@@ -1,0 +1,188 @@
+/*
+ * jt.h -- C ABI of libjt: one draft-and-verify step over a candidate token tree
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * The step (JetSpec causal parallel tree drafting):
+ *   1. jt_build_tree_mask  parent indices -> per-node 256-bit ancestor rows + depths
+ *   2. jt_tree_attention   all B tree nodes attend, in one pass, to the prefix KV and
+ *                          to the tree KV under the tree-causal mask
+ *   3. jt_topw_per_depth   top-W token ids and log-probs of each draft logit row
+ *   4. jt_verify_greedy    longest root path whose tokens equal the target argmax at
+ *                          their parent, plus the bonus token
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or keeps any of them after the call returns.
+ *   - Scratch memory is passed in as `workspace` after a *_workspace_size() query; a
+ *     NULL workspace is allowed only when the query returns 0.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous and
+ *     stream-ordered; outputs are valid once the stream reaches them.  No call
+ *     synchronises the host.  The library holds no state: concurrent calls on
+ *     different streams with disjoint outputs and workspaces are safe.
+ *   - Shape, dtype, NULL-pointer, alignment and workspace problems are detected on the
+ *     host and returned synchronously before anything is launched.  A failed launch
+ *     returns JT_ERR_LAUNCH.  No C++ exception crosses this boundary.
+ *   - Data-dependent faults are only visible on the device.  Entry points that take an
+ *     `err` array (int32 [S], may be NULL) OVERWRITE err[s] with the OR of the JT_DEV_*
+ *     flags found for sequence s (0 when clean).  Outputs of a flagged sequence are
+ *     unspecified but every memory access stays in bounds.
+ *   - Tensors are dense row-major (C order) unless a stride argument says otherwise.
+ *   - bf16 = bfloat16 (1 sign, 8 exponent, 7 mantissa bits); JT_F32 = IEEE binary32.
+ */
+#ifndef JT_H
+#define JT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JT_ABI_VERSION 1
+
+typedef enum {
+    JT_OK = 0,
+    JT_ERR_NULL = 1,      /* a required pointer is NULL */
+    JT_ERR_SHAPE = 2,     /* a size is out of the supported range (see each call) */
+    JT_ERR_DTYPE = 3,     /* unsupported element type for this call */
+    JT_ERR_WORKSPACE = 4, /* workspace smaller than the *_workspace_size() answer */
+    JT_ERR_LAUNCH = 5,    /* the HIP runtime rejected a kernel launch */
+    JT_ERR_ALIGN = 6      /* a pointer or stride breaks the stated alignment */
+} jt_status;
+
+typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
+
+/* device-side per-sequence flags written to err[s] */
+enum {
+    JT_DEV_BAD_PARENT = 1,  /* parent[s,0] != -1 or parent[s,i] not in [0, i) */
+    JT_DEV_DEPTH_GT_N = 2,  /* some node is deeper than N */
+    JT_DEV_BAD_BLOCK = 4,   /* a block-table entry needed by the prefix is outside the pool */
+    JT_DEV_NAN = 8,         /* a target logit row holds a NaN */
+    JT_DEV_BAD_PREFIX = 16  /* prefix_len[s] outside [0, max_prefix] (it is clamped) */
+};
+
+#define JT_MAX_NODES 256 /* B limit: one 256-bit ancestor row per node */
+#define JT_MAX_W 16
+
+int jt_abi_version(void);
+const char *jt_status_string(int status);
+
+/*
+ * Step 1 -- tree-causal mask from parent indices.
+ * Defines M[v,u] = 0 iff u is an ancestor of v or v itself, -inf otherwise (JetSpec
+ * review on startedourmission.github.io, "How it works", mask equation); the verifier
+ * consumes parent indices, depths and this mask without a dense per-request matrix
+ * (paperlayer.ai JetSpec summary, appendix E "Verification").
+ *
+ *   parent  int32 [S,B]     parent[s,0] = -1 (node 0 is the root, the last committed
+ *                           token); 0 <= parent[s,i] < i for i >= 1.
+ *   anc     uint64 [S,B,4]  out: bit u of row (s,v) -- word u>>6, bit u&63 -- is set
+ *                           iff u is an ancestor of v or u == v.  Bits >= B are 0.
+ *   depth   int32 [S,B]     out: parent steps from v to the root (root 0).
+ *   err     int32 [S]       out (optional): JT_DEV_BAD_PARENT; such a sequence gets
+ *                           anc = 0 and depth = -1.
+ * Supported: S >= 0, 1 <= B <= 256.  One workgroup per sequence.
+ */
+jt_status jt_build_tree_mask(const int32_t *parent, int32_t S, int32_t B, uint64_t *anc,
+                             int32_t *depth, int32_t *err, void *stream);
+
+/*
+ * Step 2 -- tree-causal GQA attention, all nodes in one pass.
+ * For sequence s, node v and query head h (KV head g = h / (Hq/Hkv)):
+ *   out[s,v,h] = softmax_j(scale * <q[s,v,h], k_j>) . v_j over j = every prefix key of s
+ *                and every tree node u with bit u set in anc[s,v];
+ * i.e. a node sees the prefix, its ancestors and itself, never siblings or descendants
+ * (startedourmission.github.io review, mask equation; paperlayer.ai JetSpec summary,
+ * section 2 "Architecture" and appendix E "Verification").  Tree keys come after the
+ * prefix.  q and k are post-RoPE: position prefix_len[s] + depth[s,v] is the caller's.
+ *
+ *   q                 [S,B,Hq,d]      dtype
+ *   k_tree, v_tree    [S,B,Hkv,d]     dtype
+ *   k_prefix,v_prefix block_table == NULL: contiguous [S,max_prefix,Hkv,d];
+ *                     otherwise a pool [num_blocks,block_size,Hkv,d] in which logical
+ *                     key j of sequence s is slot j % block_size of block
+ *                     block_table[s*max_blocks_per_seq + j/block_size].
+ *   block_table       int32 [S,max_blocks_per_seq] or NULL; entries past the prefix
+ *                     are never read.
+ *   prefix_len        int32 [S] device; keys j >= prefix_len[s] are never read.
+ *   anc               uint64 [S,B,4] as written by jt_build_tree_mask.
+ *   scale             <= 0 selects 1/sqrt(d).
+ *   out               [S,B,Hq,d] dtype.
+ *   lse               float [S,B,Hq] (optional): natural-log sum of exp of the scaled
+ *                     visible scores.
+ *   err               int32 [S] (optional): JT_DEV_BAD_PREFIX, JT_DEV_BAD_BLOCK; keys of
+ *                     an out-of-pool block are skipped.
+ * Supported: d in {64,128}; Hq % Hkv == 0 and 1 <= Hq/Hkv <= 8; 1 <= B <= 256;
+ * block_size a power of two; dtype JT_BF16 or JT_F32; q/k/v/out 16-byte aligned.
+ * bf16 runs on MFMA (fp32 accumulate, bf16 out); fp32 runs on the vector ALU.
+ */
+size_t jt_tree_attention_workspace_size(int32_t S, int32_t B, int32_t Hq, int32_t Hkv,
+                                        int32_t d, int32_t max_prefix, jt_dtype dtype);
+jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tree,
+                            const void *k_prefix, const void *v_prefix,
+                            const int32_t *block_table, int32_t max_blocks_per_seq,
+                            int32_t block_size, int32_t num_blocks,
+                            const int32_t *prefix_len, int32_t max_prefix, const uint64_t *anc,
+                            int32_t S, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                            jt_dtype dtype, float scale, void *out, float *lse, int32_t *err,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Step 3 -- per-depth top-W with log-probabilities.
+ * The proposer extracts the top-k tokens and their log-probabilities at each future
+ * position (paperlayer.ai JetSpec summary, appendix E "Drafting"), W candidates per
+ * depth (paper.rainbus.top summary, method steps).  Row r of the draft logits gives the
+ * candidates of depth r+1 (per sequence: rows s*N .. s*N+N-1).
+ *
+ *   logits    [rows, row_stride] dtype; the first V entries of a row are the vocabulary.
+ *   ids       int32 [rows,W] out: token ids, logit descending, id ascending on ties
+ *             (-0 == +0; NaN ranks below -inf).
+ *   logprob   float [rows,W] out: logit - row_lse.
+ *   row_lse   float [rows] (optional) out: log sum_t exp(logit_t) over the whole row
+ *             (NaN if the row holds a NaN, -inf if every entry is -inf).
+ * Supported: rows >= 0, 1 <= W <= min(16, V), V < 2^31, row_stride >= V.
+ */
+size_t jt_topw_workspace_size(int32_t rows, int32_t V, int32_t W, jt_dtype dtype);
+jt_status jt_topw_per_depth(const void *logits, int64_t row_stride, int32_t rows, int32_t V,
+                            int32_t W, jt_dtype dtype, int32_t *ids, float *logprob,
+                            float *row_lse, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * Step 4 -- greedy tree verification.
+ * The verifier accepts the longest prefix whose draft tokens pass the acceptance test
+ * and commits it plus one bonus token (paperlayer.ai JetSpec summary, section 2;
+ * JetSpec++ summary, section 3).  At temperature 0 the test min(1, p/q)
+ * (startedourmission.github.io review, inference) with a point-mass draft
+ * (paperlayer.ai JetSpec++ summary, appendix F.3) is "token == target argmax at the
+ * parent":
+ *   am[s,v]       = argmax_t target_logits[s,v,t], lowest id on ties, NaN skipped;
+ *   v accepted    iff tokens[s,u] == am[s,parent[s,u]] for every non-root u on the
+ *                 root path of v (the root is always accepted);
+ *   v*            = the deepest accepted node, lowest index on ties.
+ *
+ *   target_logits [S*B, row_stride] dtype (row s*B+v belongs to node v of sequence s).
+ *   parent, tokens int32 [S,B]; tokens[s,0] is never checked.
+ *   anc, depth    as written by jt_build_tree_mask for the same parent array.
+ *   accept_len    int32 [S] out: depth(v*) = number of accepted draft tokens.
+ *   accept_path   int32 [S,N+1] out: root .. v*, then -1.
+ *   bonus         int32 [S] out: am[s,v*].
+ *   argmax_out    int32 [S,B] (optional) out: am.
+ *   err           int32 [S] (optional): JT_DEV_BAD_PARENT, JT_DEV_DEPTH_GT_N,
+ *                 JT_DEV_NAN.  A bad-parent or too-deep sequence gets accept_len 0,
+ *                 path [0,-1,...] and bonus am[s,0].
+ * Supported: 1 <= B <= 256, 0 <= N <= 255, V < 2^31, row_stride >= V.
+ */
+size_t jt_verify_workspace_size(int32_t S, int32_t B, int32_t V, jt_dtype dtype);
+jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_t V,
+                           jt_dtype dtype, const int32_t *parent, const int32_t *tokens,
+                           const uint64_t *anc, const int32_t *depth, int32_t S, int32_t B,
+                           int32_t N, int32_t *accept_len, int32_t *accept_path,
+                           int32_t *bonus, int32_t *argmax_out, int32_t *err,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JT_H */

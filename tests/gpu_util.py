@@ -1,0 +1,63 @@
+"""Helpers for the GPU parity tests (device transfers and the comparison rules)."""
+import numpy as np
+import pytest
+import torch
+
+from tree_causal_draft_amd import workload as wl
+from tree_causal_draft_amd.step import to_device
+
+DEV = "cuda:0"
+
+# attention tolerances: |gpu - ref| <= atol + rtol*|ref| elementwise, plus relative L2
+BF16_ATOL, BF16_RTOL, BF16_RELL2 = 2e-2, 1e-2, 1e-2
+F32_ATOL, F32_RTOL = 1e-5, 1e-5
+# log-prob / LSE tolerance (fp32 sums over up to 151,936 terms)
+LP_ATOL, LP_RTOL = 1e-5, 1e-5
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU (deselect with -m 'not gpu')")
+
+
+def dev(a):
+    return to_device(a, DEV)
+
+
+def host(t):
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return wl.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy()
+
+
+def anc_to_dense(anc_np, B):
+    """uint64 rows [S,B,4] -> dense uint8 [S,B,B] (bit u of word u>>6)."""
+    a = anc_np.view(np.uint64)
+    S = a.shape[0]
+    out = np.zeros((S, B, B), np.uint8)
+    for u in range(B):
+        out[:, :, u] = ((a[:, :, u >> 6] >> np.uint64(u & 63)) & np.uint64(1)).astype(np.uint8)
+    return out
+
+
+def assert_attention_close(got, ref, dtype, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    if dtype == "f32":
+        bad = np.abs(got - ref) > F32_ATOL + F32_RTOL * np.abs(ref)
+        assert not bad.any(), f"{what}: {bad.sum()} elements off, max err {np.abs(got-ref).max():.3e}"
+        return
+    bad = np.abs(got - ref) > BF16_ATOL + BF16_RTOL * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} elements off, max err {np.abs(got-ref).max():.3e}"
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert rel <= BF16_RELL2, f"{what}: relative L2 {rel:.3e}"
+
+
+def assert_lp_close(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bad = np.abs(got - ref) > LP_ATOL + LP_RTOL * np.abs(ref)
+    assert not bad.any(), f"{what}: max err {np.abs(got - ref).max():.3e}"

@@ -1,0 +1,81 @@
+"""CPU checks of the C ABI: the library loads, exports what include/jt.h declares, and
+rejects bad arguments on the host before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_causal_draft_amd as jt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "jt.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(jt_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_declares_the_four_steps():
+    names = _declared()
+    for n in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth", "jt_verify_greedy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = jt.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert set(_declared()) <= set(jt.EXPORTS)
+
+
+def test_version_and_status_strings():
+    L = jt.lib()
+    assert L.jt_abi_version() == 1
+    assert L.jt_status_string(0) == b"ok"
+    assert b"NULL" in L.jt_status_string(1)
+    assert L.jt_status_string(99) == b"unknown status"
+
+
+def test_host_validation_returns_before_launch():
+    L = jt.lib()
+    nul = None
+    # mask: B out of range, NULL pointers
+    assert L.jt_build_tree_mask(nul, 1, 0, nul, nul, nul, nul) == 2
+    assert L.jt_build_tree_mask(nul, 1, 257, nul, nul, nul, nul) == 2
+    assert L.jt_build_tree_mask(nul, 1, 16, nul, nul, nul, nul) == 1
+    assert L.jt_build_tree_mask(nul, 0, 16, nul, nul, nul, nul) == 0   # empty batch: no-op
+    # top-W: W > 16, W > V, bad dtype, stride < V, NULLs
+    args = lambda rows, V, W, dt, stride=None: (nul, stride or V, rows, V, W, dt, nul, nul, nul,
+                                                 nul, 0, nul)
+    assert L.jt_topw_per_depth(*args(4, 100, 17, 1)) == 2
+    assert L.jt_topw_per_depth(*args(4, 3, 4, 1)) == 2
+    assert L.jt_topw_per_depth(*args(4, 100, 4, 7)) == 3
+    assert L.jt_topw_per_depth(*args(4, 100, 4, 1, stride=50)) == 2
+    assert L.jt_topw_per_depth(*args(4, 100, 4, 1)) == 1
+    # attention: d = 96, Hq % Hkv, G > 8, NULLs, workspace
+    def attn(S=1, B=16, Hq=32, Hkv=8, d=128, dt=1, P=64):
+        return L.jt_tree_attention(nul, nul, nul, nul, nul, nul, 0, 16, 0, nul, P, nul, S, B, Hq,
+                                   Hkv, d, dt, ctypes.c_float(0.0), nul, nul, nul, nul, 0, nul)
+    assert attn(d=96) == 2
+    assert attn(Hq=30, Hkv=8) == 2
+    assert attn(Hq=32, Hkv=2) == 2
+    assert attn(B=300) == 2
+    assert attn(dt=5) == 3
+    assert attn() == 1
+    # verify: N > 255, NULLs
+    def ver(N=8, B=16):
+        return L.jt_verify_greedy(nul, 1000, 1000, 1, nul, nul, nul, nul, 1, B, N, nul, nul, nul,
+                                  nul, nul, nul, 0, nul)
+    assert ver(N=256) == 2
+    assert ver() == 1
+
+
+def test_workspace_queries_are_pure():
+    assert jt.topw_workspace_size(16, 151936, 4, 1) > 0
+    assert jt.verify_workspace_size(1, 16, 151936, 1) > 0
+    # the large-batch attention plan needs no split workspace; the small one does
+    assert jt.tree_attention_workspace_size(32, 64, 32, 4, 128, 4096, 1) == 0
+    assert jt.tree_attention_workspace_size(1, 16, 32, 8, 128, 1024, 1) > 0
+    assert jt.tree_attention_workspace_size(1, 16, 4, 2, 64, 64, 0) == 0

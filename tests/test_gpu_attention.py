@@ -1,0 +1,159 @@
+"""GPU parity of jt_tree_attention against the fp64 oracle.
+
+bf16: |gpu - ref| <= 2e-2 + 1e-2 |ref| per element and relative L2 <= 1e-2; fp32:
+1e-5 + 1e-5 |ref|.  Each bf16 case also runs with q, k ~ N(0, 1) ("sharp"), where the
+softmax is peaked enough that a masking or rescaling mistake moves outputs far past the
+tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_causal_draft_amd as jt
+from tree_causal_draft_amd import workload as wl
+from gpu_util import assert_attention_close, dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(w, scale=0.0):
+    need_gpu()
+    anc, depth, _ = jt.build_tree_mask(dev(w.parent))
+    out, lse, err = jt.tree_attention(
+        dev(w.q), dev(w.k_tree), dev(w.v_tree), dev(w.k_prefix), dev(w.v_prefix),
+        dev(w.prefix_len), anc, block_table=None if w.block_table is None else dev(w.block_table),
+        block_size=w.cfg.block_size, num_blocks=w.num_blocks or None, max_prefix=w.max_prefix,
+        scale=scale)
+    torch.cuda.synchronize()
+    return host(out), host(lse), host(err)
+
+
+def _check(w, what, sel=None, scale=0.0):
+    cfg = w.cfg
+    print(f"[attn] {what} S={cfg.S} B={cfg.B} P={w.prefix_len.tolist()[:4]} Hq={cfg.Hq} "
+          f"Hkv={cfg.Hkv} d={cfg.d} {cfg.dtype} paged={cfg.paged}", flush=True)
+    out, lse, err = _run_gpu(w, scale)
+    kw = dict(block_table=w.block_table, block_size=cfg.block_size, num_blocks=w.num_blocks,
+              max_prefix=w.max_prefix, scale=scale)
+    if sel is None:
+        ref, rlse, rerr = oracle.tree_attention(w.q, w.k_tree, w.v_tree, w.k_prefix, w.v_prefix,
+                                                w.prefix_len, w.parent, **kw)
+        got, glse = out, lse
+    else:
+        ref, rlse, rerr = oracle.tree_attention(w.q, w.k_tree, w.v_tree, w.k_prefix, w.v_prefix,
+                                                w.prefix_len, w.parent, sel=sel, **kw)
+        got = out[sel[:, 0], sel[:, 1], sel[:, 2]]
+        glse = lse[sel[:, 0], sel[:, 1], sel[:, 2]]
+    assert np.array_equal(err, rerr)
+    assert_attention_close(got, ref, cfg.dtype, what)
+    tol = 1e-5 if cfg.dtype == "f32" else 2e-3
+    assert np.abs(glse - rlse).max() <= tol * max(1.0, np.abs(rlse).max()), what
+    return out
+
+
+def _small(**kw):
+    base = dict(S=2, prefix=300, B=40, N=10, W=4, Hq=8, Hkv=2, d=128, dtype="bf16", V=4096)
+    base.update(kw)
+    return base
+
+
+def test_tiny_fp32():
+    w = wl.make("tiny", 401, parts=("attn",))
+    _check(w, "tiny fp32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("sharp", [False, True])
+def test_bf16_random_trees(d, G, sharp):
+    w = wl.make("ragged", 410 + G, parts=("attn",), qk_std=1.0 if sharp else None,
+                **_small(d=d, Hq=2 * G, Hkv=2, paged=False, prefix=(100, 300)))
+    _check(w, f"bf16 d={d} G={G} sharp={sharp}")
+
+
+@pytest.mark.parametrize("B,P", [(1, 0), (1, 77), (16, 0), (256, 0), (256, 130), (65, 64)])
+def test_bf16_edge_shapes(B, P):
+    w = wl.make("ragged", 420 + B, parts=("attn",), qk_std=1.0,
+                **_small(S=1, B=B, N=255, W=256, prefix=P, paged=False))
+    _check(w, f"edge B={B} P={P}")
+
+
+@pytest.mark.parametrize("tree", ["chain", "star"])
+def test_bf16_chain_and_star(tree):
+    B = 200
+    t = wl.chain_tree(B) if tree == "chain" else wl.star_tree(B)
+    w = wl.make("ragged", 430, parts=("attn",), qk_std=1.0, trees=[t, t],
+                **_small(B=B, N=255, W=256, prefix=(50, 190), paged=False))
+    _check(w, tree)
+
+
+@pytest.mark.parametrize("bs", [16, 4])
+def test_bf16_paged(bs):
+    w = wl.make("ragged", 440 + bs, parts=("attn",), qk_std=1.0,
+                **_small(S=3, prefix=(1, 500), paged=True, block_size=bs))
+    _check(w, f"paged bs={bs}")
+
+
+def test_fp32_paged_and_gqa():
+    w = wl.make("ragged", 450, parts=("attn",), **_small(S=2, dtype="f32", d=64, Hq=8, Hkv=1,
+                                                           prefix=(33, 97), paged=True, B=20))
+    _check(w, "fp32 paged G=8")
+
+
+def test_bad_block_flag_and_explicit_scale():
+    w = wl.make("ragged", 460, parts=("attn",), **_small(S=2, prefix=(40, 80), paged=True))
+    w.block_table[1, 1] = w.num_blocks + 3
+    out, lse, err = _run_gpu(w)
+    assert err[0] == 0 and err[1] == jt.DEV_BAD_BLOCK
+    w2 = wl.make("ragged", 461, parts=("attn",), **_small(S=1, prefix=60, paged=False))
+    _check(w2, "scale 0.3", scale=0.3)
+
+
+def test_sibling_invariance_bitwise():
+    """Perturbing K/V of nodes outside Anc(v) u {v} leaves row v bit-identical."""
+    w = wl.make("ragged", 470, parts=("attn",), qk_std=1.0,
+                **_small(S=1, B=96, prefix=150, paged=False, N=6, W=5))
+    base, _, _ = _run_gpu(w)
+    vis, _, _ = oracle.build_mask(w.parent)
+    rng = np.random.default_rng(0)
+    for v in (3, 40, 95):
+        hidden = ~vis[0, v].astype(bool)
+        w2 = wl.make("ragged", 470, parts=("attn",), qk_std=1.0,
+                     **_small(S=1, B=96, prefix=150, paged=False, N=6, W=5))
+        n = int(hidden.sum())
+        w2.k_tree[0, hidden] = wl.to_dtype(rng.normal(0, 3, (n,) + w2.k_tree.shape[2:]), "bf16")
+        w2.v_tree[0, hidden] = wl.to_dtype(rng.normal(0, 3, (n,) + w2.v_tree.shape[2:]), "bf16")
+        pert, _, _ = _run_gpu(w2)
+        assert np.array_equal(pert[0, v], base[0, v])
+        assert not np.array_equal(pert, base)
+
+
+def _sample(w, n, seed):
+    rng = np.random.default_rng(seed)
+    cfg = w.cfg
+    sel = np.stack([rng.integers(0, cfg.S, n), rng.integers(0, cfg.B, n),
+                    rng.integers(0, cfg.Hq, n)], 1).astype(np.int32)
+    # always include the first and last rows and the deepest node of sequence 0
+    extra = np.array([[0, 0, 0], [cfg.S - 1, cfg.B - 1, cfg.Hq - 1],
+                      [0, int(w.depth[0].argmax()), 1 % cfg.Hq]], np.int32)
+    return np.concatenate([sel, extra])
+
+
+@pytest.mark.parametrize("name", ["low_budget", "high_budget", "ragged", "moe_verify"])
+def test_config_full_size_sampled(name):
+    w = wl.make(name, 480, parts=("attn",))
+    _check(w, name, sel=_sample(w, 96, 1))
+
+
+@pytest.mark.parametrize("name", ["low_budget", "high_budget"])
+def test_config_full_size_sharp_all_rows(name):
+    w = wl.make(name, 481, parts=("attn",), qk_std=1.0)
+    _check(w, name + " sharp")
+
+
+def test_deterministic():
+    w = wl.make("high_budget", 490, parts=("attn",))
+    a, _, _ = _run_gpu(w)
+    b, _, _ = _run_gpu(w)
+    assert np.array_equal(a, b)

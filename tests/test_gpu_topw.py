@@ -1,0 +1,76 @@
+"""GPU parity of jt_topw_per_depth: bit-exact ids, log-probs / LSE within 1e-5 + 1e-5|ref|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_causal_draft_amd as jt
+from tree_causal_draft_amd import workload as wl
+from gpu_util import assert_lp_close, dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(logits, W, V=None, what=""):
+    need_gpu()
+    rows, stride = logits.shape
+    V = stride if V is None else V
+    print(f"[topw] {what} rows={rows} V={V} stride={stride} W={W} {logits.dtype}", flush=True)
+    ids, lp, lse = jt.topw_per_depth(dev(logits), W, V=V)
+    torch.cuda.synchronize()
+    r_ids, r_lp, r_lse = oracle.topw(logits, W, V=V)
+    assert np.array_equal(host(ids), r_ids), what
+    assert_lp_close(host(lp), r_lp, what)
+    assert_lp_close(host(lse), r_lse, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 7, 1000, 8192, 8193, 20000, 40961])
+@pytest.mark.parametrize("W", [1, 2, 8, 16])
+def test_random_rows(dtype, V, W):
+    if W > V:
+        return
+    rng = np.random.default_rng(V * 31 + W)
+    x = rng.normal(0, 3, (9, V)).astype(np.float32)
+    _check(wl.to_dtype(x, dtype), W, what=f"{dtype}")
+
+
+def test_bf16_ties_and_constant_rows():
+    rng = np.random.default_rng(5)
+    x = wl.to_dtype(rng.normal(0, 3, (6, 30000)).astype(np.float32), "bf16")
+    x[1] = wl.scalar_in_dtype(1.5, "bf16")                     # constant row: ids 0..W-1
+    x[2, ::7] = wl.scalar_in_dtype(40.0, "bf16")               # thousands of tied maxima
+    x[3, 100:200] = wl.scalar_in_dtype(-0.0, "bf16")           # signed zeros
+    x[3, 150:250] = wl.scalar_in_dtype(0.0, "bf16")
+    for W in (1, 5, 16):
+        _check(x, W, what="ties")
+
+
+def test_row_stride_and_unaligned():
+    rng = np.random.default_rng(9)
+    x = wl.to_dtype(rng.normal(0, 3, (5, 10007)).astype(np.float32), "bf16")
+    _check(x, 4, V=9001, what="odd stride, sub-vocab")
+    y = rng.normal(0, 2, (3, 4099)).astype(np.float32)
+    _check(y, 3, V=4097, what="f32 odd stride")
+
+
+def test_neg_inf_rows():
+    x = np.full((2, 5000), -np.inf, np.float32)
+    x[1, 4000] = 1.0
+    need_gpu()
+    ids, lp, lse = jt.topw_per_depth(dev(x), 3)
+    torch.cuda.synchronize()
+    r_ids, _, r_lse = oracle.topw(x, 3)
+    assert np.array_equal(host(ids), r_ids)
+    assert np.array_equal(np.isneginf(host(lse)), np.isneginf(r_lse))
+
+
+@pytest.mark.parametrize("name", ["tiny", "low_budget", "high_budget", "ragged", "moe_verify"])
+def test_config_draft_logits(name):
+    w = wl.make(name, 202, parts=("draft",))
+    _check(w.draft_logits, w.cfg.W, what=name)
+
+
+def test_config_unplanted_ties():
+    w = wl.make("moe_verify", 203, parts=("draft",), plant=False, S=4)
+    _check(w.draft_logits, 8, what="unplanted")

@@ -1,0 +1,91 @@
+"""GPU parity of jt_verify_greedy: bit-exact argmax, accepted length, path, bonus, flags."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_causal_draft_amd as jt
+from tree_causal_draft_amd import workload as wl
+from gpu_util import dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(target, parent, tokens, N, V=None, what=""):
+    need_gpu()
+    parent = np.ascontiguousarray(parent, np.int32)
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    S, B = parent.shape
+    print(f"[verify] {what} S={S} B={B} N={N} V={V or target.shape[-1]}", flush=True)
+    dp = dev(parent)
+    anc, depth, _ = jt.build_tree_mask(dp)
+    r = jt.verify_greedy(dev(target.reshape(S * B, -1)), dp, dev(tokens), anc, depth, N, V=V)
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(target.reshape(S * B, -1), parent, tokens, N, V=V)
+    err = host(r["err"])
+    assert np.array_equal(err, ref["err"]), what
+    clean = (ref["err"] & (oracle.NAN)) == 0
+    assert np.array_equal(host(r["argmax"])[clean], ref["argmax"][clean]), what
+    for k in ("accept_len", "bonus"):
+        assert np.array_equal(host(r[k])[clean], ref[k][clean]), (what, k)
+    assert np.array_equal(host(r["accept_path"])[clean], ref["accept_path"][clean]), what
+    return r, ref
+
+
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
+def test_config_planted(name):
+    w = wl.make(name, 301, parts=("target",))
+    _, ref = _check(w.target_logits, w.parent, w.tokens, w.cfg.N, what=name)
+    assert (ref["err"] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "low_budget", "ragged"])
+def test_config_unplanted_ties(name):
+    w = wl.make(name, 302, parts=("target",), plant=False)
+    _check(w.target_logits, w.parent, w.tokens, w.cfg.N, what=name + " unplanted")
+
+
+def test_exhaustive_tiny_trees():
+    """All parent arrays with B <= 5 x all accept patterns (duplicates included)."""
+    for B in range(1, 6):
+        V = 2 * B + 2
+        pats = list(itertools.product([0, 1], repeat=B - 1))
+        pars, toks = [], []
+        for tail in itertools.product(*[range(i) for i in range(1, B)]):
+            parent = [-1] + list(tail)
+            for pat in pats:
+                tok = [0] + [2 * parent[u] + (0 if pat[u - 1] else 1) for u in range(1, B)]
+                pars.append(parent)
+                toks.append(tok)
+        S = len(pars)
+        x = np.zeros((S * B, V), np.float32)
+        x[np.arange(S * B), np.tile(2 * np.arange(B), S)] = 1.0
+        _check(x, np.array(pars), np.array(toks), B, what=f"exhaustive B={B}")
+
+
+def test_ties_nan_and_flags():
+    V = 3000
+    rng = np.random.default_rng(1)
+    x = wl.to_dtype(rng.normal(0, 3, (4 * 6, V)).astype(np.float32), "bf16")
+    x[0, [17, 900, 2999]] = wl.scalar_in_dtype(50.0, "bf16")   # tied maximum: id 17
+    x[7, 5] = np.uint16(0x7FC0)                                   # NaN -> flagged
+    par = np.array([[-1, 0, 1, 2, 3, 4]] * 4, np.int32)
+    par[2, 4] = 5                                                 # bad parent
+    tok = rng.integers(0, V, (4, 6)).astype(np.int32)
+    _check(x, par, tok, 5, what="flags")
+    _check(x, par, tok, 3, what="depth > N")
+
+
+def test_all_neg_inf_rows_pick_first_id():
+    x = np.full((3, 700), -np.inf, np.float32)
+    par = np.array([[-1, 0, 1]], np.int32)
+    _check(x, par, np.zeros((1, 3), np.int32), 2, what="-inf rows")
+
+
+def test_f32_row_stride():
+    rng = np.random.default_rng(3)
+    w = wl.make("tiny", 5, parts=("target",))
+    x = np.concatenate([w.target_logits, rng.normal(size=(16, 13)).astype(np.float32)], 1)
+    _check(x, w.parent, w.tokens, w.cfg.N, V=w.cfg.V, what="stride")

@@ -1,0 +1,211 @@
+"""Python binding of libjt (tree draft-and-verify step on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libjt.so``.  torch provides device memory and the current stream.  There is no
+CPU fallback: if the library is missing or fails to load, every call raises.
+
+Entry points (same names as the C ABI in ``include/jt.h``):
+    build_tree_mask, tree_attention, topw_per_depth, verify_greedy
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjt.so")
+
+JT_F32, JT_BF16 = 0, 1
+DEV_BAD_PARENT, DEV_DEPTH_GT_N, DEV_BAD_BLOCK, DEV_NAN, DEV_BAD_PREFIX = 1, 2, 4, 8, 16
+EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
+           "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
+           "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class JTError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libjt.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise JTError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m tree_causal_draft_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.jt_abi_version.restype = ctypes.c_int
+        L.jt_status_string.restype = ctypes.c_char_p
+        L.jt_status_string.argtypes = [ctypes.c_int]
+        L.jt_build_tree_mask.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.jt_tree_attention_workspace_size.restype = _sz
+        L.jt_tree_attention_workspace_size.argtypes = [_i32] * 6 + [ctypes.c_int]
+        L.jt_tree_attention.argtypes = ([_vp] * 6 + [_i32, _i32, _i32, _vp, _i32, _vp] +
+                                        [_i32] * 5 + [ctypes.c_int, ctypes.c_float, _vp, _vp, _vp,
+                                                      _vp, _sz, _vp])
+        L.jt_topw_workspace_size.restype = _sz
+        L.jt_topw_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
+        L.jt_topw_per_depth.argtypes = [_vp, _i64, _i32, _i32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]
+        L.jt_verify_workspace_size.restype = _sz
+        L.jt_verify_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
+        L.jt_verify_greedy.argtypes = ([_vp, _i64, _i32, ctypes.c_int] + [_vp] * 4 +
+                                       [_i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp])
+        for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
+                   "jt_verify_greedy"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return JT_BF16
+    if t.dtype == torch.float32:
+        return JT_F32
+    raise JTError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise JTError(f"{what}: {lib().jt_status_string(rc).decode()} (status {rc})")
+
+
+def _need(t, name):
+    if not t.is_cuda:
+        raise JTError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise JTError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def build_tree_mask(parent, anc=None, depth=None, err=None, stream=None):
+    """parent int32 [S,B] -> (anc uint64-as-int64 [S,B,4], depth int32 [S,B], err int32 [S])."""
+    _need(parent, "parent")
+    S, B = parent.shape
+    dev = parent.device
+    anc = torch.empty((S, B, 4), dtype=torch.int64, device=dev) if anc is None else anc
+    depth = torch.empty((S, B), dtype=torch.int32, device=dev) if depth is None else depth
+    err = torch.empty(S, dtype=torch.int32, device=dev) if err is None else err
+    _check(lib().jt_build_tree_mask(_ptr(parent), S, B, _ptr(anc), _ptr(depth), _ptr(err),
+                                    _stream(stream)), "jt_build_tree_mask")
+    return anc, depth, err
+
+
+def tree_attention_workspace_size(S, B, Hq, Hkv, d, max_prefix, dtype) -> int:
+    return int(lib().jt_tree_attention_workspace_size(S, B, Hq, Hkv, d, max_prefix, dtype))
+
+
+def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, prefix_len, anc, *, block_table=None,
+                   block_size=16, num_blocks=None, max_prefix=None, scale=0.0, out=None,
+                   lse=None, err=None, workspace=None, want_lse=True, stream=None):
+    """Tree-causal GQA attention; returns (out, lse or None, err)."""
+    for t, n in ((q, "q"), (k_tree, "k_tree"), (v_tree, "v_tree"), (k_prefix, "k_prefix"),
+                 (v_prefix, "v_prefix"), (prefix_len, "prefix_len"), (anc, "anc")):
+        _need(t, n)
+    S, B, Hq, d = q.shape
+    Hkv = k_tree.shape[2]
+    dt = _dt(q)
+    if block_table is None:
+        Pmax = k_prefix.shape[1] if max_prefix is None else max_prefix
+        maxblk, nblk = 0, 0
+    else:
+        _need(block_table, "block_table")
+        maxblk = block_table.shape[1]
+        Pmax = maxblk * block_size if max_prefix is None else max_prefix
+        nblk = k_prefix.shape[0] if num_blocks is None else num_blocks
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((S, B, Hq), dtype=torch.float32, device=dev)
+    err = torch.empty(S, dtype=torch.int32, device=dev) if err is None else err
+    need = tree_attention_workspace_size(S, B, Hq, Hkv, d, Pmax, dt)
+    ws, wsb = _workspace(need, dev, workspace)
+    _check(lib().jt_tree_attention(_ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
+                                   _ptr(v_prefix), _ptr(block_table), maxblk, block_size, nblk,
+                                   _ptr(prefix_len), Pmax, _ptr(anc), S, B, Hq, Hkv, d, dt,
+                                   float(scale), _ptr(out), _ptr(lse), _ptr(err), _ptr(ws), wsb,
+                                   _stream(stream)), "jt_tree_attention")
+    return out, lse, err
+
+
+def topw_workspace_size(rows, V, W, dtype) -> int:
+    return int(lib().jt_topw_workspace_size(rows, V, W, dtype))
+
+
+def topw_per_depth(logits, W, *, V=None, ids=None, logprob=None, row_lse=None, workspace=None,
+                   want_lse=True, stream=None):
+    """logits [rows, row_stride] -> (ids int32 [rows,W], logprob fp32 [rows,W], row_lse)."""
+    _need(logits, "logits")
+    rows, stride = logits.shape
+    V = stride if V is None else V
+    dt = _dt(logits)
+    dev = logits.device
+    ids = torch.empty((rows, W), dtype=torch.int32, device=dev) if ids is None else ids
+    logprob = torch.empty((rows, W), dtype=torch.float32, device=dev) if logprob is None else logprob
+    if row_lse is None and want_lse:
+        row_lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(topw_workspace_size(rows, V, W, dt), dev, workspace)
+    _check(lib().jt_topw_per_depth(_ptr(logits), stride, rows, V, W, dt, _ptr(ids), _ptr(logprob),
+                                   _ptr(row_lse), _ptr(ws), wsb, _stream(stream)),
+           "jt_topw_per_depth")
+    return ids, logprob, row_lse
+
+
+def verify_workspace_size(S, B, V, dtype) -> int:
+    return int(lib().jt_verify_workspace_size(S, B, V, dtype))
+
+
+def verify_greedy(target_logits, parent, tokens, anc, depth, N, *, V=None, accept_len=None,
+                  accept_path=None, bonus=None, argmax_out=None, err=None, workspace=None,
+                  want_argmax=True, stream=None):
+    """target_logits [S*B, row_stride]; returns dict of accept_len, accept_path, bonus,
+    argmax (or None) and err."""
+    for t, n in ((target_logits, "target_logits"), (parent, "parent"), (tokens, "tokens"),
+                 (anc, "anc"), (depth, "depth")):
+        _need(t, n)
+    S, B = parent.shape
+    tl = target_logits
+    stride = tl.shape[-1]
+    V = stride if V is None else V
+    dt = _dt(tl)
+    dev = tl.device
+    accept_len = torch.empty(S, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    accept_path = (torch.empty((S, N + 1), dtype=torch.int32, device=dev)
+                   if accept_path is None else accept_path)
+    bonus = torch.empty(S, dtype=torch.int32, device=dev) if bonus is None else bonus
+    if argmax_out is None and want_argmax:
+        argmax_out = torch.empty((S, B), dtype=torch.int32, device=dev)
+    err = torch.empty(S, dtype=torch.int32, device=dev) if err is None else err
+    ws, wsb = _workspace(verify_workspace_size(S, B, V, dt), dev, workspace)
+    _check(lib().jt_verify_greedy(_ptr(tl), stride, V, dt, _ptr(parent), _ptr(tokens), _ptr(anc),
+                                  _ptr(depth), S, B, N, _ptr(accept_len), _ptr(accept_path),
+                                  _ptr(bonus), _ptr(argmax_out), _ptr(err), _ptr(ws), wsb,
+                                  _stream(stream)), "jt_verify_greedy")
+    return dict(accept_len=accept_len, accept_path=accept_path, bonus=bonus, argmax=argmax_out,
+                err=err)

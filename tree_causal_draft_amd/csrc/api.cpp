@@ -1,0 +1,219 @@
+// extern "C" entry points of libjt: argument checks on the host, then stream-ordered
+// launches.  Nothing here allocates, synchronises or keeps state.
+#include <math.h>
+
+#include "jt_internal.h"
+
+using namespace jt;
+
+namespace {
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x)
+{
+    int r = 0;
+    while ((1 << r) < x)
+        ++r;
+    return r;
+}
+
+} // namespace
+
+extern "C" {
+
+int jt_abi_version(void) { return JT_ABI_VERSION; }
+
+const char *jt_status_string(int status)
+{
+    switch (status) {
+    case JT_OK: return "ok";
+    case JT_ERR_NULL: return "a required pointer is NULL";
+    case JT_ERR_SHAPE: return "a size is outside the supported range";
+    case JT_ERR_DTYPE: return "unsupported element type";
+    case JT_ERR_WORKSPACE: return "workspace too small";
+    case JT_ERR_LAUNCH: return "kernel launch failed";
+    case JT_ERR_ALIGN: return "pointer or stride misaligned";
+    default: return "unknown status";
+    }
+}
+
+jt_status jt_build_tree_mask(const int32_t *parent, int32_t S, int32_t B, uint64_t *anc,
+                             int32_t *depth, int32_t *err, void *stream)
+{
+    if (S < 0 || B < 1 || B > JT_MAX_NODES)
+        return JT_ERR_SHAPE;
+    if (S == 0)
+        return JT_OK;
+    if (!parent || !anc || !depth)
+        return JT_ERR_NULL;
+    return launch_build_mask(parent, S, B, anc, depth, err, as_stream(stream));
+}
+
+static jt_status attn_shape(int32_t S, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                            int32_t max_prefix, jt_dtype dtype)
+{
+    if (dtype != JT_BF16 && dtype != JT_F32)
+        return JT_ERR_DTYPE;
+    if (S < 0 || B < 1 || B > JT_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+        Hq / Hkv > 8 || (d != 64 && d != 128) || max_prefix < 0)
+        return JT_ERR_SHAPE;
+    if ((int64_t)S * B * Hq > INT32_MAX / 2 || (int64_t)S * Hkv > 65535)
+        return JT_ERR_SHAPE;
+    return JT_OK;
+}
+
+size_t jt_tree_attention_workspace_size(int32_t S, int32_t B, int32_t Hq, int32_t Hkv,
+                                        int32_t d, int32_t max_prefix, jt_dtype dtype)
+{
+    if (attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype) != JT_OK || S == 0)
+        return 0;
+    return attention_workspace(S, B, Hq, Hkv, d, max_prefix, dtype);
+}
+
+jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tree,
+                            const void *k_prefix, const void *v_prefix,
+                            const int32_t *block_table, int32_t max_blocks_per_seq,
+                            int32_t block_size, int32_t num_blocks,
+                            const int32_t *prefix_len, int32_t max_prefix, const uint64_t *anc,
+                            int32_t S, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                            jt_dtype dtype, float scale, void *out, float *lse, int32_t *err,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    jt_status st = attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype);
+    if (st != JT_OK)
+        return st;
+    if (S == 0)
+        return JT_OK;
+    if (!q || !k_tree || !v_tree || !prefix_len || !anc || !out)
+        return JT_ERR_NULL;
+    if (max_prefix > 0 && (!k_prefix || !v_prefix))
+        return JT_ERR_NULL;
+    if (block_table) {
+        if (!is_pow2(block_size) || max_blocks_per_seq < 0 || num_blocks < 0 ||
+            (int64_t)max_blocks_per_seq * block_size < max_prefix)
+            return JT_ERR_SHAPE;
+    }
+    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
+        (k_prefix && !aligned16(k_prefix)) || (v_prefix && !aligned16(v_prefix)))
+        return JT_ERR_ALIGN;
+    const size_t need = attention_workspace(S, B, Hq, Hkv, d, max_prefix, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return JT_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace))
+        return JT_ERR_ALIGN;
+    AttnArgs a;
+    a.q = q;
+    a.k_tree = k_tree;
+    a.v_tree = v_tree;
+    a.k_prefix = k_prefix;
+    a.v_prefix = v_prefix;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.block_size = block_table ? block_size : 1;
+    a.block_shift = block_table ? log2i(block_size) : 0;
+    a.num_blocks = num_blocks;
+    a.prefix_len = prefix_len;
+    a.max_prefix = max_prefix;
+    a.anc = anc;
+    a.S = S;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.d = d;
+    a.G = Hq / Hkv;
+    a.dtype = dtype;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+    a.out = out;
+    a.lse = lse;
+    a.err = err;
+    return launch_attention(a, workspace, as_stream(stream));
+}
+
+static jt_status topw_shape(int32_t rows, int32_t V, int32_t W, jt_dtype dtype)
+{
+    if (dtype != JT_BF16 && dtype != JT_F32)
+        return JT_ERR_DTYPE;
+    if (rows < 0 || V < 1 || W < 1 || W > JT_MAX_W || W > V)
+        return JT_ERR_SHAPE;
+    return JT_OK;
+}
+
+size_t jt_topw_workspace_size(int32_t rows, int32_t V, int32_t W, jt_dtype dtype)
+{
+    if (topw_shape(rows, V, W, dtype) != JT_OK || rows == 0)
+        return 0;
+    return topw_workspace(rows, V, W, dtype);
+}
+
+jt_status jt_topw_per_depth(const void *logits, int64_t row_stride, int32_t rows, int32_t V,
+                            int32_t W, jt_dtype dtype, int32_t *ids, float *logprob,
+                            float *row_lse, void *workspace, size_t workspace_bytes,
+                            void *stream)
+{
+    jt_status st = topw_shape(rows, V, W, dtype);
+    if (st != JT_OK)
+        return st;
+    if (row_stride < V)
+        return JT_ERR_SHAPE;
+    if (rows == 0)
+        return JT_OK;
+    if (!logits || !ids || !logprob)
+        return JT_ERR_NULL;
+    const size_t need = topw_workspace(rows, V, W, dtype);
+    if (!workspace || workspace_bytes < need)
+        return JT_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return JT_ERR_ALIGN;
+    return launch_topw(logits, row_stride, rows, V, W, dtype, ids, logprob, row_lse, workspace,
+                       as_stream(stream));
+}
+
+static jt_status verify_shape(int32_t S, int32_t B, int32_t V, int32_t N, jt_dtype dtype)
+{
+    if (dtype != JT_BF16 && dtype != JT_F32)
+        return JT_ERR_DTYPE;
+    if (S < 0 || B < 1 || B > JT_MAX_NODES || V < 1 || N < 0 || N > 255)
+        return JT_ERR_SHAPE;
+    return JT_OK;
+}
+
+size_t jt_verify_workspace_size(int32_t S, int32_t B, int32_t V, jt_dtype dtype)
+{
+    if (verify_shape(S, B, V, 0, dtype) != JT_OK || S == 0)
+        return 0;
+    return verify_workspace(S, B, V, dtype);
+}
+
+jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_t V,
+                           jt_dtype dtype, const int32_t *parent, const int32_t *tokens,
+                           const uint64_t *anc, const int32_t *depth, int32_t S, int32_t B,
+                           int32_t N, int32_t *accept_len, int32_t *accept_path,
+                           int32_t *bonus, int32_t *argmax_out, int32_t *err,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    jt_status st = verify_shape(S, B, V, N, dtype);
+    if (st != JT_OK)
+        return st;
+    if (row_stride < V)
+        return JT_ERR_SHAPE;
+    if (S == 0)
+        return JT_OK;
+    if (!target_logits || !parent || !tokens || !anc || !depth || !accept_len ||
+        !accept_path || !bonus)
+        return JT_ERR_NULL;
+    const size_t need = verify_workspace(S, B, V, dtype);
+    if (!workspace || workspace_bytes < need)
+        return JT_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return JT_ERR_ALIGN;
+    return launch_verify(target_logits, row_stride, V, dtype, parent, tokens, anc, depth, S, B, N,
+                         accept_len, accept_path, bonus, argmax_out, err, workspace,
+                         as_stream(stream));
+}
+
+} // extern "C"

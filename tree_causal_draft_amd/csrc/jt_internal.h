@@ -1,0 +1,109 @@
+// Internal helpers shared by the libjt kernels (gfx950, wave64).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/jt.h"
+
+namespace jt {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Monotone map of a float to uint32 for "value descending" comparisons.
+// -0 and +0 map to the same code; NaN maps to 0, below -inf (0x007fffff).
+__device__ __forceinline__ uint32_t order_code(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if (x != x)
+        return 0u;
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_decode(uint32_t c)
+{
+    if (c == 0u)
+        return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
+}
+// 64-bit ranking key: larger key = larger value, then lower id.  Key 0 = "no element".
+__device__ __forceinline__ uint64_t rank_key(float x, uint32_t id)
+{
+    return ((uint64_t)order_code(x) << 32) | (uint64_t)(~id);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return ~(uint32_t)k; }
+__device__ __forceinline__ float key_value(uint64_t k) { return order_decode((uint32_t)(k >> 32)); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+inline jt_status launch_status(hipError_t e) { return e == hipSuccess ? JT_OK : JT_ERR_LAUNCH; }
+
+// ---- launchers (each .hip file implements its own) ----
+jt_status launch_build_mask(const int32_t *parent, int S, int B, uint64_t *anc, int32_t *depth,
+                            int32_t *err, hipStream_t st);
+
+size_t topw_workspace(int rows, int V, int W, int dtype);
+jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, int W, int dtype,
+                      int32_t *ids, float *logprob, float *row_lse, void *ws, hipStream_t st);
+
+size_t verify_workspace(int S, int B, int V, int dtype);
+jt_status launch_verify(const void *logits, int64_t row_stride, int V, int dtype,
+                        const int32_t *parent, const int32_t *tokens, const uint64_t *anc,
+                        const int32_t *depth, int S, int B, int N, int32_t *accept_len,
+                        int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                        int32_t *err, void *ws, hipStream_t st);
+
+struct AttnArgs {
+    const void *q, *k_tree, *v_tree, *k_prefix, *v_prefix;
+    const int32_t *block_table;
+    int max_blocks, block_size, block_shift, num_blocks;
+    const int32_t *prefix_len;
+    int max_prefix;
+    const uint64_t *anc;
+    int S, B, Hq, Hkv, d, G;
+    int dtype;
+    float scale;
+    void *out;
+    float *lse;
+    int32_t *err;
+};
+size_t attention_workspace(int S, int B, int Hq, int Hkv, int d, int max_prefix, int dtype);
+jt_status launch_attention(const AttnArgs &a, void *ws, hipStream_t st);
+
+} // namespace jt

@@ -1,0 +1,282 @@
+// Step 4: greedy tree verification -- target argmax per node, then the accepted path.
+//
+// The verifier commits the longest root path whose draft tokens pass acceptance plus a
+// bonus token (paperlayer.ai JetSpec summary, section 2; JetSpec++ summary, section 3).
+// At temperature 0 the test min(1, p/q) of the review's inference section, with a
+// point-mass draft (JetSpec++ summary, appendix F.3), is token == argmax at the parent.
+//
+// Phase 1 (HBM-bound, the bulk of the bytes): arg-max of every target row.  A row is cut
+// into runs of 8192-logit sub-chunks, one workgroup per run, so a handful of rows still
+// fills the chip while 2048 rows stream whole.  Threads walk their logits in increasing
+// id order with a strict '>' so each keeps the first maximum; the workgroup then takes
+// the largest 64-bit key (order code << 32 | ~id): largest value, lowest id.
+// Phase 2 (one workgroup per sequence, thread v = node v):
+//   ok bits     ok[v] = tokens[v] == am[parent[v]] (root ok), one ballot per 64 nodes;
+//   accepted(v) (anc[v] & ~ok) == 0 -- every node on the root path is ok;
+//   v*          block max of (depth << 16 | 65535 - v) over accepted nodes;
+//   path        node u with bit u set in anc[v*] writes path[depth[u]] = u.
+#include "jt_internal.h"
+
+namespace jt {
+
+constexpr int kArgThreads = 256;
+constexpr int kArgSub = 8192;
+constexpr int kArgMaxChunks = 64;
+
+template <typename T> struct AVec;
+template <> struct AVec<uint16_t> { static constexpr int kElems = 8; static constexpr int kLoads = 4; };
+template <> struct AVec<float> { static constexpr int kElems = 4; static constexpr int kLoads = 8; };
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kArgThreads)
+argmax_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, int nsub,
+                      int sub_per_wg, int nchunk, uint64_t *__restrict__ ws_keys,
+                      uint32_t *__restrict__ ws_nan)
+{
+    constexpr int E = AVec<T>::kElems;
+    constexpr int L = AVec<T>::kLoads;
+    __shared__ uint64_t wkey[4];
+    __shared__ uint32_t wnan[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int row_idx = blockIdx.x / nchunk;
+    const int chunk = blockIdx.x % nchunk;
+    const T *row = logits + (int64_t)row_idx * row_stride;
+    const int sc0 = chunk * sub_per_wg;
+    const int sc1 = min(nsub, sc0 + sub_per_wg);
+
+    // The thread's first element seeds the running best so that a row of -inf still
+    // yields its first id; later elements replace it only when strictly larger.
+    const int64_t first = (int64_t)sc0 * kArgSub + (int64_t)tid * E;
+    float best = -INFINITY;
+    int64_t bi = first < V ? first : -1;
+    bool nan = false;
+    for (int sc = sc0; sc < sc1; ++sc) {
+        const int64_t base = (int64_t)sc * kArgSub;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int64_t e0 = base + (int64_t)(tid + kArgThreads * i) * E;
+            if (kAligned && e0 + E <= V) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(row + e0);
+                float x[E];
+                if constexpr (sizeof(T) == 2) {
+                    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+                    x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+                } else {
+                    x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+                    x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+                }
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    nan |= x[k] != x[k];
+                    if (x[k] > best) {
+                        best = x[k];
+                        bi = e0 + k;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const int64_t e = e0 + k;
+                    if (e < V) {
+                        float xv;
+                        if constexpr (sizeof(T) == 2)
+                            xv = bf16_to_f32(row[e]);
+                        else
+                            xv = row[e];
+                        nan |= xv != xv;
+                        if (xv > best) {
+                            best = xv;
+                            bi = e;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    uint64_t key = (bi >= 0) ? rank_key(best, (uint32_t)bi) : 0ull;
+    key = wave_max_u64(key);
+    const uint32_t wn = __ballot(nan) != 0ull;
+    if (lane == 0) {
+        wkey[wid] = key;
+        wnan[wid] = wn;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint64_t k = max(max(wkey[0], wkey[1]), max(wkey[2], wkey[3]));
+        ws_keys[blockIdx.x] = k;
+        ws_nan[blockIdx.x] = wnan[0] | wnan[1] | wnan[2] | wnan[3];
+    }
+}
+
+__global__ void __launch_bounds__(256)
+verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_keys,
+                   const uint32_t *__restrict__ ws_nan, const int32_t *__restrict__ parent,
+                   const int32_t *__restrict__ tokens, const uint64_t *__restrict__ anc,
+                   const int32_t *__restrict__ depth, int32_t *__restrict__ accept_len,
+                   int32_t *__restrict__ accept_path, int32_t *__restrict__ bonus,
+                   int32_t *__restrict__ argmax_out, int32_t *__restrict__ err)
+{
+    __shared__ int32_t am[JT_MAX_NODES];
+    __shared__ uint64_t okw[4];
+    __shared__ uint32_t wbest[4];
+    const int s = blockIdx.x;
+    const int v = threadIdx.x;
+    const int lane = v & 63, wid = v >> 6;
+    const int64_t nb = (int64_t)s * B + v;
+
+    int flags = 0;
+    int p = -1, dv = 0;
+    if (v < B) {
+        uint64_t k = 0ull;
+        uint32_t nn = 0u;
+        for (int c = 0; c < nchunk; ++c) {
+            const uint64_t kc = ws_keys[nb * nchunk + c];
+            k = kc > k ? kc : k;
+            nn |= ws_nan[nb * nchunk + c];
+        }
+        am[v] = (k == 0ull) ? 0 : (int32_t)key_id(k);
+        if (nn)
+            flags |= JT_DEV_NAN;
+        p = parent[nb];
+        if (v == 0 ? (p != -1) : (p < 0 || p >= v))
+            flags |= JT_DEV_BAD_PARENT;
+        dv = depth[nb];
+        if (dv > N || dv < 0)
+            flags |= JT_DEV_DEPTH_GT_N;
+    }
+    // OR of the flags over the block
+    __shared__ int fl[4];
+    int f = flags;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        f |= __shfl_xor(f, o, kWave);
+    if (lane == 0)
+        fl[wid] = f;
+    __syncthreads();
+    f = fl[0] | fl[1] | fl[2] | fl[3];
+    if (argmax_out && v < B)
+        argmax_out[nb] = am[v];
+    int32_t *path = accept_path + (int64_t)s * (N + 1);
+    if (f & (JT_DEV_BAD_PARENT | JT_DEV_DEPTH_GT_N)) {
+        if (f & JT_DEV_BAD_PARENT)
+            f &= ~JT_DEV_DEPTH_GT_N;  // depths are meaningless without a valid tree
+        for (int k = v; k <= N; k += blockDim.x)
+            path[k] = (k == 0) ? 0 : -1;
+        if (v == 0) {
+            accept_len[s] = 0;
+            bonus[s] = am[0];
+            if (err)
+                err[s] = f;
+        }
+        return;
+    }
+    const bool ok = (v < B) && (v == 0 || tokens[nb] == am[p]);
+    const uint64_t word = __ballot(ok);
+    if (lane == 0)
+        okw[wid] = word;
+    __syncthreads();
+    uint32_t key = 0u;
+    uint64_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    if (v < B) {
+        const uint64_t *ar = anc + nb * 4;
+        a0 = ar[0]; a1 = ar[1]; a2 = ar[2]; a3 = ar[3];
+        const bool accepted = ((a0 & ~okw[0]) | (a1 & ~okw[1]) | (a2 & ~okw[2]) | (a3 & ~okw[3])) == 0ull;
+        if (accepted)
+            key = ((uint32_t)dv << 16) | (uint32_t)(65535 - v);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        key = max(key, (uint32_t)__shfl_xor((int)key, o, kWave));
+    if (lane == 0)
+        wbest[wid] = key;
+    __syncthreads();
+    const uint32_t kb = max(max(wbest[0], wbest[1]), max(wbest[2], wbest[3]));
+    const int vstar = 65535 - (int)(kb & 0xffffu);
+    const int len = (int)(kb >> 16);
+    // path: every ancestor u of v* (itself included) sits at index depth[u]
+    for (int k = len + 1 + v; k <= N; k += blockDim.x)
+        path[k] = -1;
+    if (v < B) {
+        const uint64_t *ar = anc + ((int64_t)s * B + vstar) * 4;
+        if ((ar[v >> 6] >> (v & 63)) & 1ull)
+            path[dv] = v;
+    }
+    if (v == 0) {
+        accept_len[s] = len;
+        bonus[s] = am[vstar];
+        if (err)
+            err[s] = f;
+    }
+}
+
+struct ArgPlan {
+    int nsub, sub_per_wg, nchunk;
+};
+
+static ArgPlan arg_plan(int rows, int V)
+{
+    ArgPlan p;
+    p.nsub = (V + kArgSub - 1) / kArgSub;
+    int want = (rows > 0) ? (2048 + rows - 1) / rows : 1;
+    int spw = (p.nsub + want - 1) / want;
+    if (spw < 1)
+        spw = 1;
+    while ((p.nsub + spw - 1) / spw > kArgMaxChunks)
+        ++spw;
+    p.sub_per_wg = spw;
+    p.nchunk = (p.nsub + spw - 1) / spw;
+    return p;
+}
+
+size_t verify_workspace(int S, int B, int V, int /*dtype*/)
+{
+    const ArgPlan p = arg_plan(S * B, V);
+    const size_t parts = (size_t)S * B * p.nchunk;
+    return parts * (sizeof(uint64_t) + sizeof(uint32_t)) + 256;
+}
+
+jt_status launch_verify(const void *logits, int64_t row_stride, int V, int dtype,
+                        const int32_t *parent, const int32_t *tokens, const uint64_t *anc,
+                        const int32_t *depth, int S, int B, int N, int32_t *accept_len,
+                        int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                        int32_t *err, void *ws, hipStream_t st)
+{
+    if (S == 0)
+        return JT_OK;
+    const int rows = S * B;
+    const ArgPlan p = arg_plan(rows, V);
+    const size_t parts = (size_t)rows * p.nchunk;
+    uint64_t *wk = reinterpret_cast<uint64_t *>(ws);
+    uint32_t *wn = reinterpret_cast<uint32_t *>(wk + parts);
+    const dim3 grid((unsigned)parts), block(kArgThreads);
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
+    if (dtype == JT_BF16) {
+        if ((addr % 16 == 0) && (row_stride % 8 == 0))
+            hipLaunchKernelGGL((argmax_partial_kernel<uint16_t, true>), grid, block, 0, st,
+                               (const uint16_t *)logits, row_stride, V, p.nsub, p.sub_per_wg,
+                               p.nchunk, wk, wn);
+        else
+            hipLaunchKernelGGL((argmax_partial_kernel<uint16_t, false>), grid, block, 0, st,
+                               (const uint16_t *)logits, row_stride, V, p.nsub, p.sub_per_wg,
+                               p.nchunk, wk, wn);
+    } else {
+        if ((addr % 16 == 0) && (row_stride % 4 == 0))
+            hipLaunchKernelGGL((argmax_partial_kernel<float, true>), grid, block, 0, st,
+                               (const float *)logits, row_stride, V, p.nsub, p.sub_per_wg,
+                               p.nchunk, wk, wn);
+        else
+            hipLaunchKernelGGL((argmax_partial_kernel<float, false>), grid, block, 0, st,
+                               (const float *)logits, row_stride, V, p.nsub, p.sub_per_wg,
+                               p.nchunk, wk, wn);
+    }
+    jt_status e = launch_status(hipGetLastError());
+    if (e != JT_OK)
+        return e;
+    hipLaunchKernelGGL(verify_walk_kernel, dim3(S), dim3(256), 0, st, B, N, p.nchunk, wk, wn,
+                       parent, tokens, anc, depth, accept_len, accept_path, bonus, argmax_out,
+                       err);
+    return launch_status(hipGetLastError());
+}
+
+} // namespace jt
