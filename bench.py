@@ -1,0 +1,313 @@
+"""Benchmark: draft-verify steps/s of the tree step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = jt_topw_per_depth (draft logits) -> jt_build_tree_mask -> jt_tree_attention
+-> jt_verify_greedy (target logits), all sequences, one stream.  The tree (parent,
+tokens) is an input of the step, built by the seeded workload generator, and is not
+timed.  Inputs are resident in HBM before the timed region; input sets are rotated so
+that one rotation exceeds twice the 256 MB last-level cache (cold-cache figures).
+
+The JSON line reports the low-budget workload (B=16) as the headline and the
+high-budget workload (B=256) in "high_budget"; per-entry-point times come from HIP
+events recorded on the stream the kernels run on.  "cpu_baseline" times the CPU oracle
+(single thread) on full steps of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+LLC_BYTES = 256 << 20        # Infinity Cache
+CALLS = ("topw", "mask", "attention", "verify")
+KERNELS = {
+    "topw": ["topw_partial_kernel", "topw_merge_kernel"],
+    "mask": ["build_mask_kernel"],
+    "attention": ["attn_mfma_kernel", "attn_combine_kernel", "attn_simple_kernel"],
+    "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
+}
+
+
+def algorithmic(w):
+    """Bytes each entry point must move and the attention flops (visible keys only)."""
+    c = w.cfg
+    e = 4 if c.dtype == "f32" else 2
+    S, B, N, W, V = c.S, c.B, c.N, c.W, c.V
+    P = w.prefix_len.astype(np.int64)
+    b = {}
+    b["topw"] = S * N * V * e + S * N * W * 8 + S * N * 4
+    b["mask"] = S * B * (4 + 32 + 4) + S * 4
+    b["attention"] = (int(((P + B) * c.Hkv * c.d * 2 * e).sum()) + S * B * c.Hq * c.d * 2 * e
+                      + S * B * 32 + S * B * c.Hq * 4 + S * 4 * 2
+                      + (0 if w.block_table is None else int(np.ceil(P / c.block_size).sum()) * 4))
+    b["verify"] = S * B * V * e + S * B * (4 + 4 + 32 + 4 + 4) + S * (N + 1 + 3) * 4
+    vis = (P[:, None] + w.depth.astype(np.int64) + 1).sum()
+    flops = 4 * c.Hq * c.d * int(vis)
+    return b, flops
+
+
+class Rotation:
+    """Several copies of one step's inputs (same values) so reps do not hit in cache."""
+
+    def __init__(self, step, nsets):
+        import torch
+        self.steps = [step]
+        names = [n for n in ("draft", "q", "k_tree", "v_tree", "k_prefix", "v_prefix", "target")
+                 if hasattr(step, n)]
+        for _ in range(nsets - 1):
+            clone = object.__new__(type(step))
+            clone.__dict__.update(step.__dict__)
+            for n in names:
+                setattr(clone, n, getattr(step, n).clone())
+            self.steps.append(clone)
+        torch.cuda.synchronize()
+
+
+def footprint(step):
+    tot = 0
+    for n in ("draft", "q", "k_tree", "v_tree", "k_prefix", "v_prefix", "target"):
+        t = getattr(step, n, None)
+        if t is not None:
+            tot += t.numel() * t.element_size()
+    return tot
+
+
+def time_workload(name, steps, warmup, seed, use_graph=True, log=print):
+    import torch
+    from tree_causal_draft_amd import workload as wl
+    from tree_causal_draft_amd.step import DeviceStep
+
+    t0 = time.time()
+    w = wl.make(name, seed)
+    log(f"[bench] {name}: inputs generated in {time.time() - t0:.1f}s")
+    st = DeviceStep(w, "cuda:0")
+    fp = footprint(st)
+    nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(fp, 1))))
+    rot = Rotation(st, nsets)
+    log(f"[bench] {name}: footprint {fp / 1e6:.1f} MB per set, {nsets} sets rotated")
+    cur = torch.cuda.current_stream()
+
+    # ---- eager: per-entry-point events on the launch stream
+    for i in range(warmup):
+        rot.steps[i % nsets].run()
+    torch.cuda.synchronize()
+    ev = {c: [] for c in CALLS}
+    start_all = torch.cuda.Event(enable_timing=True)
+    end_all = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start_all.record(cur)
+    for i in range(steps):
+        s = rot.steps[i % nsets]
+        for c in CALLS:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            getattr(s, c)()
+            b.record(cur)
+            ev[c].append((a, b))
+    end_all.record(cur)
+    torch.cuda.synchronize()
+    wall_eager = time.perf_counter() - t_wall
+    eager_ms = start_all.elapsed_time(end_all) / steps
+    per_call_us = {c: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[c]])) for c in CALLS}
+    log(f"[bench] {name}: eager {eager_ms * 1e3:.1f} us/step " +
+        " ".join(f"{c}={per_call_us[c]:.1f}us" for c in CALLS))
+
+    # ---- hipGraph replay (one captured step per input set), checked against eager
+    graph_ms = None
+    graph_ok = None
+    if use_graph:
+        ref = st.accept_len.clone(), st.bonus.clone(), st.ids.clone(), st.attn_out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        graphs = []
+        with torch.cuda.stream(side):
+            for s in rot.steps:
+                s.run()
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        for s in rot.steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s.run()
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % nsets].replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        for i in range(steps):
+            graphs[i % nsets].replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / steps
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        got = st.accept_len, st.bonus, st.ids, st.attn_out
+        graph_ok = all(torch.equal(x, y) for x, y in zip(ref, got))
+        log(f"[bench] {name}: graph {graph_ms * 1e3:.1f} us/step, replay == eager: {graph_ok}")
+        del graphs
+
+    bytes_, flops = algorithmic(w)
+    calls = {}
+    for c in CALLS:
+        us = per_call_us[c]
+        calls[c] = {"us": round(us, 2), "bytes": int(bytes_[c]),
+                    "GBps": round(bytes_[c] / (us * 1e-6) / 1e9, 1)}
+    att_us = per_call_us["attention"]
+    calls["attention"]["TFLOPs"] = round(flops / (att_us * 1e-6) / 1e12, 2)
+    calls["attention"]["flops"] = int(flops)
+    res = dict(workload=name, w=w, eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok,
+               wall_eager=wall_eager, calls=calls, nsets=nsets, flops=flops, bytes=bytes_,
+               per_call_us=per_call_us, footprint=fp)
+    del rot, st
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline(res, call):
+    w = res["w"]
+    us = res["per_call_us"][call]
+    byt = res["bytes"][call]
+    if call == "attention":
+        ai = res["flops"] / byt
+        if ai > (MFMA_BF16_PEAK_TFS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.cfg.dtype == "bf16":
+            ach = res["flops"] / (us * 1e-6) / 1e12
+            return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                    "kernel": call, "kernels": KERNELS[call], "per_launch_us": round(us, 2)}
+    ach = byt / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": call,
+            "kernels": KERNELS[call], "per_launch_us": round(us, 2)}
+
+
+def cpu_baseline(name, seed, budget_s=20.0, log=print):
+    """The CPU oracle, single-threaded, on full steps of the same workload."""
+    import oracle
+    from tree_causal_draft_amd import workload as wl
+    w = wl.make(name, seed)
+    c = w.cfg
+    times = []
+    t_all = time.perf_counter()
+    while not times or (time.perf_counter() - t_all < budget_s and len(times) < 50):
+        t = time.perf_counter()
+        oracle.topw(w.draft_logits, c.W)
+        oracle.build_mask(w.parent)
+        oracle.tree_attention(w.q, w.k_tree, w.v_tree, w.k_prefix, w.v_prefix, w.prefix_len,
+                              w.parent, block_table=w.block_table, block_size=c.block_size,
+                              num_blocks=w.num_blocks, max_prefix=w.max_prefix)
+        oracle.verify_greedy(w.target_logits, w.parent, w.tokens, c.N)
+        times.append(time.perf_counter() - t)
+    sec = float(np.mean(times))
+    log(f"[bench] cpu oracle {name}: {sec:.2f} s/step over {len(times)} steps")
+    return {"value": round(1.0 / sec, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} full steps of {name} (seed {seed}), single thread",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="low_budget")
+    ap.add_argument("--secondary", default="high_budget", help="'' to skip")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how the step would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tree_causal_draft_amd as jt
+    from tree_causal_draft_amd import workload as wl
+    jt.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    seed_of = lambda n: 1000 * (wl.CONFIG_ORDER.index(n) + 1)
+
+    prim = time_workload(args.workload, args.steps, args.warmup, seed_of(args.workload),
+                         use_graph=not args.no_graph, log=log)
+    sec = None
+    if args.secondary:
+        sec = time_workload(args.secondary, args.steps, args.warmup, seed_of(args.secondary),
+                            use_graph=not args.no_graph, log=log)
+    cpu = None if args.no_cpu else cpu_baseline(args.workload, seed_of(args.workload),
+                                                args.cpu_seconds, log=log)
+
+    def step_ms(r):
+        return r["graph_ms"] if (r["graph_ms"] is not None and r["graph_ok"]) else r["eager_ms"]
+
+    ms = step_ms(prim)
+    dom = max(CALLS, key=lambda c: prim["per_call_us"][c])
+    c = prim["w"].cfg
+    line = {
+        "metric": "draft-verify steps/s + tree-attn HBM GB/s / MFMA % at B=16,256 (1xMI355X)",
+        "value": round(1e3 / ms, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic (seeded; tree prebuilt, not timed)",
+        "config": {"workload": f"{c.name}: S={c.S} prefix={c.prefix} B={c.B} N={c.N} W={c.W} "
+                               f"heads {c.Hq}/{c.Hkv} d={c.d} V={c.V} {c.dtype}",
+                   "timing": "hipGraph replay" if step_ms(prim) == prim["graph_ms"] else "eager",
+                   "cold_sets": prim["nsets"]},
+        "eager_steps_per_s": round(1e3 / prim["eager_ms"], 1),
+        "graph_steps_per_s": None if prim["graph_ms"] is None else round(1e3 / prim["graph_ms"], 1),
+        "graph_matches_eager": prim["graph_ok"],
+        "calls": prim["calls"],
+        "roofline": roofline(prim, dom),
+        "attention_roofline": roofline(prim, "attention"),
+        "cpu_baseline": cpu,
+    }
+    if sec is not None:
+        sc = sec["w"].cfg
+        line["high_budget"] = {
+            "workload": f"{sc.name}: S={sc.S} prefix={sc.prefix} B={sc.B} N={sc.N} W={sc.W} "
+                        f"heads {sc.Hq}/{sc.Hkv} d={sc.d}",
+            "steps_per_s": round(1e3 / step_ms(sec), 1),
+            "eager_steps_per_s": round(1e3 / sec["eager_ms"], 1),
+            "calls": sec["calls"],
+            "attention_roofline": roofline(sec, "attention"),
+            "roofline": roofline(sec, max(CALLS, key=lambda k: sec["per_call_us"][k])),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
