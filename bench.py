@@ -83,7 +83,45 @@ def footprint(step):
     return tot
 
 
-def time_workload(name, steps, warmup, seed, use_graph=True, log=print):
+def _capture(fns):
+    """One hipGraph that runs every callable in ``fns`` in order on a capture stream."""
+    import torch
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_graph(g, launches_per_replay, total_launches, warmup):
+    """Average time per launch (us): the graph replayed back-to-back on the current stream,
+    bracketed by HIP events on that stream."""
+    import torch
+    cur = torch.cuda.current_stream()
+    for _ in range(max(1, warmup // max(1, launches_per_replay))):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(total_launches / launches_per_replay))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(cur)
+    for _ in range(reps):
+        g.replay()
+    b.record(cur)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / (reps * launches_per_replay), reps * launches_per_replay
+
+
+def time_workload(name, steps, warmup, seed, log=print):
     import torch
     from tree_causal_draft_amd import workload as wl
     from tree_causal_draft_amd.step import DeviceStep
@@ -98,81 +136,52 @@ def time_workload(name, steps, warmup, seed, use_graph=True, log=print):
     log(f"[bench] {name}: footprint {fp / 1e6:.1f} MB per set, {nsets} sets rotated")
     cur = torch.cuda.current_stream()
 
-    # ---- eager: per-entry-point events on the launch stream
-    for i in range(warmup):
+    # ---- eager reference run (also the graph-vs-eager check)
+    for i in range(max(warmup, nsets)):
         rot.steps[i % nsets].run()
     torch.cuda.synchronize()
-    ev = {c: [] for c in CALLS}
-    start_all = torch.cuda.Event(enable_timing=True)
-    end_all = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start_all.record(cur)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(cur)
     for i in range(steps):
-        s = rot.steps[i % nsets]
-        for c in CALLS:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(cur)
-            getattr(s, c)()
-            b.record(cur)
-            ev[c].append((a, b))
-    end_all.record(cur)
+        rot.steps[i % nsets].run()
+    b.record(cur)
     torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t_wall
-    eager_ms = start_all.elapsed_time(end_all) / steps
-    per_call_us = {c: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[c]])) for c in CALLS}
-    log(f"[bench] {name}: eager {eager_ms * 1e3:.1f} us/step " +
-        " ".join(f"{c}={per_call_us[c]:.1f}us" for c in CALLS))
+    eager_us = 1e3 * a.elapsed_time(b) / steps
+    ref = [t.clone() for t in (st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob,
+                               st.attn_out, st.anc)]
 
-    # ---- hipGraph replay (one captured step per input set), checked against eager
-    graph_ms = None
-    graph_ok = None
-    if use_graph:
-        ref = st.accept_len.clone(), st.bonus.clone(), st.ids.clone(), st.attn_out.clone()
-        side = torch.cuda.Stream()
-        side.wait_stream(cur)
-        graphs = []
-        with torch.cuda.stream(side):
-            for s in rot.steps:
-                s.run()
-        cur.wait_stream(side)
-        torch.cuda.synchronize()
-        for s in rot.steps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                s.run()
-            graphs.append(g)
-        for i in range(warmup):
-            graphs[i % nsets].replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(cur)
-        for i in range(steps):
-            graphs[i % nsets].replay()
-        b.record(cur)
-        torch.cuda.synchronize()
-        graph_ms = a.elapsed_time(b) / steps
-        graphs[0].replay()
-        torch.cuda.synchronize()
-        got = st.accept_len, st.bonus, st.ids, st.attn_out
-        graph_ok = all(torch.equal(x, y) for x, y in zip(ref, got))
-        log(f"[bench] {name}: graph {graph_ms * 1e3:.1f} us/step, replay == eager: {graph_ok}")
-        del graphs
+    # ---- whole step: one graph holding one step per input set, replayed back-to-back
+    g = _capture([s.run for s in rot.steps])
+    step_us, nsteps = _time_graph(g, nsets, steps, warmup)
+    g.replay()
+    torch.cuda.synchronize()
+    got = [st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob, st.attn_out, st.anc]
+    graph_ok = all(torch.equal(x, y) for x, y in zip(ref, got))
+    del g
+    log(f"[bench] {name}: eager {eager_us:.1f} us/step, graph {step_us:.1f} us/step "
+        f"({nsteps} steps), replay == eager: {graph_ok}")
+
+    # ---- each entry point alone: one graph of nsets launches (one per cold input set)
+    per_call_us = {}
+    for c in CALLS:
+        g = _capture([getattr(s, c) for s in rot.steps])
+        per_call_us[c], _ = _time_graph(g, nsets, steps, warmup)
+        del g
+    log(f"[bench] {name}: per call " + " ".join(f"{c}={per_call_us[c]:.2f}us" for c in CALLS))
 
     bytes_, flops = algorithmic(w)
     calls = {}
     for c in CALLS:
         us = per_call_us[c]
-        calls[c] = {"us": round(us, 2), "bytes": int(bytes_[c]),
+        calls[c] = {"us": round(us, 3), "bytes": int(bytes_[c]),
                     "GBps": round(bytes_[c] / (us * 1e-6) / 1e9, 1)}
     att_us = per_call_us["attention"]
     calls["attention"]["TFLOPs"] = round(flops / (att_us * 1e-6) / 1e12, 2)
     calls["attention"]["flops"] = int(flops)
-    res = dict(workload=name, w=w, eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok,
-               wall_eager=wall_eager, calls=calls, nsets=nsets, flops=flops, bytes=bytes_,
-               per_call_us=per_call_us, footprint=fp)
+    res = dict(workload=name, w=w, eager_us=eager_us, step_us=step_us, graph_ok=graph_ok,
+               calls=calls, nsets=nsets, flops=flops, bytes=bytes_, per_call_us=per_call_us,
+               footprint=fp)
     del rot, st
     torch.cuda.empty_cache()
     return res
@@ -229,15 +238,46 @@ def _cpu_model():
     return None
 
 
+def _kernel_hash(call):
+    import hashlib
+    files = {"topw": ["topw.hip"], "mask": ["mask.hip"], "attention": ["attn.hip"],
+             "verify": ["verify.hip"]}[call]
+    h = hashlib.sha256()
+    for f in files + ["jt_internal.h"]:
+        with open(os.path.join(ROOT, "tree_causal_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(workload, call):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel factor), or None when no summary exists or the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)["entries"][workload][call]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("src_sha") != _kernel_hash(call):
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def roofline_line(res, call):
+    r = roofline(res, call)
+    r["traffic"] = traffic(res["workload"], call)
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="low_budget")
     ap.add_argument("--secondary", default="high_budget", help="'' to skip")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,56 +295,54 @@ def main():
     log = lambda m: print(m, file=sys.stderr, flush=True)
     seed_of = lambda n: 1000 * (wl.CONFIG_ORDER.index(n) + 1)
 
-    prim = time_workload(args.workload, args.steps, args.warmup, seed_of(args.workload),
-                         use_graph=not args.no_graph, log=log)
-    sec = None
-    if args.secondary:
-        sec = time_workload(args.secondary, args.steps, args.warmup, seed_of(args.secondary),
-                            use_graph=not args.no_graph, log=log)
+    results = [time_workload(args.workload, args.steps, args.warmup, seed_of(args.workload),
+                             log=log)]
+    for name in [n for n in args.secondary.split(",") if n]:
+        results.append(time_workload(name, args.steps, args.warmup, seed_of(name), log=log))
     cpu = None if args.no_cpu else cpu_baseline(args.workload, seed_of(args.workload),
                                                 args.cpu_seconds, log=log)
 
-    def step_ms(r):
-        return r["graph_ms"] if (r["graph_ms"] is not None and r["graph_ok"]) else r["eager_ms"]
+    def summary(r):
+        c = r["w"].cfg
+        return f"{c.name}: S={c.S} prefix={c.prefix} B={c.B} N={c.N} W={c.W} " \
+               f"heads {c.Hq}/{c.Hkv} d={c.d} V={c.V} {c.dtype}"
 
-    ms = step_ms(prim)
-    dom = max(CALLS, key=lambda c: prim["per_call_us"][c])
+    prim = results[0]
+    us = prim["step_us"]
+    dom = max(CALLS, key=lambda k: prim["per_call_us"][k])
     c = prim["w"].cfg
     line = {
         "metric": "draft-verify steps/s + tree-attn HBM GB/s / MFMA % at B=16,256 (1xMI355X)",
-        "value": round(1e3 / ms, 1),
+        "value": round(1e6 / us, 1),
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(us * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": c.dtype,
         "data": "synthetic (seeded; tree prebuilt, not timed)",
-        "config": {"workload": f"{c.name}: S={c.S} prefix={c.prefix} B={c.B} N={c.N} W={c.W} "
-                               f"heads {c.Hq}/{c.Hkv} d={c.d} V={c.V} {c.dtype}",
-                   "timing": "hipGraph replay" if step_ms(prim) == prim["graph_ms"] else "eager",
+        "config": {"workload": summary(prim),
+                   "timing": "hipGraph replay of one step per cold input set",
                    "cold_sets": prim["nsets"]},
-        "eager_steps_per_s": round(1e3 / prim["eager_ms"], 1),
-        "graph_steps_per_s": None if prim["graph_ms"] is None else round(1e3 / prim["graph_ms"], 1),
+        "eager_steps_per_s": round(1e6 / prim["eager_us"], 1),
         "graph_matches_eager": prim["graph_ok"],
         "calls": prim["calls"],
-        "roofline": roofline(prim, dom),
-        "attention_roofline": roofline(prim, "attention"),
+        "roofline": roofline_line(prim, dom),
+        "attention_roofline": roofline_line(prim, "attention"),
         "cpu_baseline": cpu,
     }
-    if sec is not None:
-        sc = sec["w"].cfg
-        line["high_budget"] = {
-            "workload": f"{sc.name}: S={sc.S} prefix={sc.prefix} B={sc.B} N={sc.N} W={sc.W} "
-                        f"heads {sc.Hq}/{sc.Hkv} d={sc.d}",
-            "steps_per_s": round(1e3 / step_ms(sec), 1),
-            "eager_steps_per_s": round(1e3 / sec["eager_ms"], 1),
-            "calls": sec["calls"],
-            "attention_roofline": roofline(sec, "attention"),
-            "roofline": roofline(sec, max(CALLS, key=lambda k: sec["per_call_us"][k])),
+    for r in results[1:]:
+        line[r["workload"]] = {
+            "workload": summary(r),
+            "steps_per_s": round(1e6 / r["step_us"], 1),
+            "eager_steps_per_s": round(1e6 / r["eager_us"], 1),
+            "graph_matches_eager": r["graph_ok"],
+            "calls": r["calls"],
+            "attention_roofline": roofline_line(r, "attention"),
+            "roofline": roofline_line(r, max(CALLS, key=lambda k: r["per_call_us"][k])),
         }
     print(json.dumps(line), flush=True)
 

@@ -14,7 +14,10 @@
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never
  *     allocates, frees or keeps any of them after the call returns.
  *   - Scratch memory is passed in as `workspace` after a *_workspace_size() query; a
- *     NULL workspace is allowed only when the query returns 0.
+ *     NULL workspace is allowed only when the query returns 0.  A workspace must be
+ *     zero-filled before its first use (it holds arrival counters); every call leaves it
+ *     zero-filled again, so one zero-fill at allocation is enough.  Calls that overlap in
+ *     time need distinct workspaces.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous and
  *     stream-ordered; outputs are valid once the stream reaches them.  No call
  *     synchronises the host.  The library holds no state: concurrent calls on
@@ -111,14 +114,17 @@ jt_status jt_build_tree_mask(const int32_t *parent, int32_t S, int32_t B, uint64
  *   out               [S,B,Hq,d] dtype.
  *   lse               float [S,B,Hq] (optional): natural-log sum of exp of the scaled
  *                     visible scores.
- *   err               int32 [S] (optional): JT_DEV_BAD_PREFIX, JT_DEV_BAD_BLOCK; keys of
- *                     an out-of-pool block are skipped.
+ *   err               int32 [S] (optional): JT_DEV_BAD_PREFIX, JT_DEV_BAD_BLOCK (the
+ *                     flagged sequence's output is unspecified; nothing outside the
+ *                     pool is read).
  * Supported: d in {64,128}; Hq % Hkv == 0 and 1 <= Hq/Hkv <= 8; 1 <= B <= 256;
  * block_size a power of two; dtype JT_BF16 or JT_F32; q/k/v/out 16-byte aligned.
  * bf16 runs on MFMA (fp32 accumulate, bf16 out); fp32 runs on the vector ALU.
  */
+/* block_size: the paged pool's block size, or 0 for a contiguous prefix. */
 size_t jt_tree_attention_workspace_size(int32_t S, int32_t B, int32_t Hq, int32_t Hkv,
-                                        int32_t d, int32_t max_prefix, jt_dtype dtype);
+                                        int32_t d, int32_t max_prefix, int32_t block_size,
+                                        jt_dtype dtype);
 jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tree,
                             const void *k_prefix, const void *v_prefix,
                             const int32_t *block_table, int32_t max_blocks_per_seq,

@@ -47,7 +47,7 @@ def lib() -> ctypes.CDLL:
         L.jt_status_string.argtypes = [ctypes.c_int]
         L.jt_build_tree_mask.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp, _vp]
         L.jt_tree_attention_workspace_size.restype = _sz
-        L.jt_tree_attention_workspace_size.argtypes = [_i32] * 6 + [ctypes.c_int]
+        L.jt_tree_attention_workspace_size.argtypes = [_i32] * 7 + [ctypes.c_int]
         L.jt_tree_attention.argtypes = ([_vp] * 6 + [_i32, _i32, _i32, _vp, _i32, _vp] +
                                         [_i32] * 5 + [ctypes.c_int, ctypes.c_float, _vp, _vp, _vp,
                                                       _vp, _sz, _vp])
@@ -101,7 +101,8 @@ def _workspace(nbytes: int, device, workspace):
         return None, 0
     if workspace is not None:
         return workspace, workspace.numel() * workspace.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    # zero-filled once: the library keeps its arrival counters at zero between calls
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def build_tree_mask(parent, anc=None, depth=None, err=None, stream=None):
@@ -117,8 +118,10 @@ def build_tree_mask(parent, anc=None, depth=None, err=None, stream=None):
     return anc, depth, err
 
 
-def tree_attention_workspace_size(S, B, Hq, Hkv, d, max_prefix, dtype) -> int:
-    return int(lib().jt_tree_attention_workspace_size(S, B, Hq, Hkv, d, max_prefix, dtype))
+def tree_attention_workspace_size(S, B, Hq, Hkv, d, max_prefix, dtype, block_size=0) -> int:
+    """block_size: paged pool block size, 0 for a contiguous prefix."""
+    return int(lib().jt_tree_attention_workspace_size(S, B, Hq, Hkv, d, max_prefix, block_size,
+                                                      dtype))
 
 
 def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, prefix_len, anc, *, block_table=None,
@@ -144,7 +147,8 @@ def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, prefix_len, anc, *, bl
     if lse is None and want_lse:
         lse = torch.empty((S, B, Hq), dtype=torch.float32, device=dev)
     err = torch.empty(S, dtype=torch.int32, device=dev) if err is None else err
-    need = tree_attention_workspace_size(S, B, Hq, Hkv, d, Pmax, dt)
+    need = tree_attention_workspace_size(S, B, Hq, Hkv, d, Pmax, dt,
+                                         0 if block_table is None else block_size)
     ws, wsb = _workspace(need, dev, workspace)
     _check(lib().jt_tree_attention(_ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
                                    _ptr(v_prefix), _ptr(block_table), maxblk, block_size, nblk,

@@ -34,6 +34,22 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 
 
+# Kernels whose software pipeline counts outstanding loads exactly (s_waitcnt vmcnt(N)):
+# a register spill would add scratch loads to that count, so the build refuses one.
+NO_SCRATCH = {"attn.hip": "attn_bf16_kernel"}
+
+
+def _scratch_violations(stderr: str, kernel: str):
+    bad, fn = [], None
+    for ln in stderr.splitlines():
+        if "Function Name:" in ln:
+            fn = ln.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in ln and fn and kernel in fn:
+            if int(ln.split("ScratchSize [bytes/lane]:")[1].split()[0]) != 0:
+                bad.append(fn)
+    return bad
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -42,11 +58,17 @@ def build(verbose: bool = False) -> str:
         path = os.path.join(CSRC, src)
         obj = os.path.join(BUILD, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *FLAGS, *lang, "-c", path, "-o", obj]
+        extra = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SCRATCH else []
+        cmd = [cc, *FLAGS, *extra, *lang, "-c", path, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
-        noise = [ln for ln in (res.stderr or "").splitlines() if "packed-fp32-ops" not in ln]
+        noise = [ln for ln in (res.stderr or "").splitlines()
+                 if "packed-fp32-ops" not in ln and "remark:" not in ln]
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(noise))
+        if src in NO_SCRATCH:
+            bad = _scratch_violations(res.stderr or "", NO_SCRATCH[src])
+            if bad:
+                raise RuntimeError(f"{src}: kernels spill to scratch: {bad}")
         if verbose and noise:
             print("\n".join(noise), file=sys.stderr)
         objs.append(obj)

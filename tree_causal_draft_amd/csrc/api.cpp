@@ -68,11 +68,13 @@ static jt_status attn_shape(int32_t S, int32_t B, int32_t Hq, int32_t Hkv, int32
 }
 
 size_t jt_tree_attention_workspace_size(int32_t S, int32_t B, int32_t Hq, int32_t Hkv,
-                                        int32_t d, int32_t max_prefix, jt_dtype dtype)
+                                        int32_t d, int32_t max_prefix, int32_t block_size,
+                                        jt_dtype dtype)
 {
     if (attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype) != JT_OK || S == 0)
         return 0;
-    return attention_workspace(S, B, Hq, Hkv, d, max_prefix, dtype);
+    return attention_workspace(S, B, Hq, Hkv, d, max_prefix, block_size > 0 ? block_size : 0,
+                               dtype);
 }
 
 jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tree,
@@ -101,7 +103,8 @@ jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tre
     if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
         (k_prefix && !aligned16(k_prefix)) || (v_prefix && !aligned16(v_prefix)))
         return JT_ERR_ALIGN;
-    const size_t need = attention_workspace(S, B, Hq, Hkv, d, max_prefix, dtype);
+    const size_t need =
+        attention_workspace(S, B, Hq, Hkv, d, max_prefix, block_table ? block_size : 0, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return JT_ERR_WORKSPACE;
     if (need > 0 && !aligned16(workspace))

@@ -103,7 +103,8 @@ struct AttnArgs {
     float *lse;
     int32_t *err;
 };
-size_t attention_workspace(int S, int B, int Hq, int Hkv, int d, int max_prefix, int dtype);
+size_t attention_workspace(int S, int B, int Hq, int Hkv, int d, int max_prefix, int block_size,
+                           int dtype);
 jt_status launch_attention(const AttnArgs &a, void *ws, hipStream_t st);
 
 } // namespace jt

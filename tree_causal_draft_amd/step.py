@@ -50,16 +50,17 @@ class DeviceStep:
             self.attn_out = torch.empty_like(self.q)
             self.lse = torch.empty((S, B, cfg.Hq), dtype=torch.float32, device=dev)
             self.err_attn = torch.empty(S, dtype=torch.int32, device=dev)
-            nb = self.attn_ws_bytes = tree_attention_workspace_size(S, B, cfg.Hq, cfg.Hkv, cfg.d,
-                                                                    w.max_prefix, dt)
-            self.attn_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev) if nb else None
+            nb = self.attn_ws_bytes = tree_attention_workspace_size(
+                S, B, cfg.Hq, cfg.Hkv, cfg.d, w.max_prefix, dt,
+                cfg.block_size if w.block_table is not None else 0)
+            self.attn_ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev) if nb else None
         if "topw" in parts:
             self.draft = to_device(w.draft_logits, dev)
             self.ids = torch.empty((S * N, W), dtype=torch.int32, device=dev)
             self.logprob = torch.empty((S * N, W), dtype=torch.float32, device=dev)
             self.row_lse = torch.empty(S * N, dtype=torch.float32, device=dev)
             nb = topw_workspace_size(S * N, cfg.V, W, dt)
-            self.topw_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.topw_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
         if "verify" in parts:
             self.target = to_device(w.target_logits, dev)
             self.accept_len = torch.empty(S, dtype=torch.int32, device=dev)
@@ -68,7 +69,7 @@ class DeviceStep:
             self.argmax = torch.empty((S, B), dtype=torch.int32, device=dev)
             self.err_verify = torch.empty(S, dtype=torch.int32, device=dev)
             nb = verify_workspace_size(S, B, cfg.V, dt)
-            self.verify_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.verify_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
 
     # ---- the four calls
     def topw(self):
