@@ -151,16 +151,28 @@ def time_workload(name, steps, warmup, seed, log=print):
     ref = [t.clone() for t in (st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob,
                                st.attn_out, st.anc)]
 
-    # ---- whole step: one graph holding one step per input set, replayed back-to-back
-    g = _capture([s.run for s in rot.steps])
-    step_us, nsteps = _time_graph(g, nsets, steps, warmup)
-    g.replay()
-    torch.cuda.synchronize()
-    got = [st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob, st.attn_out, st.anc]
-    graph_ok = all(torch.equal(x, y) for x, y in zip(ref, got))
-    del g
-    log(f"[bench] {name}: eager {eager_us:.1f} us/step, graph {step_us:.1f} us/step "
-        f"({nsteps} steps), replay == eager: {graph_ok}")
+    # ---- whole step: one graph holding one step per input set, replayed back-to-back;
+    # once with the four calls on one stream, once with their independence exposed
+    # (top-W and verification on side streams), which is the reported figure
+    def graph_step(fn_name):
+        g = _capture([getattr(s, fn_name) for s in rot.steps])
+        us, n = _time_graph(g, nsets, steps, warmup)
+        for t in got_bufs():
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = all(torch.equal(x, y) for x, y in zip(ref, got_bufs()))
+        del g
+        return us, n, ok
+
+    def got_bufs():
+        return [st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob, st.attn_out, st.anc]
+
+    serial_us, nsteps, serial_ok = graph_step("run")
+    step_us, nsteps, conc_ok = graph_step("run_concurrent")
+    graph_ok = serial_ok and conc_ok
+    log(f"[bench] {name}: eager {eager_us:.1f} us/step, graph one-stream {serial_us:.1f} us/step, "
+        f"graph concurrent {step_us:.1f} us/step ({nsteps} steps), replay == eager: {graph_ok}")
 
     # ---- each entry point alone: one graph of nsets launches (one per cold input set)
     per_call_us = {}
@@ -179,7 +191,8 @@ def time_workload(name, steps, warmup, seed, log=print):
     att_us = per_call_us["attention"]
     calls["attention"]["TFLOPs"] = round(flops / (att_us * 1e-6) / 1e12, 2)
     calls["attention"]["flops"] = int(flops)
-    res = dict(workload=name, w=w, eager_us=eager_us, step_us=step_us, graph_ok=graph_ok,
+    res = dict(workload=name, w=w, eager_us=eager_us, step_us=step_us, serial_us=serial_us,
+               graph_ok=graph_ok,
                calls=calls, nsets=nsets, flops=flops, bytes=bytes_, per_call_us=per_call_us,
                footprint=fp)
     del rot, st
@@ -325,9 +338,11 @@ def main():
         "dtype": c.dtype,
         "data": "synthetic (seeded; tree prebuilt, not timed)",
         "config": {"workload": summary(prim),
-                   "timing": "hipGraph replay of one step per cold input set",
+                   "timing": "hipGraph replay of one step per cold input set; top-W and "
+                             "verification on side streams",
                    "cold_sets": prim["nsets"]},
         "eager_steps_per_s": round(1e6 / prim["eager_us"], 1),
+        "one_stream_graph_steps_per_s": round(1e6 / prim["serial_us"], 1),
         "graph_matches_eager": prim["graph_ok"],
         "calls": prim["calls"],
         "roofline": roofline_line(prim, dom),
@@ -339,6 +354,7 @@ def main():
             "workload": summary(r),
             "steps_per_s": round(1e6 / r["step_us"], 1),
             "eager_steps_per_s": round(1e6 / r["eager_us"], 1),
+            "one_stream_graph_steps_per_s": round(1e6 / r["serial_us"], 1),
             "graph_matches_eager": r["graph_ok"],
             "calls": r["calls"],
             "attention_roofline": roofline_line(r, "attention"),

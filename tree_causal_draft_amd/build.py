@@ -9,6 +9,7 @@ it does not know that feature, which is harmless.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -62,7 +63,8 @@ def build(verbose: bool = False) -> str:
         cmd = [cc, *FLAGS, *extra, *lang, "-c", path, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         noise = [ln for ln in (res.stderr or "").splitlines()
-                 if "packed-fp32-ops" not in ln and "remark:" not in ln]
+                 if "packed-fp32-ops" not in ln and "remark:" not in ln
+                 and not re.match(r"^\s*(\d+\s*)?\|", ln)]
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(noise))
         if src in NO_SCRATCH:

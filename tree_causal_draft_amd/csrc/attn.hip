@@ -13,24 +13,24 @@
 //
 // bf16 -> attn_bf16_kernel (MFMA).  The G query heads of a KV group times the B nodes
 // form the rows of one dense problem (row r = node r / G, head r % G), so one K/V tile
-// in LDS serves every row of the workgroup.  A wave owns 64 rows (two 32-row blocks)
-// and runs, per 64-key tile,
+// in LDS serves every row of the workgroup.  A wave owns 32 rows and runs, per 64-key
+// tile,
 //   S^T = K . Q^T     v_mfma_f32_32x32x16_bf16; K rows from LDS (one 16-byte read per
 //                     lane), Q^T fragments held in registers for the whole kernel;
-//   online softmax    exp2 domain; a lane holds one row and 32 of the tile's keys, the
-//                     other 32 sit in lane ^ 32;
+//   online softmax    exp2 domain, lazily moved reference maximum; a lane holds one row
+//                     and 32 of the tile's keys, the other 32 sit in lane ^ 32;
 //   O^T += V^T . P^T  P^T is the S^T accumulator converted to bf16 in place (the key
 //                     order of the accumulator layout is applied to the V reads), V^T
 //                     fragments come from row-major V in LDS through ds_read_b64_tr_b16.
 // K/V tiles are copied HBM -> LDS by global_load_lds_dwordx4 (no register staging)
-// into rows whose 16-byte segments are XOR-swizzled, which keeps both the K reads (16
-// rows x 16 bytes) and the transposing V reads (4 rows x 32 bytes) free of bank
-// conflicts.  A workgroup (4 waves) is NWR row blocks of 64 x NWK key columns:
-//   NWR = 4: 256 rows share one double-buffered tile stream;
-//   NWR = 1, 2: the waves of a column walk their own tiles and merge in LDS at the end.
-// Work that still leaves the chip idle is split over keys (split-KV): each chunk writes
-// an unnormalised fp32 partial (O, running max, running sum) and attn_combine_kernel
-// merges them.
+// into rows whose 16-byte segments are XOR-swizzled, which keeps both the K reads and
+// the transposing V reads free of bank conflicts.  A workgroup is 2, 4 or 8 waves (64,
+// 128 or 256 rows) sharing one tile stream: 8 waves run two half-tile-apart groups over
+// 4 stages (ping-pong: one wave's softmax under the other's MFMAs), fewer waves double
+// buffer.  All LDS reads of tiles are inline asm and only tile copies are in flight in
+// the loop, so each wait is an exact vmcnt.  Keys are split over workgroups
+// (split-KV) until the chip is covered; each chunk writes a normalised bf16 partial with
+// its (max, sum) and attn_combine_kernel merges them.
 //
 // fp32 -> attn_simple_kernel: one workgroup per (s, v, g) on the vector ALU.
 #include <type_traits>
@@ -251,24 +251,23 @@ constexpr int kBtCap = 1024;  // block-table entries of one chunk staged in LDS
 
 // Work decomposition shared by the host launcher and the kernels.
 struct AttnPlan {
-    int nwr;       // 32-row waves per key column (2, 4 or 8); key columns = 8 / nwr
+    int nwr;       // waves per workgroup, one 32-row block each (2, 4 or 8)
     int rt;        // rows per workgroup = 32 * nwr
     int n_rtiles;  // row tiles per (s, g)
     int units;     // S * Hkv * n_rtiles
-    int ch;        // keys per chunk (multiple of 64 * key columns)
+    int ch;        // keys per chunk (multiple of 64)
     int n_chunks;  // chunks per unit (1 = no split-KV)
     int remap;     // 1: place consecutive work items on one XCD
-    int fused;     // split-KV partials merged in-kernel by the unit's last workgroup
 };
 
-// Split-KV workspace: per-unit arrival counters, then (m, l) per partial row, then the
-// partial rows themselves (normalised, bf16).
+// Split-KV workspace: (m, l) per partial row, then the partial rows themselves
+// (normalised, bf16).  A merge inside the main kernel by the last-arriving workgroup
+// would need device-scope fences, which write back a whole L2 and cost more than the
+// separate merge pass.
 struct AttnWs {
-    int *cnt;
     float2 *ml;
     uint16_t *o;
 };
-constexpr size_t kCntBytes = 256;  // granularity of the counter block
 
 static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int block_size)
 {
@@ -278,11 +277,12 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     p.rt = 32 * p.nwr;
     p.n_rtiles = (rows + p.rt - 1) / p.rt;
     p.units = S * Hkv * p.n_rtiles;
-    const int kcol = 8 / p.nwr;
-    const int gran = 64 * kcol;
+    const int gran = 64;
     const int keys = max_prefix + B;
     const int maxc = (keys + gran - 1) / gran;
-    int want = (256 + p.units - 1) / p.units;
+    // 8-wave workgroups hold 128 KB of LDS (one per CU); the smaller ones two per CU
+    const int target = p.nwr == 8 ? 256 : 512;
+    int want = (target + p.units - 1) / p.units;
     if (want > maxc)
         want = maxc;
     if (want < 1)
@@ -299,9 +299,6 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     p.n_chunks = (keys + ch - 1) / ch;
     const long grid = (long)p.units * p.n_chunks;
     p.remap = (grid % 8 == 0) ? 1 : 0;
-    // A last-arriving-workgroup merge needs device-scope fences, which write back the whole
-    // L2 and cost more than a second launch here: the merge is always a separate pass.
-    p.fused = 0;
     return p;
 }
 
@@ -310,21 +307,18 @@ static size_t attn_ws_bytes(const AttnPlan &p, int d)
     if (p.n_chunks <= 1)
         return 0;
     const size_t slots = (size_t)p.units * p.n_chunks * p.rt;
-    const size_t cnt = ((size_t)p.units * sizeof(int) + kCntBytes - 1) / kCntBytes * kCntBytes;
-    return cnt + slots * sizeof(float2) + slots * (size_t)d * 2;
+    return slots * sizeof(float2) + slots * (size_t)d * 2;
 }
 
 static AttnWs attn_ws_split(const AttnPlan &p, void *ws)
 {
-    AttnWs w{nullptr, nullptr, nullptr};
+    AttnWs w{nullptr, nullptr};
     if (p.n_chunks <= 1 || !ws)
         return w;
     const size_t slots = (size_t)p.units * p.n_chunks * p.rt;
-    const size_t cnt = ((size_t)p.units * sizeof(int) + kCntBytes - 1) / kCntBytes * kCntBytes;
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
-    w.cnt = reinterpret_cast<int *>(b);
-    w.ml = reinterpret_cast<float2 *>(b + cnt);
-    w.o = reinterpret_cast<uint16_t *>(b + cnt + slots * sizeof(float2));
+    w.ml = reinterpret_cast<float2 *>(b);
+    w.o = reinterpret_cast<uint16_t *>(b + slots * sizeof(float2));
     return w;
 }
 
@@ -351,6 +345,15 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, void *ldst)
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// Returns v unchanged but opaque to the compiler, so values derived from it are computed
+// where they are used instead of being hoisted out of the tile loop (once per unrolled
+// pipeline stage) and held in registers.
+template <typename T> __device__ __forceinline__ T opaque(T v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
 
 __device__ __forceinline__ uint32_t lds_off(const void *p)
 {
@@ -414,26 +417,43 @@ __device__ void attn_merge_unit(const AttnArgs &a, const AttnPlan &pl, const Att
         const int r = rt * pl.rt + rl;
         if (r >= G * B)
             continue;
+        // Chunks are read 8 at a time with every load of a batch issued before any is used,
+        // and folded with an online max (one pass).  The reads do not wait for the prefix
+        // length (inactive chunks' slots lie inside the workspace); a chunk k >= nact is
+        // dropped by selection, never multiplied in, since its bytes are stale.
         const int64_t base = (int64_t)unit * pl.n_chunks * pl.rt + rl;
-        float M = -INFINITY;
-        for (int k = 0; k < nact; ++k)
-            M = fmaxf(M, w.ml[base + (int64_t)k * pl.rt].x);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < nact; ++k) {
-            const int64_t slot = base + (int64_t)k * pl.rt;
-            const float2 ml = w.ml[slot];
-            const float wk = __builtin_amdgcn_exp2f(ml.x - Mu) * ml.y;
-            l += wk;
-            const uint4 u = *reinterpret_cast<const uint4 *>(w.o + slot * D + sgm * 8);
-            acc[0] += wk * bf16_lo(u.x);
-            acc[1] += wk * bf16_hi(u.x);
-            acc[2] += wk * bf16_lo(u.y);
-            acc[3] += wk * bf16_hi(u.y);
-            acc[4] += wk * bf16_lo(u.z);
-            acc[5] += wk * bf16_hi(u.z);
-            acc[6] += wk * bf16_lo(u.w);
-            acc[7] += wk * bf16_hi(u.w);
+        float M = -INFINITY, l = 0.f;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < pl.n_chunks; k0 += 8) {
+            float2 ml[8];
+            uint4 u[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int k = min(k0 + q, pl.n_chunks - 1);
+                const int64_t slot = base + (int64_t)k * pl.rt;
+                ml[q] = w.ml[slot];
+                u[q] = *reinterpret_cast<const uint4 *>(w.o + slot * D + sgm * 8);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bool use = k0 + q < nact && k0 + q < pl.n_chunks;
+                const float mk = use ? ml[q].x : -INFINITY;
+                if (mk == -INFINITY)
+                    continue;  // inactive chunk, or no visible key in it
+                const float Mn = fmaxf(M, mk);
+                const float sc = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M = -inf
+                const float wk = __builtin_amdgcn_exp2f(mk - Mn) * ml[q].y;
+                l = l * sc + wk;
+                acc[0] = acc[0] * sc + wk * bf16_lo(u[q].x);
+                acc[1] = acc[1] * sc + wk * bf16_hi(u[q].x);
+                acc[2] = acc[2] * sc + wk * bf16_lo(u[q].y);
+                acc[3] = acc[3] * sc + wk * bf16_hi(u[q].y);
+                acc[4] = acc[4] * sc + wk * bf16_lo(u[q].z);
+                acc[5] = acc[5] * sc + wk * bf16_hi(u[q].z);
+                acc[6] = acc[6] * sc + wk * bf16_lo(u[q].w);
+                acc[7] = acc[7] * sc + wk * bf16_hi(u[q].w);
+                M = Mn;
+            }
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int v = r / G, h = g * G + r % G;
@@ -470,11 +490,10 @@ __device__ __forceinline__ void barrier_keep_dma()
 
 
 template <int D, int NWR>
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(64 * NWR)
 attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
-    constexpr int NWK = 8 / NWR;                 // key columns
-    constexpr int NST = NWK == 1 ? 4 : (NWK == 2 ? 2 : 1);  // tile buffers per column
+    constexpr int NST = NWR == 8 ? 4 : 2;        // tile stages: 4 for the ping-pong, else 2
     constexpr int SEGS = D / 8;                  // 16-byte segments per K/V row
     constexpr int ROWB = D * 2;                  // bytes per K/V row
     constexpr int TILE = 64;                     // keys per tile
@@ -485,23 +504,18 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
     constexpr int NOPS = 2 * NIW;                // DMA instructions per tile per wave
     constexpr int KS = D / 16;                   // MFMA k-steps over the head dim
     constexpr int DB = D / 32;                   // 32-wide output blocks over the head dim
-    constexpr int NREG = DB * 16 + 2;            // merge record per lane: O, m, l
-    constexpr int BUFB = NWK * 2 * TILEB;        // one stage: K and V tile of every column
-    constexpr int RECB = NREG * 64 * 4;          // bytes of one merge record
-    constexpr int CAP0 = BUFB / RECB;            // merge records per stage buffer
+    constexpr int BUFB = 2 * TILEB;              // one stage: a K and a V tile
     static_assert(NIW >= 1 && NINS % NWR == 0, "DMA split");
-    static_assert((NWK - 1) * NWR <= CAP0 * NST, "LDS too small for the merge");
-    static_assert(NOPS * (NST - 2 > 0 ? NST - 2 : 0) < 64, "vmcnt range");
-    // One array per stage: distinct objects let the compiler see that a DMA into one
-    // stage does not alias the reads of another, so it does not wait for it.
-    __shared__ __attribute__((aligned(16))) uint8_t L0[BUFB];
-    __shared__ __attribute__((aligned(16))) uint8_t L1[NST > 1 ? BUFB : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t L2[NST > 2 ? BUFB : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t L3[NST > 3 ? BUFB : 16];
+    static_assert(NOPS < 64, "vmcnt range");
+    // The NST stage buffers.  Every LDS read of a tile is inline asm, so the compiler
+    // sees no LDS load to order against the in-flight copies and adds no waits of its
+    // own; a stage can therefore be chosen at run time (one loop body, small code).
+    __shared__ __attribute__((aligned(16))) uint8_t L0[NST * BUFB];
     __shared__ int bt_lds[kBtCap];
+    __shared__ __attribute__((aligned(16))) uint64_t anc_lds[NWR][32][5];  // rows' ancestor bits (+pad)
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wr = wid % NWR, wc = wid / NWR;
+    const int wr = wid;  // the wave's 32-row block
     const int col = lane & 31, hh = lane >> 5;
 
     // ---- work item
@@ -518,17 +532,8 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
     const int G = a.G, B = a.B, R = G * B;
     const int r0 = rt * pl.rt;
 
-    if (a.err && rt == 0 && chunk == 0 && g == 0)
-        attn_validate(a, s);
-    const int P = clamp_prefix(a, s);
-    const int v_hi = min(B - 1, (r0 + pl.rt - 1) / G);
-    const int kend_u = P + v_hi + 1;
     const int kbeg = chunk * pl.ch;
-    const int kend = min(kend_u, kbeg + pl.ch);
-    if (kbeg >= kend)
-        return;  // nothing to do: the combine pass skips this chunk
-    const int ntiles = (kend - kbeg + TILE - 1) / TILE;
-    const int nsteps = (ntiles + NWK - 1) / NWK;
+    const int v_hi = min(B - 1, (r0 + pl.rt - 1) / G);
 
     const uintptr_t kpre_a = reinterpret_cast<uintptr_t>(a.k_prefix);
     const uintptr_t vpre_a = reinterpret_cast<uintptr_t>(a.v_prefix);
@@ -538,20 +543,50 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
     const int64_t pre_s = (int64_t)s * a.max_prefix;  // contiguous prefix: first row of s
     const bool paged = a.block_table != nullptr;
     const int bshift = a.block_shift, bsize = a.block_size, nblocks = a.num_blocks;
+    auto stage = [&](int k) -> uint8_t * { return L0 + k * BUFB; };
 
-    // ---- paged prefix: the chunk's block-table entries, staged once in LDS
-    const int pend = min(kend, P);                   // prefix keys of this chunk end here
-    const int bt0 = kbeg >> bshift;                  // first block of the chunk
-    if (paged) {
-        const int nb = kbeg < pend ? ((pend - 1) >> bshift) - bt0 + 1 : 0;
-        const int32_t *btab = a.block_table + (int64_t)s * a.max_blocks;
-        for (int i = tid; i < nb; i += 512)
-            bt_lds[i] = (bt0 + i < a.max_blocks) ? btab[bt0 + i] : -1;
-        __syncthreads();
+    // ---- DMA of one tile (keys kt..kt+63) into `base` (K) and base + TILEB (V).  The
+    // NWR waves share the NINS row groups; a lane copies one 16-byte segment.
+    // `off_of(key)` gives the key's K/V row (element offset) and whether it lies in the
+    // prefix buffers.  Exactly NOPS loads per wave.
+    auto dma_tile = [=](int kt, uint8_t *base, auto off_of) {
+        const int rrow = lane / SEGS, pslot = lane % SEGS;
+#pragma unroll
+        for (int ii = 0; ii < NIW; ++ii) {
+            const int i = ii * NWR + wr;
+            const int row = i * RPI + rrow;
+            bool pre;
+            const int64_t off = off_of(kt + row, pre);
+            const int seg = pslot ^ seg_swz<SEGS>(row);
+            const uintptr_t boff = (uintptr_t)(off * 2 + seg * 16);
+            lds_dma16(reinterpret_cast<const void *>((pre ? kpre_a : ktr_a) + boff), base + i * 1024);
+            lds_dma16(reinterpret_cast<const void *>((pre ? vpre_a : vtr_a) + boff),
+                      base + TILEB + i * 1024);
+        }
+    };
+
+    // ---- speculative copies.  The prefix length is a device value: rather than wait
+    // for it before the first copies, the first tiles of a contiguous prefix are fetched
+    // as prefix keys right away (valid addresses for any key below max_prefix) and kept
+    // if, once the length is known, every key of the tile is an in-range prefix key --
+    // the same copy the exact path would have made.
+    constexpr int NPRO = NST == 4 ? 2 : 1;  // tiles fetched before the loop
+    bool spec[NPRO];
+#pragma unroll
+    for (int k = 0; k < NPRO; ++k) {
+        const int kt = kbeg + k * TILE;
+        spec[k] = !paged && kt + TILE <= a.max_prefix;
+        if (spec[k]) {
+            auto off_spec = [=](int key, bool &pre) -> int64_t {
+                pre = true;
+                return ((pre_s + key) * Hkv + g) * D;
+            };
+            dma_tile(kt, stage(k), off_spec);
+        }
     }
 
     // ---- rows of this wave: one 32-row block, lane holds row `col`; its Q^T fragments
-    // and its ancestor row stay in registers
+    // stay in registers.  Loaded, like the speculative copies, before the prefix length.
     const int wrow0 = r0 + wr * 32;
     const bool wave_has_rows = wrow0 < R;
     const int rr = wrow0 + col;
@@ -569,52 +604,75 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
             qf[ks] = __builtin_bit_cast(bf16x8_t, u);
         }
     }
-    uint64_t anc0, anc1, anc2, anc3;
-    {
-        const uint64_t *ar = a.anc + ((int64_t)s * B + vrow) * 4;
-        anc0 = ar[0];
-        anc1 = ar[1];
-        anc2 = ar[2];
-        anc3 = ar[3];
+    // the wave's 32 ancestor rows, later parked in LDS (lane hh holds words 2hh, 2hh+1)
+    const uint64_t *anc_src = a.anc + ((int64_t)s * B + vrow) * 4 + 2 * hh;
+    const uint64_t anc_a = anc_src[0], anc_b = anc_src[1];
+
+    if (a.err && rt == 0 && chunk == 0 && g == 0)
+        attn_validate(a, s);
+    const int P = clamp_prefix(a, s);
+    const int kend_u = P + v_hi + 1;
+    const int kend = min(kend_u, kbeg + pl.ch);
+    if (kbeg >= kend) {
+        wait_vm<0>();  // speculative copies land before the workgroup's LDS is released
+        return;        // nothing to do: the combine pass skips this chunk
+    }
+    const int ntiles = (kend - kbeg + TILE - 1) / TILE;
+    anc_lds[wid][col][2 * hh] = anc_a;
+    anc_lds[wid][col][2 * hh + 1] = anc_b;
+
+    // ---- paged prefix: the chunk's block-table entries, staged once in LDS
+    const int pend = min(kend, P);                   // prefix keys of this chunk end here
+    const int bt0 = kbeg >> bshift;                  // first block of the chunk
+    if (paged) {
+        const int nb = kbeg < pend ? ((pend - 1) >> bshift) - bt0 + 1 : 0;
+        const int32_t *btab = a.block_table + (int64_t)s * a.max_blocks;
+        for (int i = tid; i < nb; i += 64 * NWR)
+            bt_lds[i] = (bt0 + i < a.max_blocks) ? btab[bt0 + i] : -1;
+        __syncthreads();
     }
 
-    // ---- DMA of one tile (keys kt..kt+63) into `base` (K) and base + TILEB (V).  The
-    // NWR waves of a column share the NINS row groups; a lane copies one 16-byte segment.
-    // Keys past the range are clamped to the range's last key and absent keys (a bad
-    // block) read the sequence's first tree row: a finite value whose score the mask
-    // removes, or whose sequence is flagged.  Exactly NOPS loads per wave.
-    auto issue_tile = [=](int kt, uint8_t *base) {
-        const int rrow = lane / SEGS, pslot = lane % SEGS;
-#pragma unroll
-        for (int ii = 0; ii < NIW; ++ii) {
-            const int i = ii * NWR + wr;
-            const int row = i * RPI + rrow;
-            const int key = min(kt + row, kend - 1);
-            int64_t off;  // element offset of the key's K/V row, -1 if absent
-            bool pre = key < P;
-            if (pre) {
-                if (paged) {
-                    const int blk = bt_lds[(key >> bshift) - bt0];
-                    off = (blk >= 0 && blk < nblocks)
-                              ? (((int64_t)blk * bsize + (key & (bsize - 1))) * Hkv + g) * D
-                              : -1;
-                } else {
-                    off = ((pre_s + key) * Hkv + g) * D;
-                }
+    // Exact copy: keys past the range are clamped to the range's last key and absent
+    // keys (a bad block) read the sequence's first tree row -- a finite value whose score
+    // the mask removes, or whose sequence is flagged.
+    auto off_exact = [=](int key_raw, bool &pre) -> int64_t {
+        const int key = min(key_raw, kend - 1);
+        int64_t off;
+        pre = key < P;
+        if (pre) {
+            if (paged) {
+                const int blk = bt_lds[(key >> bshift) - bt0];
+                off = (blk >= 0 && blk < nblocks)
+                          ? (((int64_t)blk * bsize + (key & (bsize - 1))) * Hkv + g) * D
+                          : -1;
             } else {
-                off = (((int64_t)s * B + (key - P)) * Hkv + g) * D;
+                off = ((pre_s + key) * Hkv + g) * D;
             }
-            if (off < 0) {
-                pre = false;
-                off = ((int64_t)s * B * Hkv + g) * D;
-            }
-            const int seg = pslot ^ seg_swz<SEGS>(row);
-            const uintptr_t boff = (uintptr_t)(off * 2 + seg * 16);
-            lds_dma16(reinterpret_cast<const void *>((pre ? kpre_a : ktr_a) + boff), base + i * 1024);
-            lds_dma16(reinterpret_cast<const void *>((pre ? vpre_a : vtr_a) + boff),
-                      base + TILEB + i * 1024);
+        } else {
+            off = (((int64_t)s * B + (key - P)) * Hkv + g) * D;
         }
+        if (off < 0) {
+            pre = false;
+            off = ((int64_t)s * B * Hkv + g) * D;
+        }
+        return off;
     };
+    auto issue_tile = [=](int kt, uint8_t *base) { dma_tile(kt, base, off_exact); };
+
+    // ---- settle the speculation: keep a copy only if every key is an in-range prefix
+    // key; otherwise let it land and fetch the tile exactly.
+    bool have_pro[NPRO];
+    {
+        bool stale = false;
+#pragma unroll
+        for (int k = 0; k < NPRO; ++k) {
+            const int kt = kbeg + k * TILE;
+            have_pro[k] = spec[k] && kt + TILE <= min(P, kend);
+            stale |= spec[k] && !have_pro[k];
+        }
+        if (stale)
+            wait_vm<0>();
+    }
 
     float m_i = -INFINITY, l_i = 0.f;
     f32x16_t o_acc[DB];
@@ -637,21 +695,19 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         const int wa = __builtin_amdgcn_readfirstlane(ua >> 6), sh = ua & 63;
         if (wa >= 4)
             return 0ull;
-        // uniform branches (no indexed register array, which would live in scratch)
+        // words wa and wa+1 of this lane's row from LDS (inline asm read: the compiler
+        // then has no LDS access to order against the in-flight tile copies)
         uint64_t w0, w1;
-        if (wa == 0) {
-            w0 = anc0;
-            w1 = anc1;
-        } else if (wa == 1) {
-            w0 = anc1;
-            w1 = anc2;
-        } else if (wa == 2) {
-            w0 = anc2;
-            w1 = anc3;
-        } else {
-            w0 = anc3;
-            w1 = 0ull;
+        {
+            const uint32_t ad = lds_off(&anc_lds[wid][col][wa]);
+            asm volatile("ds_read_b64 %0, %2\n\t"
+                         "ds_read_b64 %1, %2 offset:8\n\t"
+                         "s_waitcnt lgkmcnt(0)"
+                         : "=&v"(w0), "=&v"(w1)
+                         : "v"(ad));
         }
+        if (wa == 3)
+            w1 = 0ull;
         const uint64_t t = sh ? ((w0 >> sh) | (w1 << (64 - sh))) : w0;
         const uint64_t win = u0 < 0 ? ((t << (-u0)) | ((1ull << (-u0)) - 1ull)) : t;
         return win & inr;
@@ -668,17 +724,20 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 sacc[kbk][j] = 0.f;
-        const uint32_t kbase = lds_off(kb) + col * ROWB;
+        // segment (2*ks + hh) ^ z = 2*(ks ^ (z >> 1)) + (hh ^ (z & 1)): one XOR per k-step
         const int zs = seg_swz<SEGS>(col);
+        const uint32_t kbase =
+            lds_off(kb) + opaque((uint32_t)(col * ROWB + (hh ^ (zs & 1)) * 16));
+        const int zk = opaque(zs >> 1);
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
             for (int k4 = 0; k4 < KS; k4 += 4) {
                 uint4 kf[4];
-                const uint32_t a0 = kbase + (((2 * (k4 + 0) + hh) ^ zs) * 16);
-                const uint32_t a1 = kbase + (((2 * (k4 + 1) + hh) ^ zs) * 16);
-                const uint32_t a2 = kbase + (((2 * (k4 + 2) + hh) ^ zs) * 16);
-                const uint32_t a3 = kbase + (((2 * (k4 + 3) + hh) ^ zs) * 16);
+                const uint32_t a0 = kbase + (uint32_t)(((k4 + 0) ^ zk) * 32);
+                const uint32_t a1 = kbase + (uint32_t)(((k4 + 1) ^ zk) * 32);
+                const uint32_t a2 = kbase + (uint32_t)(((k4 + 2) ^ zk) * 32);
+                const uint32_t a3 = kbase + (uint32_t)(((k4 + 3) ^ zk) * 32);
                 if (kbk == 0)
                     k_read4<0>(a0, a1, a2, a3, kf[0], kf[1], kf[2], kf[3]);
                 else
@@ -746,13 +805,19 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         // rows of fragment (kbk, m2) are kbk*32 + 16*m2 + 4*hh + j16/4 (+8 for the upper
         // half); the 16- and 32-row steps leave the swizzle unchanged, so they are
         // immediate offsets.
+        // segment (4*db + x) ^ z, x = 2*b2 + (j16 & 3)/2 < 4, splits into (x ^ (z & 3)) and
+        // 4*(db ^ (z >> 2)): two bases per lane, one XOR per output block
         const int rowa = 4 * hh + (j16 >> 2), rowb = rowa + 8;
+        const int xs = 2 * b2 + ((j16 & 3) >> 1), half = (j16 & 1) * 8;
+        const int za = seg_swz<SEGS>(rowa), zb = seg_swz<SEGS>(rowb);
+        const uint32_t vbase = lds_off(vb);
+        const uint32_t basea = vbase + opaque((uint32_t)(rowa * ROWB + (xs ^ (za & 3)) * 16 + half));
+        const uint32_t baseb = vbase + opaque((uint32_t)(rowb * ROWB + (xs ^ (zb & 3)) * 16 + half));
+        const int zda = opaque(za >> 2), zdb = opaque(zb >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int cc = db * 32 + 16 * b2 + 4 * (j16 & 3);
-            const int half = (cc & 4) * 2;
-            const uint32_t aa = lds_off(vb + rowa * ROWB + (((cc >> 3) ^ seg_swz<SEGS>(rowa)) * 16) + half);
-            const uint32_t ab = lds_off(vb + rowb * ROWB + (((cc >> 3) ^ seg_swz<SEGS>(rowb)) * 16) + half);
+            const uint32_t aa = basea + (uint32_t)((db ^ zda) * 64);
+            const uint32_t ab = baseb + (uint32_t)((db ^ zdb) * 64);
             i32x2_t r[8];
             tr16_x8<0, 16 * ROWB, 32 * ROWB, 48 * ROWB>(aa, ab, r);
 #pragma unroll
@@ -769,18 +834,8 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         pv(vb, pf);
     };
 
-    auto stage = [&](auto kst) -> uint8_t * {
-        constexpr int k = decltype(kst)::value;
-        uint8_t *b = k == 0 ? L0 : (k == 1 ? L1 : (k == 2 ? L2 : L3));
-        return b + wc * 2 * TILEB;
-    };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-
-    if constexpr (NWK == 1) {
-        // ---- one key column, 8 waves, 4 stages, ping-pong.  Waves 0-3 (group A) and
+    if constexpr (NWR == 8) {
+        // ---- 8 waves, 4 stages, ping-pong.  Waves 0-3 (group A) and
         // 4-7 (group B) share the SIMDs pairwise; B runs half a tile behind A, so on a SIMD
         // one wave's softmax (VALU) runs under the other's MFMAs.  Barrier j is where A
         // starts tile j and where B has finished the softmax of tile j - 1 (its PV of
@@ -790,10 +845,10 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         // that wait is vmcnt(NOPS) while the DMA of tile j + 1 may still run.
         const int grp = wid >> 2;
         bf16x8_t pf[2][2];
-        if (0 < ntiles)
-            issue_tile(kbeg, stage(I0{}));
-        if (1 < ntiles)
-            issue_tile(kbeg + TILE, stage(I1{}));
+        if (0 < ntiles && !have_pro[0])
+            issue_tile(kbeg, stage(0));
+        if (1 < ntiles && !have_pro[NPRO - 1])
+            issue_tile(kbeg + TILE, stage(1));
         auto wait_own = [&](bool newer_in_flight) {
             if (newer_in_flight)
                 wait_vm<NOPS>();
@@ -802,129 +857,50 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         };
         if (grp == 1)
             wait_own(1 < ntiles);
-        auto body = [&](int j, auto kst) {
-            constexpr int k = decltype(kst)::value;
+        for (int j = 0; j < ntiles; ++j) {
+            const int k = j & 3;
             const int kt = kbeg + j * TILE;
             if (grp == 0)
                 wait_own(j + 1 < ntiles);
             barrier_keep_dma();
             if (j + 2 < ntiles)
-                issue_tile(kt + 2 * TILE, stage(std::integral_constant<int, (k + 2) % 4>{}));
+                issue_tile(kt + 2 * TILE, stage((k + 2) & 3));
             if (grp == 0) {
                 if (wave_has_rows) {
-                    qk_softmax(stage(kst), vis_window(kt), pf);
-                    pv(stage(kst) + TILEB, pf);
+                    qk_softmax(stage(k), vis_window(kt), pf);
+                    pv(stage(k) + TILEB, pf);
                 }
             } else {
                 if (wave_has_rows) {
                     if (j > 0)
-                        pv(stage(std::integral_constant<int, (k + 3) % 4>{}) + TILEB, pf);
-                    qk_softmax(stage(kst), vis_window(kt), pf);
+                        pv(stage((k + 3) & 3) + TILEB, pf);
+                    qk_softmax(stage(k), vis_window(kt), pf);
                 }
                 wait_own(j + 2 < ntiles);
             }
-        };
-        for (int j = 0; j < ntiles; j += 4) {
-            body(j, I0{});
-            if (j + 1 < ntiles)
-                body(j + 1, I1{});
-            if (j + 2 < ntiles)
-                body(j + 2, I2{});
-            if (j + 3 < ntiles)
-                body(j + 3, I3{});
         }
-        if (grp == 1 && wave_has_rows) {  // B's PV of the last tile
-            switch ((ntiles - 1) & 3) {
-            case 0: pv(stage(I0{}) + TILEB, pf); break;
-            case 1: pv(stage(I1{}) + TILEB, pf); break;
-            case 2: pv(stage(I2{}) + TILEB, pf); break;
-            default: pv(stage(I3{}) + TILEB, pf); break;
-            }
-        }
+        if (grp == 1 && wave_has_rows)  // B's PV of the last tile
+            pv(stage((ntiles - 1) & 3) + TILEB, pf);
     } else {
-        // ---- several key columns (few rows): column wc takes tiles wc, wc + NWK, ...;
-        // two stages (NWK = 2: the next step's DMA runs under this step's work) or one.
-        auto tile_of = [&](int step) { return step * NWK + wc; };
-        auto body = [&](int step, auto kst) {
-            constexpr int k = decltype(kst)::value;
-            uint8_t *cur = stage(kst);
-            const int tile = tile_of(step);
-            const int kt = kbeg + tile * TILE;
-            if constexpr (NST == 1) {
-                if (tile < ntiles)
-                    issue_tile(kt, cur);
-            }
+        // ---- 2 or 4 waves (few rows), double buffering: after barrier j, tile j + 1 goes
+        // to the stage tile j - 1 used, which every wave has finished.
+        if (0 < ntiles && !have_pro[0])
+            issue_tile(kbeg, stage(0));
+        for (int j = 0; j < ntiles; ++j) {
+            const int k = j & 1;
+            const int kt = kbeg + j * TILE;
             wait_vm<0>();
             barrier_keep_dma();
-            if constexpr (NST > 1) {
-                const int tn = tile_of(step + 1);
-                if (tn < ntiles)
-                    issue_tile(kbeg + tn * TILE, stage(std::integral_constant<int, (k + 1) % NST>{}));
-            }
-            if (tile < ntiles && wave_has_rows)
-                compute_tile(cur, cur + TILEB, vis_window(kt));
-            if constexpr (NST == 1)
-                barrier_keep_dma();
-        };
-        if constexpr (NST > 1) {
-            if (tile_of(0) < ntiles)
-                issue_tile(kbeg + tile_of(0) * TILE, stage(I0{}));
-        }
-        for (int step = 0; step < nsteps; step += NST) {
-            body(step, I0{});
-            if constexpr (NST > 1)
-                if (step + 1 < nsteps)
-                    body(step + 1, std::integral_constant<int, 1 % NST>{});
+            if (j + 1 < ntiles)
+                issue_tile(kt + TILE, stage(k ^ 1));
+            if (wave_has_rows)
+                compute_tile(stage(k), stage(k) + TILEB, vis_window(kt));
         }
     }
 
-    // ---- merge the key columns of a row block in LDS (NWK > 1): columns 1.. publish
-    // (O, m, l), column 0 folds them in.
-    if constexpr (NWK > 1) {
-        wait_dma();
-        // merge record k lives in buffer set 0 while it fits, then in set 1
-        auto rec = [&](int k) -> float * {
-            return reinterpret_cast<float *>(k < CAP0 ? L0 + k * RECB : L1 + (k - CAP0) * RECB);
-        };
-        __syncthreads();
-        if (wc > 0) {
-            float *mine = rec((wc - 1) * NWR + wr);
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    mine[(db * 16 + j) * 64 + lane] = o_acc[db][j];
-            mine[(DB * 16) * 64 + lane] = m_i;
-            mine[(DB * 16 + 1) * 64 + lane] = l_i;
-        }
-        __syncthreads();
-        if (wc == 0) {
-            float M = m_i;
-            for (int k = 1; k < NWK; ++k)
-                M = fmaxf(M, rec((k - 1) * NWR + wr)[(DB * 16) * 64 + lane]);
-            const float Mu = M == -INFINITY ? 0.f : M;
-            const float w0 = __builtin_amdgcn_exp2f(m_i - Mu);
-            float l = l_i * w0;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                o_acc[db] *= w0;
-            for (int k = 1; k < NWK; ++k) {
-                const float *oth = rec((k - 1) * NWR + wr);
-                const float wk = __builtin_amdgcn_exp2f(oth[(DB * 16) * 64 + lane] - Mu);
-                l += wk * oth[(DB * 16 + 1) * 64 + lane];
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        o_acc[db][j] += wk * oth[(db * 16 + j) * 64 + lane];
-            }
-            m_i = M;
-            l_i = l;
-        }
-    }
     // ---- epilogue: final output (one chunk), or a normalised bf16 partial plus (m, l)
     const float l = l_i + __shfl_xor(l_i, 32, kWave);
-    if (wc == 0 && wave_has_rows && row_ok) {
+    if (wave_has_rows && row_ok) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t *dst;
         if (pl.n_chunks == 1) {
@@ -950,27 +926,6 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
                        ((uint32_t)f32_to_bf16(o_acc[db][4 * q + 3] * inv) << 16);
                 *reinterpret_cast<uint2 *>(dst + d0) = pk;
             }
-    }
-    // ---- fused merge: the unit's last-arriving workgroup merges its partials.  Release:
-    // every thread's partial stores are made visible at device scope before the arrival
-    // is counted; acquire: the last workgroup fences before reading the others'.  The
-    // counter goes back to zero, ready for the next call on the same workspace.
-    if (pl.fused) {
-        __shared__ int s_last;
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const int nact = (kend_u + pl.ch - 1) / pl.ch;
-            const int old = atomicAdd(ws.cnt + unit, 1);
-            s_last = old == nact - 1;
-        }
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
-            attn_merge_unit<D>(a, pl, ws, unit, tid, 512);
-            if (tid == 0)
-                ws.cnt[unit] = 0;
-        }
     }
 }
 
@@ -1001,7 +956,7 @@ template <int D, int NWR>
 static void launch_main(const AttnArgs &a, const AttnPlan &p, const AttnWs &w, hipStream_t st)
 {
     const unsigned grid = (unsigned)((long)p.units * p.n_chunks);
-    hipLaunchKernelGGL((attn_bf16_kernel<D, NWR>), dim3(grid), dim3(512), 0, st, a, p, w);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NWR>), dim3(grid), dim3(64 * NWR), 0, st, a, p, w);
 }
 
 template <int D>
@@ -1016,7 +971,7 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
     else
         launch_main<D, 8>(a, p, w, st);
     jt_status e = launch_status(hipGetLastError());
-    if (e != JT_OK || p.n_chunks == 1 || p.fused)
+    if (e != JT_OK || p.n_chunks == 1)
         return e;
     const long threads = (long)p.units * p.rt * (D / 8);
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,

@@ -55,15 +55,37 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
     uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
     return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+// Wave-wide maximum of a 64-bit key through DPP moves (no LDS round trips): pairs,
+// quads, half rows, rows, then the row broadcasts; lane 63 ends with the maximum, which
+// is returned to every lane.
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v, uint32_t ohi, uint32_t olo)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const bool take = ohi > hi || (ohi == hi && olo > lo);
+    return take ? (((uint64_t)ohi << 32) | olo) : v;
 }
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_u64_stage(uint64_t v)
+{
+    const int hi = (int)(v >> 32), lo = (int)(uint32_t)v;
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+    return dpp_max_step(v, ohi, olo);
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v)
+{
+    v = dpp_max_u64_stage<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_u64_stage<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_u64_stage<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max_u64_stage<0x140, 0xF>(v);  // row_mirror
+    v = dpp_max_u64_stage<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max_u64_stage<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 63);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) { return wave_max_u64_dpp(v); }
+
 __device__ __forceinline__ float wave_max_f32(float v)
 {
 #pragma unroll

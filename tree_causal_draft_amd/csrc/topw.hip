@@ -5,44 +5,45 @@
 // (paper.rainbus.top summary, method steps).
 //
 // Bytes, not flops, bound this step: every logit is read once.  Layout of the work:
-//   * a row is cut into sub-chunks of 8192 logits; one workgroup (4 waves) owns a run of
-//     consecutive sub-chunks of one row, so even 16 rows fill the 256 CUs;
-//   * a sub-chunk is pulled into registers with 16-byte loads (32 logits per thread) and
-//     reduced there: thread max, then sum of exp(x - max) (exact per-thread rescale);
-//   * a threshold tau (the W-th largest thread maximum inside one wave, found by a 32-step
-//     ballot bisection on order codes) bounds the chunk's W-th largest logit from below,
-//     so only threads whose maximum reaches tau scan for candidates;
-//   * candidates land in LDS as 64-bit keys (order code << 32 | ~id): value descending,
-//     id ascending in one integer compare, so bf16 ties resolve exactly like a full
-//     sort; the running top-W is kept in LDS across the sub-chunks of a workgroup;
-//   * a merge kernel (one wave per row) combines the partial top-W lists and the
+//   * a row is cut into pieces of 2048 logits; each wave of a workgroup owns one piece
+//     (or a run of them for very long rows) and works alone, with no workgroup barrier,
+//     so the many small pieces spread the row over the whole chip;
+//   * a piece is pulled into registers with 16-byte loads (32 logits per lane) and
+//     reduced there: lane max, then sum of exp(x - max) (exact per-lane rescale);
+//   * a threshold tau (the W-th largest lane maximum, found by a 32-step ballot
+//     bisection on order codes) bounds the piece's W-th largest logit from below, so
+//     only logits >= tau become candidates;
+//   * candidates land in the wave's LDS slice as 64-bit keys (order code << 32 | ~id):
+//     value descending, id ascending in one integer compare, so bf16 ties resolve
+//     exactly like a full sort; W rounds of a DPP wave max extract the W largest;
+//   * a merge kernel (one wave per row) combines the per-wave top-W lists and the
 //     (max, sum-exp) pairs into ids, log-probs and the row log-sum-exp.
 #include "jt_internal.h"
 
 namespace jt {
 
-constexpr int kTopwThreads = 256;
-constexpr int kSub = 8192;          // logits per sub-chunk (32 per thread)
-constexpr int kCap = 1024;          // candidate slots in LDS
-constexpr int kMaxMergeChunks = 64; // partial lists per row seen by the merge kernel
+constexpr int kTopwThreads = 256;   // 4 independent waves per workgroup
+constexpr int kPiece = 2048;        // logits per wave piece (32 per lane)
+constexpr int kWaveCap = 512;       // candidate slots per wave in LDS
+constexpr int kMaxLists = 128;      // partial lists per row seen by the merge kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int kElems = 8; static constexpr int kLoads = 4; };
 template <> struct Vec<float> { static constexpr int kElems = 4; static constexpr int kLoads = 8; };
 
-// Loads the thread's 32 logits of one sub-chunk.  Element k of load i sits at index
-// base + (tid + 256*i)*E + k.  Out-of-row entries become -inf with valid = false.
+// Loads a lane's 32 logits of one piece.  Element k of load i sits at index
+// base + (lane + 64*i)*E + k.  Out-of-row entries become -inf with valid = false.
 template <typename T, bool kAligned>
-__device__ __forceinline__ void load_sub(const T *__restrict__ row, int64_t base, int V, int tid,
-                                         float (&x)[32], uint32_t &valid)
+__device__ __forceinline__ void load_piece(const T *__restrict__ row, int64_t base, int V, int lane,
+                                           float (&x)[32], uint32_t &valid)
 {
     constexpr int E = Vec<T>::kElems;
     constexpr int L = Vec<T>::kLoads;
     valid = 0;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const int64_t e0 = base + (int64_t)(tid + kTopwThreads * i) * E;
+        const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
         if (kAligned && e0 + E <= V) {
             const uint4 u = *reinterpret_cast<const uint4 *>(row + e0);
             if constexpr (sizeof(T) == 2) {
@@ -74,10 +75,10 @@ __device__ __forceinline__ void load_sub(const T *__restrict__ row, int64_t base
 }
 
 template <typename T>
-__device__ __forceinline__ uint32_t elem_id(int64_t base, int tid, int j)
+__device__ __forceinline__ uint32_t elem_id(int64_t base, int lane, int j)
 {
     constexpr int E = Vec<T>::kElems;
-    return (uint32_t)(base + (int64_t)(tid + kTopwThreads * (j / E)) * E + (j % E));
+    return (uint32_t)(base + (int64_t)(lane + kWave * (j / E)) * E + (j % E));
 }
 
 // Largest code t such that at least W lanes of the wave hold a code >= t.
@@ -93,127 +94,130 @@ __device__ __forceinline__ uint32_t wave_wth_code(uint32_t code, int W)
     return prefix;
 }
 
-// Selects the W largest keys among keys[0..n) (distinct keys; 0 = empty) into out[0..W)
-// sorted descending, padding with 0.  Block-wide; ends with a barrier.
-__device__ void select_topw(const uint64_t *keys, int n, int W, uint64_t *out)
+// Orders the LDS accesses of one wave: writes by some lanes before reads by others.
+__device__ __forceinline__ void wave_sync()
 {
-    for (int i = threadIdx.x; i < W; i += blockDim.x)
-        out[i] = 0ull;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const uint64_t k = keys[i];
-        if (k == 0ull)
-            continue;
-        int rank = 0;
-        for (int j = 0; j < n; ++j)
-            rank += keys[j] > k;
-        if (rank < W)
-            out[rank] = k;
-    }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One wave selects the W largest of keys[0..n) (distinct keys; 0 = empty) into out[0..W),
+// descending, padding with 0: W rounds, each taking the largest key below the previous
+// winner (lane-local scan, then a DPP wave max).  Keys are distinct because ids are, so
+// the order is exactly (value desc, id asc).
+__device__ void wave_select_topw(const uint64_t *keys, int n, int W, uint64_t *out)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < W; ++r) {
+        uint64_t mine = 0ull;
+        for (int i = lane; i < n; i += 64) {
+            const uint64_t k = keys[i];
+            mine = (k < prev && k > mine) ? k : mine;
+        }
+        mine = wave_max_u64_dpp(mine);
+        if (lane == 0)
+            out[r] = mine;
+        prev = mine;
+    }
+    wave_sync();
+}
+
+// Each wave owns `ppw` consecutive pieces of 2048 logits of one row and works alone (no
+// workgroup barrier): lane max and sum of exp(x - max); a threshold tau = the W-th
+// largest lane maximum of the piece, a lower bound on the piece's W-th largest logit;
+// the logits >= tau (and above the running W-th best) compacted into the wave's LDS
+// slice by ballot + mbcnt; W rounds of a wave max over those and the running top-W.
+// Output per wave: its W best keys and its (max, sum-exp) pair.
 template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kTopwThreads)
-topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, int W, int nsub,
-                    int sub_per_wg, int nchunk, uint64_t *__restrict__ ws_keys,
+topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, int V, int W,
+                    int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
                     float2 *__restrict__ ws_ms)
 {
-    __shared__ uint64_t cand[kCap + JT_MAX_W];
-    __shared__ uint64_t best[JT_MAX_W];
-    __shared__ int ncand;
-    __shared__ uint32_t wave_tau[4];
-    __shared__ float wave_m[4], wave_s[4];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const int row_idx = blockIdx.x / nchunk;
-    const int chunk = blockIdx.x % nchunk;
+    __shared__ uint64_t cand_all[4][kWaveCap + JT_MAX_W];
+    __shared__ uint64_t best_all[4][JT_MAX_W];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int gl = blockIdx.x * 4 + wid;  // list index = (row, list within the row)
+    if (gl >= rows * nlist)
+        return;
+    const int row_idx = gl / nlist, li = gl % nlist;
     const T *row = logits + (int64_t)row_idx * row_stride;
-    const int sc0 = chunk * sub_per_wg;
-    const int sc1 = min(nsub, sc0 + sub_per_wg);
-
-    if (tid < JT_MAX_W)
-        best[tid] = 0ull;
-    float run_m = -INFINITY, run_s = 0.f;   // this thread's running (max, sum exp(x-max))
-
-    for (int sc = sc0; sc < sc1; ++sc) {
-        const int64_t base = (int64_t)sc * kSub;
+    uint64_t *cand = cand_all[wid];
+    uint64_t *best = best_all[wid];
+    if (lane < JT_MAX_W)
+        best[lane] = 0ull;
+    wave_sync();
+    float run_m = -INFINITY, run_s = 0.f;  // lane's running (max, sum exp(x - max))
+    const int p0 = li * ppw, p1 = min(npiece, p0 + ppw);
+    for (int pc = p0; pc < p1; ++pc) {
+        const int64_t base = (int64_t)pc * kPiece;
         float x[32];
         uint32_t valid;
-        load_sub<T, kAligned>(row, base, V, tid, x, valid);
-
+        load_piece<T, kAligned>(row, base, V, lane, x, valid);
         float m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 32; ++j)
             m = fmaxf(m, x[j]);
-        // sum exp(x - m) over this sub-chunk, then fold into the running pair
-        float s = 0.f;
+        float sx = 0.f;
         if (m != -INFINITY) {
             const float mb = m * kLog2e;
 #pragma unroll
             for (int j = 0; j < 32; ++j)
-                s += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+                sx += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
         } else {
             // every entry is -inf, padding or NaN: only a NaN must still poison the sum
 #pragma unroll
             for (int j = 0; j < 32; ++j)
                 if (x[j] != x[j])
-                    s = x[j];
+                    sx = x[j];
         }
         if (m > run_m) {
             const float prev = (run_m == -INFINITY)
                                    ? ((run_s != run_s) ? run_s : 0.f)
                                    : run_s * __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
-            run_s = prev + s;
+            run_s = prev + sx;
             run_m = m;
         } else if (m == -INFINITY) {
-            run_s += s;  // adds 0, or propagates a NaN
+            run_s += sx;  // adds 0, or propagates a NaN
         } else {
-            run_s += s * __builtin_amdgcn_exp2f((m - run_m) * kLog2e);
+            run_s += sx * __builtin_amdgcn_exp2f((m - run_m) * kLog2e);
         }
 
-        // ---- candidate threshold
-        // a thread's code counts only if it holds a real (non-NaN) element equal to m
+        // ---- threshold: a lane's code counts only if it holds a real (non-NaN) element
+        // equal to its maximum
         bool real = m != -INFINITY;
         if (!real) {
 #pragma unroll
             for (int j = 0; j < 32; ++j)
                 real |= ((valid >> j) & 1u) && x[j] == -INFINITY;
         }
-        const uint32_t my_code = real ? order_code(m) : 0u;
-        const uint32_t tau_w = wave_wth_code(my_code, W);
-        if (lane == 0)
-            wave_tau[wid] = tau_w;
-        if (tid == 0)
-            ncand = 0;
-        __syncthreads();
-        uint32_t tau = max(max(wave_tau[0], wave_tau[1]), max(wave_tau[2], wave_tau[3]));
+        uint32_t tau = wave_wth_code(real ? order_code(m) : 0u, W);
         const uint64_t wth = best[W - 1];
         if (wth != 0ull)
             tau = max(tau, (uint32_t)(wth >> 32));
-        // tau == 0 means "fewer than W thread maxima": every valid element is a candidate
-        if (tau == 0u || my_code >= tau) {
+        // tau == 0: fewer than W lane maxima, every valid element is a candidate
+        int n = 0;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                if (!((valid >> j) & 1u))
-                    continue;
-                const uint32_t c = order_code(x[j]);
-                if (c >= tau) {
-                    const int slot = atomicAdd(&ncand, 1);
-                    if (slot < kCap)
-                        cand[slot] = ((uint64_t)c << 32) | (uint64_t)(~elem_id<T>(base, tid, j));
-                }
+        for (int j = 0; j < 32; ++j) {
+            const uint32_t c = order_code(x[j]);
+            const bool pred = ((valid >> j) & 1u) && c >= tau;
+            const uint64_t b = __ballot(pred);
+            if (b) {
+                const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                if (pred && slot < kWaveCap)
+                    cand[slot] = ((uint64_t)c << 32) | (uint64_t)(~elem_id<T>(base, lane, j));
+                n += __popcll(b);
             }
         }
-        __syncthreads();
-        const int n = ncand;
-        if (n <= kCap) {
-            // merge the previous top-W into the candidate list, then re-select
-            if (tid < W)
-                cand[n + tid] = best[tid];
-            __syncthreads();
-            select_topw(cand, n + W, W, best);
+        wave_sync();
+        if (n <= kWaveCap) {
+            if (lane < W)
+                cand[n + lane] = best[lane];
+            wave_sync();
+            wave_select_topw(cand, n + W, W, best);
         } else {
             // rare overflow (huge ties): W rounds of exact arg-max over the registers
             uint64_t prev = ~0ull;
@@ -223,53 +227,33 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, int
                 for (int j = 0; j < 32; ++j) {
                     if (!((valid >> j) & 1u))
                         continue;
-                    const uint64_t k = rank_key(x[j], elem_id<T>(base, tid, j));
+                    const uint64_t k = rank_key(x[j], elem_id<T>(base, lane, j));
                     if (k < prev && k > mine)
                         mine = k;
                 }
-                mine = wave_max_u64(mine);
+                mine = wave_max_u64_dpp(mine);
                 if (lane == 0)
-                    cand[wid] = mine;
-                __syncthreads();
-                const uint64_t g = max(max(cand[0], cand[1]), max(cand[2], cand[3]));
-                __syncthreads();
-                if (tid == 0)
-                    cand[4 + r] = g;
-                prev = g;
+                    cand[r] = mine;
+                prev = mine;
             }
-            __syncthreads();
-            if (tid < W)
-                cand[4 + W + tid] = best[tid];
-            __syncthreads();
-            select_topw(cand + 4, 2 * W, W, best);
+            if (lane < W)
+                cand[W + lane] = best[lane];
+            wave_sync();
+            wave_select_topw(cand, 2 * W, W, best);
         }
     }
 
-    // ---- (max, sum) over the workgroup
-    float m = wave_max_f32(run_m);
-    float s = (run_m == -INFINITY) ? ((run_s != run_s) ? run_s : 0.f)
-                                   : run_s * __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
+    // ---- (max, sum) over the wave
+    const float m = wave_max_f32(run_m);
+    float sw = (run_m == -INFINITY) ? ((run_s != run_s) ? run_s : 0.f)
+                                    : run_s * __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
-        s += __shfl_xor(s, o, kWave);
-    if (lane == 0) {
-        wave_m[wid] = m;
-        wave_s[wid] = s;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float M = fmaxf(fmaxf(wave_m[0], wave_m[1]), fmaxf(wave_m[2], wave_m[3]));
-        float Ssum = 0.f;
-        for (int w = 0; w < 4; ++w) {
-            if (wave_m[w] == -INFINITY)
-                Ssum += (wave_s[w] != wave_s[w]) ? wave_s[w] : 0.f;
-            else
-                Ssum += wave_s[w] * __builtin_amdgcn_exp2f((wave_m[w] - M) * kLog2e);
-        }
-        ws_ms[blockIdx.x] = make_float2(M, Ssum);
-    }
-    if (tid < W)
-        ws_keys[(int64_t)blockIdx.x * W + tid] = best[tid];
+        sw += __shfl_xor(sw, o, kWave);
+    if (lane == 0)
+        ws_ms[gl] = make_float2(m, sw);
+    if (lane < W)
+        ws_keys[(int64_t)gl * W + lane] = best[lane];
 }
 
 // One wave per row: merge the partial lists and (max, sum) pairs.
@@ -278,7 +262,7 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
                   const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
                   float *__restrict__ logprob, float *__restrict__ row_lse)
 {
-    __shared__ uint64_t keys[kMaxMergeChunks * JT_MAX_W];
+    __shared__ uint64_t keys[kMaxLists * JT_MAX_W];
     __shared__ uint64_t top[JT_MAX_W];
     const int r = blockIdx.x;
     const int lane = threadIdx.x;
@@ -309,7 +293,8 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
     else
         lse = m + logf(s);
     __syncthreads();
-    select_topw(keys, n, W, top);
+    wave_select_topw(keys, n, W, top);
+    __syncthreads();
     if (lane < W) {
         const uint64_t k = top[lane];
         ids[(int64_t)r * W + lane] = (int32_t)key_id(k);
@@ -320,29 +305,22 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
 }
 
 struct TopwPlan {
-    int nsub, sub_per_wg, nchunk;
+    int npiece, ppw, nlist;
 };
 
 static TopwPlan topw_plan(int rows, int V)
 {
     TopwPlan p;
-    p.nsub = (V + kSub - 1) / kSub;
-    // aim for ~2048 workgroups in flight, at most kMaxMergeChunks partial lists per row
-    int want = (rows > 0) ? (2048 + rows - 1) / rows : 1;
-    int spw = (p.nsub + want - 1) / want;
-    if (spw < 1)
-        spw = 1;
-    while ((p.nsub + spw - 1) / spw > kMaxMergeChunks)
-        ++spw;
-    p.sub_per_wg = spw;
-    p.nchunk = (p.nsub + spw - 1) / spw;
+    p.npiece = (V + kPiece - 1) / kPiece;
+    p.ppw = (p.npiece + kMaxLists - 1) / kMaxLists;  // pieces per wave
+    p.nlist = (p.npiece + p.ppw - 1) / p.ppw;        // partial lists per row
     return p;
 }
 
 size_t topw_workspace(int rows, int V, int W, int /*dtype*/)
 {
     const TopwPlan p = topw_plan(rows, V);
-    const size_t parts = (size_t)rows * p.nchunk;
+    const size_t parts = (size_t)rows * p.nlist;
     return parts * (size_t)W * sizeof(uint64_t) + parts * sizeof(float2) + 256;
 }
 
@@ -352,38 +330,38 @@ jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, i
     if (rows == 0)
         return JT_OK;
     const TopwPlan p = topw_plan(rows, V);
-    const size_t parts = (size_t)rows * p.nchunk;
+    const size_t parts = (size_t)rows * p.nlist;
     uint64_t *wk = reinterpret_cast<uint64_t *>(ws);
     uintptr_t mp = reinterpret_cast<uintptr_t>(wk + parts * W);
     mp = (mp + 15) & ~(uintptr_t)15;
     float2 *wm = reinterpret_cast<float2 *>(mp);
-    const dim3 grid((unsigned)parts), block(kTopwThreads);
+    const dim3 grid((unsigned)((parts + 3) / 4)), block(kTopwThreads);
     const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
     if (dtype == JT_BF16) {
         const bool al = (addr % 16 == 0) && (row_stride % 8 == 0);
         if (al)
             hipLaunchKernelGGL((topw_partial_kernel<uint16_t, true>), grid, block, 0, st,
-                               (const uint16_t *)logits, row_stride, V, W, p.nsub, p.sub_per_wg,
-                               p.nchunk, wk, wm);
+                               (const uint16_t *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
+                               p.nlist, wk, wm);
         else
             hipLaunchKernelGGL((topw_partial_kernel<uint16_t, false>), grid, block, 0, st,
-                               (const uint16_t *)logits, row_stride, V, W, p.nsub, p.sub_per_wg,
-                               p.nchunk, wk, wm);
+                               (const uint16_t *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
+                               p.nlist, wk, wm);
     } else {
         const bool al = (addr % 16 == 0) && (row_stride % 4 == 0);
         if (al)
             hipLaunchKernelGGL((topw_partial_kernel<float, true>), grid, block, 0, st,
-                               (const float *)logits, row_stride, V, W, p.nsub, p.sub_per_wg,
-                               p.nchunk, wk, wm);
+                               (const float *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
+                               p.nlist, wk, wm);
         else
             hipLaunchKernelGGL((topw_partial_kernel<float, false>), grid, block, 0, st,
-                               (const float *)logits, row_stride, V, W, p.nsub, p.sub_per_wg,
-                               p.nchunk, wk, wm);
+                               (const float *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
+                               p.nlist, wk, wm);
     }
     jt_status e = launch_status(hipGetLastError());
     if (e != JT_OK)
         return e;
-    hipLaunchKernelGGL(topw_merge_kernel, dim3(rows), dim3(64), 0, st, rows, W, p.nchunk, wk, wm,
+    hipLaunchKernelGGL(topw_merge_kernel, dim3(rows), dim3(64), 0, st, rows, W, p.nlist, wk, wm,
                        ids, logprob, row_lse);
     return launch_status(hipGetLastError());
 }

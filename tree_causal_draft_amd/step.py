@@ -93,6 +93,7 @@ class DeviceStep:
                       argmax_out=self.argmax, err=self.err_verify, workspace=self.verify_ws)
 
     def run(self):
+        """The four calls in order on the current stream."""
         if "topw" in self.parts:
             self.topw()
         self.mask()
@@ -100,3 +101,29 @@ class DeviceStep:
             self.attention()
         if "verify" in self.parts:
             self.verify()
+
+    def run_concurrent(self):
+        """The same four calls with their independence exposed to the GPU: top-W (draft
+        logits only) on a side stream from the start; after the mask, verification on a
+        second side stream beside the attention.  Both side streams rejoin the current
+        stream before return, so the step is still one stream-ordered unit (and can be
+        captured into one graph).  Streams keep the default priority."""
+        cur = torch.cuda.current_stream()
+        if not hasattr(self, "_side"):
+            self._side = (torch.cuda.Stream(device=self.dev), torch.cuda.Stream(device=self.dev))
+        s_topw, s_verify = self._side
+        if "topw" in self.parts:
+            s_topw.wait_stream(cur)
+            with torch.cuda.stream(s_topw):
+                self.topw()
+        self.mask()
+        if "verify" in self.parts:
+            s_verify.wait_stream(cur)
+            with torch.cuda.stream(s_verify):
+                self.verify()
+        if "attn" in self.parts:
+            self.attention()
+        if "topw" in self.parts:
+            cur.wait_stream(s_topw)
+        if "verify" in self.parts:
+            cur.wait_stream(s_verify)
