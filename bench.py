@@ -9,9 +9,21 @@ timed.  Inputs are resident in HBM before the timed region; input sets are rotat
 that one rotation exceeds twice the 256 MB last-level cache (cold-cache figures).
 
 The JSON line reports the low-budget workload (B=16) as the headline and the
-high-budget workload (B=256) in "high_budget"; per-entry-point times come from HIP
-events recorded on the stream the kernels run on.  "cpu_baseline" times the CPU oracle
-(single thread) on full steps of the headline workload.
+high-budget workload (B=256) in "high_budget".  Every figure is timed with HIP events
+on the stream the work runs on, around back-to-back replays of a hipGraph that holds
+one step (or one call of one entry point) per cold input set:
+  value / ms_per_step   whole step, top-W and verification on side streams
+  calls[*].us           each entry point alone (the roofline's per-launch time)
+"cpu_baseline" times the CPU oracle (single thread) on full steps of the headline
+workload.
+
+Profiling modes (their output feeds the summaries kept under profiles/):
+  --calls-only          time each entry point alone, nothing else (for a kernel trace)
+  --traffic-run NAME    launch each entry point of workload NAME on cold input sets,
+                        then a 1 GiB device-to-device copy that calibrates the
+                        FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)
+  --traffic-summarize NAME FETCH_DIR WRITE_DIR
+                        HBM bytes per launch from those two counter runs
 """
 from __future__ import annotations
 
@@ -34,7 +46,7 @@ CALLS = ("topw", "mask", "attention", "verify")
 KERNELS = {
     "topw": ["topw_partial_kernel", "topw_merge_kernel"],
     "mask": ["build_mask_kernel"],
-    "attention": ["attn_mfma_kernel", "attn_combine_kernel", "attn_simple_kernel"],
+    "attention": ["attn_bf16_kernel", "attn_combine_kernel", "attn_simple_kernel"],
     "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
 }
 
@@ -121,7 +133,7 @@ def _time_graph(g, launches_per_replay, total_launches, warmup):
     return 1e3 * a.elapsed_time(b) / (reps * launches_per_replay), reps * launches_per_replay
 
 
-def time_workload(name, steps, warmup, seed, log=print):
+def time_workload(name, steps, warmup, seed, log=print, calls_only=False):
     import torch
     from tree_causal_draft_amd import workload as wl
     from tree_causal_draft_amd.step import DeviceStep
@@ -135,6 +147,11 @@ def time_workload(name, steps, warmup, seed, log=print):
     rot = Rotation(st, nsets)
     log(f"[bench] {name}: footprint {fp / 1e6:.1f} MB per set, {nsets} sets rotated")
     cur = torch.cuda.current_stream()
+    eager_us = step_us = serial_us = None
+    graph_ok = None
+    if calls_only:
+        return _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us,
+                           serial_us, graph_ok, log)
 
     # ---- eager reference run (also the graph-vs-eager check)
     for i in range(max(warmup, nsets)):
@@ -174,6 +191,13 @@ def time_workload(name, steps, warmup, seed, log=print):
     log(f"[bench] {name}: eager {eager_us:.1f} us/step, graph one-stream {serial_us:.1f} us/step, "
         f"graph concurrent {step_us:.1f} us/step ({nsteps} steps), replay == eager: {graph_ok}")
 
+    return _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us,
+                       serial_us, graph_ok, log)
+
+
+def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, serial_us,
+                graph_ok, log):
+    import torch
     # ---- each entry point alone: one graph of nsets launches (one per cold input set)
     per_call_us = {}
     for c in CALLS:
@@ -283,6 +307,95 @@ def roofline_line(res, call):
     return r
 
 
+CALIB_BYTES = 1 << 30
+
+
+def traffic_run(name, seed, reps=3, log=print):
+    """Launch every entry point of one workload eagerly on cold input sets, then one
+    1 GiB device-to-device copy (the counter calibration).  Meant to run under
+    ``rocprofv3 --pmc FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``."""
+    import torch
+    from tree_causal_draft_amd import workload as wl
+    from tree_causal_draft_amd.step import DeviceStep
+    w = wl.make(name, seed)
+    st = DeviceStep(w, "cuda:0")
+    nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(footprint(st), 1))))
+    rot = Rotation(st, nsets)
+    for c in CALLS:
+        for i in range(reps * nsets):
+            getattr(rot.steps[i % nsets], c)()
+        torch.cuda.synchronize()
+    del rot, st
+    torch.cuda.empty_cache()
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] traffic run {name}: {reps} x {nsets} launches per entry point, "
+        f"then a {CALIB_BYTES >> 20} MiB copy")
+
+
+def _counter_rows(path, counter):
+    """(dispatch_id, kernel_name, value summed over the dispatch) from a rocprofv3 db."""
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise FileNotFoundError(f"no rocprofv3 database under {path}")
+    con = sqlite3.connect(dbs[0])
+    rows = con.execute("select dispatch_id, kernel_name, sum(value) from counters_collection "
+                       "where counter_name = ? group by dispatch_id, kernel_name "
+                       "order by dispatch_id", (counter,)).fetchall()
+    con.close()
+    return rows
+
+
+def traffic_summarize(name, fetch_dir, write_dir):
+    """Per entry point, HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE) KiB summed over the
+    entry point's kernels, divided by its launch count, each counter scaled by
+    (bytes the calibration copy moved) / (what the counter read for it)."""
+    out = {"counters": {}}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(path, counter)
+        ours = [r for r in rows if any(k in r[1] for ks in KERNELS.values() for k in ks)]
+        last = max(r[0] for r in ours)
+        calib = [r for r in rows if r[0] > last and "copyBuffer" in r[1]]
+        if not calib:
+            raise RuntimeError(f"{counter}: no calibration copy after the last step kernel")
+        kib = sum(r[2] for r in calib)
+        factor = CALIB_BYTES / (kib * 1024.0)
+        out["counters"][counter] = {"calibration_kib": kib, "scale": factor}
+        for call, ks in KERNELS.items():
+            first = [r for r in ours if ks[0] in r[1] or (call == "attention" and ks[2] in r[1])]
+            tot = sum(r[2] for r in ours if any(k in r[1] for k in ks))
+            n = len(first)
+            if n:
+                per.setdefault(call, {})[counter] = tot * 1024.0 * factor / n
+                per[call]["launches"] = n
+    out["entries"] = {}
+    for call, d in per.items():
+        if "FETCH_SIZE" in d and "WRITE_SIZE" in d:
+            out["entries"][call] = {
+                "fetch_bytes_per_launch": int(d["FETCH_SIZE"]),
+                "write_bytes_per_launch": int(d["WRITE_SIZE"]),
+                "bytes_per_launch": int(d["FETCH_SIZE"] + d["WRITE_SIZE"]),
+                "launches": d["launches"], "src_sha": _kernel_hash(call)}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {"entries": {}, "counters": {}}
+    allrec["entries"][name] = out["entries"]
+    allrec["counters"][name] = out["counters"]
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({name: out}, indent=1, sort_keys=True))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,11 +405,17 @@ def main():
     ap.add_argument("--secondary", default="high_budget", help="'' to skip")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--calls-only", action="store_true")
+    ap.add_argument("--traffic-run", metavar="NAME")
+    ap.add_argument("--traffic-summarize", nargs=3, metavar=("NAME", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how the step would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the step has no multi-GPU path here "
+              "(sequences and KV groups would shard with no exchange).", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_summarize:
+        traffic_summarize(*args.traffic_summarize)
+        return
 
     import torch
     import tree_causal_draft_amd as jt
@@ -307,18 +426,24 @@ def main():
         sys.exit(2)
     log = lambda m: print(m, file=sys.stderr, flush=True)
     seed_of = lambda n: 1000 * (wl.CONFIG_ORDER.index(n) + 1)
+    if args.traffic_run:
+        traffic_run(args.traffic_run, seed_of(args.traffic_run), log=log)
+        return
 
-    results = [time_workload(args.workload, args.steps, args.warmup, seed_of(args.workload),
-                             log=log)]
-    for name in [n for n in args.secondary.split(",") if n]:
-        results.append(time_workload(name, args.steps, args.warmup, seed_of(name), log=log))
-    cpu = None if args.no_cpu else cpu_baseline(args.workload, seed_of(args.workload),
-                                                args.cpu_seconds, log=log)
+    names = [args.workload] + [n for n in args.secondary.split(",") if n]
+    results = [time_workload(n, args.steps, args.warmup, seed_of(n), log=log,
+                             calls_only=args.calls_only) for n in names]
+    cpu = None
+    if not args.no_cpu and not args.calls_only:
+        cpu = cpu_baseline(args.workload, seed_of(args.workload), args.cpu_seconds, log=log)
 
     def summary(r):
         c = r["w"].cfg
         return f"{c.name}: S={c.S} prefix={c.prefix} B={c.B} N={c.N} W={c.W} " \
                f"heads {c.Hq}/{c.Hkv} d={c.d} V={c.V} {c.dtype}"
+
+    def rate(us):
+        return None if us is None else round(1e6 / us, 1)
 
     prim = results[0]
     us = prim["step_us"]
@@ -326,12 +451,12 @@ def main():
     c = prim["w"].cfg
     line = {
         "metric": "draft-verify steps/s + tree-attn HBM GB/s / MFMA % at B=16,256 (1xMI355X)",
-        "value": round(1e6 / us, 1),
+        "value": rate(us),
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(us * 1e-3, 6),
+        "ms_per_step": None if us is None else round(us * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -341,20 +466,22 @@ def main():
                    "timing": "hipGraph replay of one step per cold input set; top-W and "
                              "verification on side streams",
                    "cold_sets": prim["nsets"]},
-        "eager_steps_per_s": round(1e6 / prim["eager_us"], 1),
-        "one_stream_graph_steps_per_s": round(1e6 / prim["serial_us"], 1),
+        "eager_steps_per_s": rate(prim["eager_us"]),
+        "one_stream_graph_steps_per_s": rate(prim["serial_us"]),
         "graph_matches_eager": prim["graph_ok"],
         "calls": prim["calls"],
         "roofline": roofline_line(prim, dom),
         "attention_roofline": roofline_line(prim, "attention"),
         "cpu_baseline": cpu,
     }
+    if args.calls_only:
+        line["mode"] = "calls-only (entry points timed alone; no whole-step figure)"
     for r in results[1:]:
         line[r["workload"]] = {
             "workload": summary(r),
-            "steps_per_s": round(1e6 / r["step_us"], 1),
-            "eager_steps_per_s": round(1e6 / r["eager_us"], 1),
-            "one_stream_graph_steps_per_s": round(1e6 / r["serial_us"], 1),
+            "steps_per_s": rate(r["step_us"]),
+            "eager_steps_per_s": rate(r["eager_us"]),
+            "one_stream_graph_steps_per_s": rate(r["serial_us"]),
             "graph_matches_eager": r["graph_ok"],
             "calls": r["calls"],
             "attention_roofline": roofline_line(r, "attention"),

@@ -14,10 +14,9 @@
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library never
  *     allocates, frees or keeps any of them after the call returns.
  *   - Scratch memory is passed in as `workspace` after a *_workspace_size() query; a
- *     NULL workspace is allowed only when the query returns 0.  A workspace must be
- *     zero-filled before its first use (it holds arrival counters); every call leaves it
- *     zero-filled again, so one zero-fill at allocation is enough.  Calls that overlap in
- *     time need distinct workspaces.
+ *     NULL workspace is allowed only when the query returns 0.  Its contents need no
+ *     initialisation and are meaningless after the call.  Calls that overlap in time
+ *     need distinct workspaces.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous and
  *     stream-ordered; outputs are valid once the stream reaches them.  No call
  *     synchronises the host.  The library holds no state: concurrent calls on
