@@ -400,7 +400,8 @@ __device__ __forceinline__ void tr16_x8(uint32_t aa, uint32_t ab, i32x2_t (&r)[8
 // Merge of one unit's split-KV partials for output items it .. (row, 8 columns), step
 // `stride`.  Partial c of a row holds m_c (log2 domain), l_c and O_c / l_c in bf16; the
 // merged row is sum_c 2^(m_c - M) l_c (O_c/l_c) / sum_c 2^(m_c - M) l_c, M = max_c m_c.
-template <int D>
+// NB chunks are loaded per round trip (the host picks NB >= the chunk count when it can).
+template <int D, int NB>
 __device__ void attn_merge_unit(const AttnArgs &a, const AttnPlan &pl, const AttnWs &w,
                                 int unit, int it, int stride)
 {
@@ -417,25 +418,25 @@ __device__ void attn_merge_unit(const AttnArgs &a, const AttnPlan &pl, const Att
         const int r = rt * pl.rt + rl;
         if (r >= G * B)
             continue;
-        // Chunks are read 8 at a time with every load of a batch issued before any is used,
+        // Chunks are read NB at a time with every load of a batch issued before any is used,
         // and folded with an online max (one pass).  The reads do not wait for the prefix
         // length (inactive chunks' slots lie inside the workspace); a chunk k >= nact is
         // dropped by selection, never multiplied in, since its bytes are stale.
         const int64_t base = (int64_t)unit * pl.n_chunks * pl.rt + rl;
         float M = -INFINITY, l = 0.f;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < pl.n_chunks; k0 += 8) {
-            float2 ml[8];
-            uint4 u[8];
+        for (int k0 = 0; k0 < pl.n_chunks; k0 += NB) {
+            float2 ml[NB];
+            uint4 u[NB];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < NB; ++q) {
                 const int k = min(k0 + q, pl.n_chunks - 1);
                 const int64_t slot = base + (int64_t)k * pl.rt;
                 ml[q] = w.ml[slot];
                 u[q] = *reinterpret_cast<const uint4 *>(w.o + slot * D + sgm * 8);
             }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < NB; ++q) {
                 const bool use = k0 + q < nact && k0 + q < pl.n_chunks;
                 const float mk = use ? ml[q].x : -INFINITY;
                 if (mk == -INFINITY)
@@ -930,7 +931,7 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 }
 
 // Separate merge pass for large units: one thread per (unit, row, 8 output columns).
-template <int D>
+template <int D, int NB>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
@@ -939,7 +940,7 @@ attn_combine_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
     const int unit = (int)(t / per_unit);
     if (unit >= pl.units)
         return;
-    attn_merge_unit<D>(a, pl, ws, unit, (int)(t % per_unit), (int)per_unit);
+    attn_merge_unit<D, NB>(a, pl, ws, unit, (int)(t % per_unit), (int)per_unit);
 }
 
 // ------------------------------------------------------------------ host side --
@@ -974,8 +975,13 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
     if (e != JT_OK || p.n_chunks == 1)
         return e;
     const long threads = (long)p.units * p.rt * (D / 8);
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       st, a, p, w);
+    const dim3 cgrid((unsigned)((threads + 255) / 256)), cblock(256);
+    // 16 chunks per round trip only where that makes it a single trip; wider batches cost
+    // more in registers (occupancy) and padded loads than the trips they save
+    if (p.n_chunks > 8 && p.n_chunks <= 16)
+        hipLaunchKernelGGL((attn_combine_kernel<D, 16>), cgrid, cblock, 0, st, a, p, w);
+    else
+        hipLaunchKernelGGL((attn_combine_kernel<D, 8>), cgrid, cblock, 0, st, a, p, w);
     return launch_status(hipGetLastError());
 }
 

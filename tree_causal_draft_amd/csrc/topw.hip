@@ -267,16 +267,42 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
     const int r = blockIdx.x;
     const int lane = threadIdx.x;
     const int n = nchunk * W;
-    for (int i = lane; i < n; i += 64)
-        keys[i] = ws_keys[(int64_t)r * n + i];
+    // Every load is issued before any result is used (one memory round trip for lists of
+    // up to 64 * kKeyBatch keys): the (max, sum) pairs, then the keys.
+    constexpr int kMsPerLane = kMaxLists / kWave;
+    constexpr int kKeyBatch = 16;
+    const float2 *msr = ws_ms + (int64_t)r * nchunk;
+    const uint64_t *src = ws_keys + (int64_t)r * n;
+    float2 ms[kMsPerLane];
+#pragma unroll
+    for (int j = 0; j < kMsPerLane; ++j) {
+        const int c = lane + kWave * j;
+        ms[j] = c < nchunk ? msr[c] : make_float2(-INFINITY, 0.f);
+    }
+    for (int i0 = 0; i0 < n; i0 += kWave * kKeyBatch) {
+        uint64_t kr[kKeyBatch];
+#pragma unroll
+        for (int q = 0; q < kKeyBatch; ++q) {
+            const int i = i0 + lane + kWave * q;
+            kr[q] = i < n ? src[i] : 0ull;
+        }
+#pragma unroll
+        for (int q = 0; q < kKeyBatch; ++q) {
+            const int i = i0 + lane + kWave * q;
+            if (i < n)
+                keys[i] = kr[q];
+        }
+    }
     // LSE over the row
     float m = -INFINITY;
-    for (int c = lane; c < nchunk; c += 64)
-        m = fmaxf(m, ws_ms[(int64_t)r * nchunk + c].x);
+#pragma unroll
+    for (int j = 0; j < kMsPerLane; ++j)
+        m = fmaxf(m, ms[j].x);
     m = wave_max_f32(m);
     float s = 0.f;
-    for (int c = lane; c < nchunk; c += 64) {
-        const float2 p = ws_ms[(int64_t)r * nchunk + c];
+#pragma unroll
+    for (int j = 0; j < kMsPerLane; ++j) {
+        const float2 p = ms[j];
         if (p.x == -INFINITY)
             s += (p.y != p.y) ? p.y : 0.f;
         else

@@ -10,7 +10,8 @@
 // fills the chip while 2048 rows stream whole.  Threads walk their logits in increasing
 // id order with a strict '>' so each keeps the first maximum; the workgroup then takes
 // the largest 64-bit key (order code << 32 | ~id): largest value, lowest id.
-// Phase 2 (one workgroup per sequence, thread v = node v):
+// Phase 2 (one workgroup per sequence, thread v = node v; every global read is issued
+// in one batch, the partial keys fold into LDS with 64-bit atomic max):
 //   ok bits     ok[v] = tokens[v] == am[parent[v]] (root ok), one ballot per 64 nodes;
 //   accepted(v) (anc[v] & ~ok) == 0 -- every node on the root path is ok;
 //   v*          block max of (depth << 16 | 65535 - v) over accepted nodes;
@@ -117,36 +118,82 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
                    int32_t *__restrict__ accept_path, int32_t *__restrict__ bonus,
                    int32_t *__restrict__ argmax_out, int32_t *__restrict__ err)
 {
-    __shared__ int32_t am[JT_MAX_NODES];
+    __shared__ unsigned long long amk[JT_MAX_NODES];
+    __shared__ uint32_t amn[JT_MAX_NODES];
+    __shared__ uint64_t ancl[JT_MAX_NODES][4];
     __shared__ uint64_t okw[4];
     __shared__ uint32_t wbest[4];
+    __shared__ int fl[4];
     const int s = blockIdx.x;
     const int v = threadIdx.x;
     const int lane = v & 63, wid = v >> 6;
     const int64_t nb = (int64_t)s * B + v;
 
-    int flags = 0;
-    int p = -1, dv = 0;
     if (v < B) {
-        uint64_t k = 0ull;
-        uint32_t nn = 0u;
-        for (int c = 0; c < nchunk; ++c) {
-            const uint64_t kc = ws_keys[nb * nchunk + c];
-            k = kc > k ? kc : k;
-            nn |= ws_nan[nb * nchunk + c];
-        }
-        am[v] = (k == 0ull) ? 0 : (int32_t)key_id(k);
-        if (nn)
-            flags |= JT_DEV_NAN;
+        amk[v] = 0ull;
+        amn[v] = 0u;
+    }
+    __syncthreads();
+
+    // One memory round trip: the node's own parent, depth, token and ancestor row, and a
+    // share of the B * nchunk partial argmax keys (item i = node i / nchunk, chunk
+    // i % nchunk), all issued before any is used.
+    int p = -1, dv = 0, tok = 0;
+    uint64_t a0 = 0ull, a1 = 0ull, a2 = 0ull, a3 = 0ull;
+    if (v < B) {
         p = parent[nb];
+        dv = depth[nb];
+        tok = tokens[nb];
+        const uint64_t *ar = anc + nb * 4;
+        a0 = ar[0];
+        a1 = ar[1];
+        a2 = ar[2];
+        a3 = ar[3];
+    }
+    const int items = B * nchunk;
+    const uint64_t *kbase = ws_keys + (int64_t)s * items;
+    const uint32_t *nbase = ws_nan + (int64_t)s * items;
+    constexpr int kItemBatch = 8;
+    for (int i0 = 0; i0 < items; i0 += 256 * kItemBatch) {
+        uint64_t kc[kItemBatch];
+        uint32_t nc[kItemBatch];
+#pragma unroll
+        for (int q = 0; q < kItemBatch; ++q) {
+            const int i = i0 + v + 256 * q;
+            kc[q] = i < items ? kbase[i] : 0ull;
+            nc[q] = i < items ? nbase[i] : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < kItemBatch; ++q) {
+            const int i = i0 + v + 256 * q;
+            if (i < items) {
+                const int u = i / nchunk;
+                atomicMax(&amk[u], (unsigned long long)kc[q]);
+                if (nc[q])
+                    atomicOr(&amn[u], nc[q]);
+            }
+        }
+    }
+    int flags = 0;
+    if (v < B) {
+        ancl[v][0] = a0;
+        ancl[v][1] = a1;
+        ancl[v][2] = a2;
+        ancl[v][3] = a3;
         if (v == 0 ? (p != -1) : (p < 0 || p >= v))
             flags |= JT_DEV_BAD_PARENT;
-        dv = depth[nb];
         if (dv > N || dv < 0)
             flags |= JT_DEV_DEPTH_GT_N;
     }
+    __syncthreads();
+    int am_v = 0;
+    if (v < B) {
+        const uint64_t k = amk[v];
+        am_v = (k == 0ull) ? 0 : (int32_t)key_id(k);
+        if (amn[v])
+            flags |= JT_DEV_NAN;
+    }
     // OR of the flags over the block
-    __shared__ int fl[4];
     int f = flags;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
@@ -156,7 +203,11 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
     __syncthreads();
     f = fl[0] | fl[1] | fl[2] | fl[3];
     if (argmax_out && v < B)
-        argmax_out[nb] = am[v];
+        argmax_out[nb] = am_v;
+    auto am_of = [&](int u) {
+        const uint64_t k = amk[u];
+        return (k == 0ull) ? 0 : (int32_t)key_id(k);
+    };
     int32_t *path = accept_path + (int64_t)s * (N + 1);
     if (f & (JT_DEV_BAD_PARENT | JT_DEV_DEPTH_GT_N)) {
         if (f & JT_DEV_BAD_PARENT)
@@ -165,23 +216,21 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
             path[k] = (k == 0) ? 0 : -1;
         if (v == 0) {
             accept_len[s] = 0;
-            bonus[s] = am[0];
+            bonus[s] = am_v;
             if (err)
                 err[s] = f;
         }
         return;
     }
-    const bool ok = (v < B) && (v == 0 || tokens[nb] == am[p]);
+    const bool ok = (v < B) && (v == 0 || tok == am_of(p));
     const uint64_t word = __ballot(ok);
     if (lane == 0)
         okw[wid] = word;
     __syncthreads();
     uint32_t key = 0u;
-    uint64_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
     if (v < B) {
-        const uint64_t *ar = anc + nb * 4;
-        a0 = ar[0]; a1 = ar[1]; a2 = ar[2]; a3 = ar[3];
-        const bool accepted = ((a0 & ~okw[0]) | (a1 & ~okw[1]) | (a2 & ~okw[2]) | (a3 & ~okw[3])) == 0ull;
+        const bool accepted = ((ancl[v][0] & ~okw[0]) | (ancl[v][1] & ~okw[1]) |
+                               (ancl[v][2] & ~okw[2]) | (ancl[v][3] & ~okw[3])) == 0ull;
         if (accepted)
             key = ((uint32_t)dv << 16) | (uint32_t)(65535 - v);
     }
@@ -197,14 +246,11 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
     // path: every ancestor u of v* (itself included) sits at index depth[u]
     for (int k = len + 1 + v; k <= N; k += blockDim.x)
         path[k] = -1;
-    if (v < B) {
-        const uint64_t *ar = anc + ((int64_t)s * B + vstar) * 4;
-        if ((ar[v >> 6] >> (v & 63)) & 1ull)
-            path[dv] = v;
-    }
+    if (v < B && ((ancl[vstar][v >> 6] >> (v & 63)) & 1ull))
+        path[dv] = v;
     if (v == 0) {
         accept_len[s] = len;
-        bonus[s] = am[vstar];
+        bonus[s] = am_of(vstar);
         if (err)
             err[s] = f;
     }
