@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step = jt_topw_per_depth (draft logits) -> jt_build_tree_mask -> jt_tree_attention
--> jt_verify_greedy (target logits), all sequences, one stream.  The tree (parent,
+-> jt_verify_greedy (target logits), all sequences; for bf16 it runs as one
+jt_draft_verify_step call (the same four steps in two launches).  The tree (parent,
 tokens) is an input of the step, built by the seeded workload generator, and is not
 timed.  Inputs are resident in HBM before the timed region; input sets are rotated so
 that one rotation exceeds twice the 256 MB last-level cache (cold-cache figures).
@@ -12,8 +13,10 @@ The JSON line reports the low-budget workload (B=16) as the headline and the
 high-budget workload (B=256) in "high_budget".  Every figure is timed with HIP events
 on the stream the work runs on, around back-to-back replays of a hipGraph that holds
 one step (or one call of one entry point) per cold input set:
-  value / ms_per_step   whole step, top-W and verification on side streams
-  calls[*].us           each entry point alone (the roofline's per-launch time)
+  value / ms_per_step   whole step (jt_draft_verify_step; the four calls with top-W and
+                        verification on side streams where it does not apply)
+  calls[*].us           each entry point alone (the roofline's per-launch time; "step" is
+                        jt_draft_verify_step)
 "cpu_baseline" times the CPU oracle (single thread) on full steps of the headline
 workload.
 
@@ -48,6 +51,7 @@ KERNELS = {
     "mask": ["build_mask_kernel"],
     "attention": ["attn_bf16_kernel", "attn_combine_kernel", "attn_simple_kernel"],
     "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
+    "step": ["step_phase1", "step_phase2"],
 }
 
 
@@ -66,6 +70,7 @@ def algorithmic(w):
     b["verify"] = S * B * V * e + S * B * (4 + 4 + 32 + 4 + 4) + S * (N + 1 + 3) * 4
     vis = (P[:, None] + w.depth.astype(np.int64) + 1).sum()
     flops = 4 * c.Hq * c.d * int(vis)
+    b["step"] = b["topw"] + b["mask"] + b["attention"] + b["verify"]
     return b, flops
 
 
@@ -186,13 +191,20 @@ def time_workload(name, steps, warmup, seed, log=print, calls_only=False):
         return [st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob, st.attn_out, st.anc]
 
     serial_us, nsteps, serial_ok = graph_step("run")
-    step_us, nsteps, conc_ok = graph_step("run_concurrent")
-    graph_ok = serial_ok and conc_ok
+    conc_us, nsteps, conc_ok = graph_step("run_concurrent")
+    fused_us, fused_ok = None, True
+    if hasattr(st, "step_ws"):
+        fused_us, nsteps, fused_ok = graph_step("run_fused")
+    graph_ok = serial_ok and conc_ok and fused_ok
+    step_us = fused_us if fused_us is not None else conc_us
     log(f"[bench] {name}: eager {eager_us:.1f} us/step, graph one-stream {serial_us:.1f} us/step, "
-        f"graph concurrent {step_us:.1f} us/step ({nsteps} steps), replay == eager: {graph_ok}")
+        f"graph concurrent {conc_us:.1f} us/step, fused {fused_us} us/step ({nsteps} steps), "
+        f"replay == eager: {graph_ok}")
 
-    return _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us,
-                       serial_us, graph_ok, log)
+    res = _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us,
+                      serial_us, graph_ok, log)
+    res["conc_us"], res["fused_us"] = conc_us, fused_us
+    return res
 
 
 def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, serial_us,
@@ -200,15 +212,16 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
     import torch
     # ---- each entry point alone: one graph of nsets launches (one per cold input set)
     per_call_us = {}
-    for c in CALLS:
-        g = _capture([getattr(s, c) for s in rot.steps])
+    calls_here = CALLS + (("step",) if hasattr(st, "step_ws") else ())
+    for c in calls_here:
+        g = _capture([getattr(s, "run_fused" if c == "step" else c) for s in rot.steps])
         per_call_us[c], _ = _time_graph(g, nsets, steps, warmup)
         del g
-    log(f"[bench] {name}: per call " + " ".join(f"{c}={per_call_us[c]:.2f}us" for c in CALLS))
+    log(f"[bench] {name}: per call " + " ".join(f"{c}={per_call_us[c]:.2f}us" for c in calls_here))
 
     bytes_, flops = algorithmic(w)
     calls = {}
-    for c in CALLS:
+    for c in calls_here:
         us = per_call_us[c]
         calls[c] = {"us": round(us, 3), "bytes": int(bytes_[c]),
                     "GBps": round(bytes_[c] / (us * 1e-6) / 1e9, 1)}
@@ -225,10 +238,12 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
 
 
 def roofline(res, call):
+    """Roofline of one entry point: the binding resource is the one whose floor (bytes at
+    the HBM peak, or flops at the bf16 MFMA peak) is longer."""
     w = res["w"]
     us = res["per_call_us"][call]
     byt = res["bytes"][call]
-    if call == "attention":
+    if call in ("attention", "step"):
         ai = res["flops"] / byt
         if ai > (MFMA_BF16_PEAK_TFS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.cfg.dtype == "bf16":
             ach = res["flops"] / (us * 1e-6) / 1e12
@@ -278,7 +293,8 @@ def _cpu_model():
 def _kernel_hash(call):
     import hashlib
     files = {"topw": ["topw.hip"], "mask": ["mask.hip"], "attention": ["attn.hip"],
-             "verify": ["verify.hip"]}[call]
+             "verify": ["verify.hip"],
+             "step": ["mask.hip", "topw.hip", "verify.hip", "attn.hip", "step.hip"]}[call]
     h = hashlib.sha256()
     for f in files + ["jt_internal.h"]:
         with open(os.path.join(ROOT, "tree_causal_draft_amd", "csrc", f), "rb") as fh:
@@ -321,7 +337,7 @@ def traffic_run(name, seed, reps=3, log=print):
     st = DeviceStep(w, "cuda:0")
     nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(footprint(st), 1))))
     rot = Rotation(st, nsets)
-    for c in CALLS:
+    for c in CALLS + (("run_fused",) if hasattr(st, "step_ws") else ()):
         for i in range(reps * nsets):
             getattr(rot.steps[i % nsets], c)()
         torch.cuda.synchronize()
@@ -368,6 +384,8 @@ def traffic_summarize(name, fetch_dir, write_dir):
         out["counters"][counter] = {"calibration_kib": kib, "scale": factor}
         for call, ks in KERNELS.items():
             first = [r for r in ours if ks[0] in r[1] or (call == "attention" and ks[2] in r[1])]
+            if call == "attention":  # the fused step's phase kernels inline attn_* code only
+                first = [r for r in first if "step_phase" not in r[1]]
             tot = sum(r[2] for r in ours if any(k in r[1] for k in ks))
             n = len(first)
             if n:
@@ -445,10 +463,19 @@ def main():
     def rate(us):
         return None if us is None else round(1e6 / us, 1)
 
+    def dominant(r):
+        if "step" in r["per_call_us"]:
+            return "step"
+        return max(CALLS, key=lambda k: r["per_call_us"][k])
+
     prim = results[0]
     us = prim["step_us"]
-    dom = max(CALLS, key=lambda k: prim["per_call_us"][k])
+    dom = dominant(prim)
     c = prim["w"].cfg
+    fused = prim.get("fused_us") is not None
+    timing = ("hipGraph replay of one jt_draft_verify_step (two launches) per cold input set"
+              if fused else "hipGraph replay of one step per cold input set; top-W and "
+              "verification on side streams")
     line = {
         "metric": "draft-verify steps/s + tree-attn HBM GB/s / MFMA % at B=16,256 (1xMI355X)",
         "value": rate(us),
@@ -462,12 +489,10 @@ def main():
         "vs_baseline": None,
         "dtype": c.dtype,
         "data": "synthetic (seeded; tree prebuilt, not timed)",
-        "config": {"workload": summary(prim),
-                   "timing": "hipGraph replay of one step per cold input set; top-W and "
-                             "verification on side streams",
-                   "cold_sets": prim["nsets"]},
+        "config": {"workload": summary(prim), "timing": timing, "cold_sets": prim["nsets"]},
         "eager_steps_per_s": rate(prim["eager_us"]),
         "one_stream_graph_steps_per_s": rate(prim["serial_us"]),
+        "four_calls_concurrent_graph_steps_per_s": rate(prim.get("conc_us")),
         "graph_matches_eager": prim["graph_ok"],
         "calls": prim["calls"],
         "roofline": roofline_line(prim, dom),
@@ -482,10 +507,11 @@ def main():
             "steps_per_s": rate(r["step_us"]),
             "eager_steps_per_s": rate(r["eager_us"]),
             "one_stream_graph_steps_per_s": rate(r["serial_us"]),
+            "four_calls_concurrent_graph_steps_per_s": rate(r.get("conc_us")),
             "graph_matches_eager": r["graph_ok"],
             "calls": r["calls"],
             "attention_roofline": roofline_line(r, "attention"),
-            "roofline": roofline_line(r, max(CALLS, key=lambda k: r["per_call_us"][k])),
+            "roofline": roofline_line(r, dominant(r)),
         }
     print(json.dumps(line), flush=True)
 

@@ -187,6 +187,41 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
                            int32_t *bonus, int32_t *argmax_out, int32_t *err,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The whole step in one call -- steps 3, 1, 2 and 4 with the arguments and outputs
+ * documented above, in two kernel launches instead of seven: the bandwidth-bound logit
+ * scans (top-W partials, target arg-max partials), the mask and the attention's main pass
+ * share the first launch; the split-KV merge, the top-W merge and the verification walk
+ * share the second.  The attention builds the ancestor rows it needs from `parent`
+ * itself, so it does not wait for the mask.  Every output equals what the four separate
+ * calls produce; `err` (int32 [S], optional) receives the OR of the flags the mask,
+ * attention and verification calls would report.
+ *
+ *   draft_logits   [S*N, draft_row_stride]   target_logits [S*B, target_row_stride]
+ *   (both dtype, V used columns, 16-byte aligned with row strides a multiple of 8)
+ *   W, N           as for jt_topw_per_depth (rows = S*N) and jt_verify_greedy
+ *   attention args as for jt_tree_attention (anc is produced here)
+ * Supported: dtype JT_BF16 only; d in {64, 128}; the ranges of the four calls.  Anything
+ * else returns JT_ERR_DTYPE / JT_ERR_ALIGN / JT_ERR_SHAPE: use the four calls instead.
+ */
+size_t jt_step_workspace_size(int32_t S, int32_t B, int32_t N, int32_t W, int32_t V, int32_t Hq,
+                              int32_t Hkv, int32_t d, int32_t max_prefix, int32_t block_size,
+                              jt_dtype dtype);
+jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_stride,
+                               const void *target_logits, int64_t target_row_stride, int32_t V,
+                               int32_t W, const int32_t *parent, const int32_t *tokens,
+                               int32_t S, int32_t B, int32_t N, const void *q,
+                               const void *k_tree, const void *v_tree, const void *k_prefix,
+                               const void *v_prefix, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               int32_t num_blocks, const int32_t *prefix_len, int32_t max_prefix,
+                               int32_t Hq, int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
+                               int32_t *ids, float *logprob, float *row_lse, uint64_t *anc,
+                               int32_t *depth, void *out, float *lse, int32_t *accept_len,
+                               int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                               int32_t *err, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,142 @@
+"""GPU parity of jt_draft_verify_step (the four steps in two launches).
+
+The fused call must reproduce, bit for bit, every output of the four separate calls on the
+same inputs (those are held to the oracle by the other GPU tests), and its err must be the
+OR of their flags.  One case is also compared with the oracle directly.  Attention outputs
+of a sequence with a bad parent array are unspecified and are not compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_causal_draft_amd import workload as wl
+from tree_causal_draft_amd.step import DeviceStep
+from gpu_util import BF16_ATOL, BF16_RTOL, LP_ATOL, LP_RTOL, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("ids", "logprob", "row_lse", "anc", "depth", "accept_len", "accept_path", "bonus",
+        "argmax", "attn_out", "lse")
+ATTN = ("attn_out", "lse")
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32 if t.element_size() == 4 else torch.int64)
+
+
+def _compare(w, what, tamper=None):
+    need_gpu()
+    c = w.cfg
+    print(f"[step] {what}: S={c.S} B={c.B} N={c.N} W={c.W} V={c.V} heads {c.Hq}/{c.Hkv} "
+          f"d={c.d} paged={w.block_table is not None}", flush=True)
+    st = DeviceStep(w, "cuda:0")
+    if tamper:
+        tamper(st)
+    st.run()
+    torch.cuda.synchronize()
+    sep = {k: getattr(st, k).clone() for k in OUTS}
+    err_sep = (st.err_mask | st.err_attn | st.err_verify).clone()
+    for k in OUTS:
+        getattr(st, k).view(torch.uint8).fill_(0x7F)
+    st.err_step.fill_(-1)
+    st.run_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(st.err_step, err_sep), (what, host(st.err_step), host(err_sep))
+    bad_parent = (err_sep & 1) != 0
+    for k in OUTS:
+        a, b = _bits(getattr(st, k)), _bits(sep[k])
+        if k in ATTN and bool(bad_parent.any()):
+            keep = ~bad_parent
+            a, b = a[keep], b[keep]
+        assert torch.equal(a, b), (what, k)
+    return st, err_sep
+
+
+def _small(name, **kw):
+    base = dict(V=8192)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("name", ["low_budget", "high_budget"])
+def test_benchmarked_configs_full_size(name):
+    w = wl.make(name, 811)
+    _, err = _compare(w, name)
+    assert int(err.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("name", ["moe_verify", "ragged"])
+def test_other_configs_small_vocab(name):
+    w = wl.make(name, 812, **_small(name))
+    _compare(w, name + " V=8192")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(S=3, B=1, N=1, W=2, prefix=70),                      # root only, tiny prefix
+    dict(S=2, B=37, N=5, W=3, prefix=0),                      # no prefix at all
+    dict(S=2, B=256, N=16, W=16, prefix=200, V=5000),         # widest W, ragged vocab tail
+    dict(S=1, B=100, N=9, W=4, prefix=333, d=64),             # head dim 64, 8-wave groups
+    dict(S=5, B=20, N=6, W=5, prefix=129, Hq=24, Hkv=3),      # G = 8
+])
+def test_shapes(kw):
+    kw = dict(kw)
+    V = kw.pop("V", 4096)
+    w = wl.make("low_budget", 813, tree="random", V=V, **kw)
+    _compare(w, f"shape {kw}")
+
+
+def test_flags_bad_parent_nan_bad_block():
+    w = wl.make("ragged", 814, V=4096)
+
+    def tamper(st):
+        par = st.parent.clone()
+        par[1, 5] = 7          # parent after the node: bad array
+        st.parent.copy_(par)
+        tgt = st.target.clone()
+        tgt[3 * w.cfg.B + 2, 100] = float("nan")   # a NaN target logit in sequence 3
+        st.target.copy_(tgt)
+        bt = st.block_table.clone()
+        bt[5, 0] = w.num_blocks + 3                # a block outside the pool in sequence 5
+        st.block_table.copy_(bt)
+
+    st, err = _compare(w, "flags", tamper)
+    e = host(err)
+    assert e[1] & 1 and e[3] & 8 and e[5] & 4, e
+
+
+def test_fused_against_oracle():
+    w = wl.make("low_budget", 815, V=4096, prefix=300, B=40, N=7, W=3, tree="random")
+    st, _ = _compare(w, "oracle check")
+    c = w.cfg
+    ids, lp, lse = oracle.topw(w.draft_logits, c.W)
+    assert np.array_equal(host(st.ids), ids)
+    np.testing.assert_allclose(host(st.logprob), lp, rtol=LP_RTOL, atol=LP_ATOL)
+    ref = oracle.verify_greedy(w.target_logits, w.parent, w.tokens, c.N)
+    for k in ("accept_len", "accept_path", "bonus"):
+        assert np.array_equal(host(getattr(st, k)), ref[k]), k
+    out, _, _ = oracle.tree_attention(w.q, w.k_tree, w.v_tree, w.k_prefix, w.v_prefix,
+                                      w.prefix_len, w.parent, max_prefix=w.max_prefix)
+    got = host(st.attn_out).astype(np.float64)
+    assert (np.abs(got - out) <= BF16_ATOL + BF16_RTOL * np.abs(out)).all()
+
+
+def test_rejects_fp32_and_misaligned_rows():
+    need_gpu()
+    import tree_causal_draft_amd as jt
+    w = wl.make("tiny", 816)
+    st = DeviceStep(w, "cuda:0")
+    assert not hasattr(st, "step_ws")  # fp32 has no fused path
+    with pytest.raises(jt.JTError, match="element type"):
+        jt.draft_verify_step(st.draft, st.target, st.parent, st.tokens, w.cfg.N, w.cfg.W, st.q,
+                             st.k_tree, st.v_tree, st.k_prefix, st.v_prefix, st.prefix_len)
+    w = wl.make("low_budget", 817, V=4096)
+    st = DeviceStep(w, "cuda:0")
+    rows, stride = st.draft.shape
+    buf = torch.empty(rows * stride + 1, dtype=st.draft.dtype, device=st.draft.device)
+    shifted = buf[1:].view(rows, stride)  # contiguous, 2 bytes past a 16-byte boundary
+    shifted.copy_(st.draft)
+    with pytest.raises(jt.JTError, match="misaligned"):
+        jt.draft_verify_step(shifted, st.target, st.parent, st.tokens, w.cfg.N, w.cfg.W, st.q,
+                             st.k_tree, st.v_tree, st.k_prefix, st.v_prefix, st.prefix_len,
+                             workspace=st.step_ws)

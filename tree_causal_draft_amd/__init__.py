@@ -5,7 +5,8 @@ Argument marshalling only: every step of the path runs in the HIP kernels of
 CPU fallback: if the library is missing or fails to load, every call raises.
 
 Entry points (same names as the C ABI in ``include/jt.h``):
-    build_tree_mask, tree_attention, topw_per_depth, verify_greedy
+    build_tree_mask, tree_attention, topw_per_depth, verify_greedy, and
+    draft_verify_step (the four steps in two launches)
 """
 from __future__ import annotations
 
@@ -21,7 +22,8 @@ JT_F32, JT_BF16 = 0, 1
 DEV_BAD_PARENT, DEV_DEPTH_GT_N, DEV_BAD_BLOCK, DEV_NAN, DEV_BAD_PREFIX = 1, 2, 4, 8, 16
 EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
            "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
-           "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy")
+           "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy",
+           "jt_step_workspace_size", "jt_draft_verify_step")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -59,8 +61,14 @@ def lib() -> ctypes.CDLL:
         L.jt_verify_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
         L.jt_verify_greedy.argtypes = ([_vp, _i64, _i32, ctypes.c_int] + [_vp] * 4 +
                                        [_i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp])
+        L.jt_step_workspace_size.restype = _sz
+        L.jt_step_workspace_size.argtypes = [_i32] * 10 + [ctypes.c_int]
+        L.jt_draft_verify_step.argtypes = (
+            [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _i32] + [_vp] * 6 +
+            [_i32, _i32, _i32, _vp] + [_i32] * 4 + [ctypes.c_float, ctypes.c_int] + [_vp] * 13 +
+            [_sz, _vp])
         for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
-                   "jt_verify_greedy"):
+                   "jt_verify_greedy", "jt_draft_verify_step"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -101,8 +109,7 @@ def _workspace(nbytes: int, device, workspace):
         return None, 0
     if workspace is not None:
         return workspace, workspace.numel() * workspace.element_size()
-    # zero-filled once: the library keeps its arrival counters at zero between calls
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def build_tree_mask(parent, anc=None, depth=None, err=None, stream=None):
@@ -213,3 +220,66 @@ def verify_greedy(target_logits, parent, tokens, anc, depth, N, *, V=None, accep
                                   _stream(stream)), "jt_verify_greedy")
     return dict(accept_len=accept_len, accept_path=accept_path, bonus=bonus, argmax=argmax_out,
                 err=err)
+
+
+def step_workspace_size(S, B, N, W, V, Hq, Hkv, d, max_prefix, dtype, block_size=0) -> int:
+    """block_size: paged pool block size, 0 for a contiguous prefix."""
+    return int(lib().jt_step_workspace_size(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_size,
+                                            dtype))
+
+
+def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tree, v_tree,
+                      k_prefix, v_prefix, prefix_len, *, V=None, block_table=None, block_size=16,
+                      num_blocks=None, max_prefix=None, scale=0.0, out=None, lse=None, ids=None,
+                      logprob=None, row_lse=None, anc=None, depth=None, accept_len=None,
+                      accept_path=None, bonus=None, argmax_out=None, err=None, workspace=None,
+                      stream=None):
+    """The four steps in one call (two launches).  draft_logits [S*N, stride] and
+    target_logits [S*B, stride] bf16; the rest as for the separate calls.  Returns a dict
+    of every output."""
+    for t, n in ((draft_logits, "draft_logits"), (target_logits, "target_logits"),
+                 (parent, "parent"), (tokens, "tokens"), (q, "q"), (k_tree, "k_tree"),
+                 (v_tree, "v_tree"), (k_prefix, "k_prefix"), (v_prefix, "v_prefix"),
+                 (prefix_len, "prefix_len")):
+        _need(t, n)
+    S, B = parent.shape
+    _, _, Hq, d = q.shape
+    Hkv = k_tree.shape[2]
+    dt = _dt(q)
+    dstride, tstride = draft_logits.shape[-1], target_logits.shape[-1]
+    V = tstride if V is None else V
+    if block_table is None:
+        Pmax = k_prefix.shape[1] if max_prefix is None else max_prefix
+        maxblk, nblk = 0, 0
+    else:
+        _need(block_table, "block_table")
+        maxblk = block_table.shape[1]
+        Pmax = maxblk * block_size if max_prefix is None else max_prefix
+        nblk = k_prefix.shape[0] if num_blocks is None else num_blocks
+    dev = q.device
+    e = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=dev)
+    out = torch.empty_like(q) if out is None else out
+    lse = e((S, B, Hq), torch.float32) if lse is None else lse
+    ids = e((S * N, W), torch.int32) if ids is None else ids
+    logprob = e((S * N, W), torch.float32) if logprob is None else logprob
+    row_lse = e(S * N, torch.float32) if row_lse is None else row_lse
+    anc = e((S, B, 4), torch.int64) if anc is None else anc
+    depth = e((S, B), torch.int32) if depth is None else depth
+    accept_len = e(S, torch.int32) if accept_len is None else accept_len
+    accept_path = e((S, N + 1), torch.int32) if accept_path is None else accept_path
+    bonus = e(S, torch.int32) if bonus is None else bonus
+    argmax_out = e((S, B), torch.int32) if argmax_out is None else argmax_out
+    err = e(S, torch.int32) if err is None else err
+    need = step_workspace_size(S, B, N, W, V, Hq, Hkv, d, Pmax, dt,
+                               0 if block_table is None else block_size)
+    ws, wsb = _workspace(need, dev, workspace)
+    _check(lib().jt_draft_verify_step(
+        _ptr(draft_logits), dstride, _ptr(target_logits), tstride, V, W, _ptr(parent),
+        _ptr(tokens), S, B, N, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
+        _ptr(v_prefix), _ptr(block_table), maxblk, block_size, nblk, _ptr(prefix_len), Pmax, Hq,
+        Hkv, d, float(scale), dt, _ptr(ids), _ptr(logprob), _ptr(row_lse), _ptr(anc),
+        _ptr(depth), _ptr(out), _ptr(lse), _ptr(accept_len), _ptr(accept_path), _ptr(bonus),
+        _ptr(argmax_out), _ptr(err), _ptr(ws), wsb, _stream(stream)), "jt_draft_verify_step")
+    return dict(ids=ids, logprob=logprob, row_lse=row_lse, anc=anc, depth=depth, out=out,
+                lse=lse, accept_len=accept_len, accept_path=accept_path, bonus=bonus,
+                argmax=argmax_out, err=err)

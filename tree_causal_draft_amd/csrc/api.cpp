@@ -123,6 +123,7 @@ jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tre
     a.prefix_len = prefix_len;
     a.max_prefix = max_prefix;
     a.anc = anc;
+    a.parent = nullptr;
     a.S = S;
     a.B = B;
     a.Hq = Hq;
@@ -217,6 +218,120 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
     return launch_verify(target_logits, row_stride, V, dtype, parent, tokens, anc, depth, S, B, N,
                          accept_len, accept_path, bonus, argmax_out, err, workspace,
                          as_stream(stream));
+}
+
+size_t jt_step_workspace_size(int32_t S, int32_t B, int32_t N, int32_t W, int32_t V, int32_t Hq,
+                              int32_t Hkv, int32_t d, int32_t max_prefix, int32_t block_size,
+                              jt_dtype dtype)
+{
+    if (dtype != JT_BF16 || attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype) != JT_OK ||
+        topw_shape(S * N, V, W, dtype) != JT_OK || verify_shape(S, B, V, N, dtype) != JT_OK ||
+        S == 0)
+        return 0;
+    return step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_size > 0 ? block_size : 0);
+}
+
+jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_stride,
+                               const void *target_logits, int64_t target_row_stride, int32_t V,
+                               int32_t W, const int32_t *parent, const int32_t *tokens,
+                               int32_t S, int32_t B, int32_t N, const void *q,
+                               const void *k_tree, const void *v_tree, const void *k_prefix,
+                               const void *v_prefix, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               int32_t num_blocks, const int32_t *prefix_len, int32_t max_prefix,
+                               int32_t Hq, int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
+                               int32_t *ids, float *logprob, float *row_lse, uint64_t *anc,
+                               int32_t *depth, void *out, float *lse, int32_t *accept_len,
+                               int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                               int32_t *err, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    if (dtype != JT_BF16)
+        return JT_ERR_DTYPE;
+    jt_status st = attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype);
+    if (st == JT_OK)
+        st = verify_shape(S, B, V, N, dtype);
+    if (st == JT_OK && (int64_t)S * N > INT32_MAX)
+        st = JT_ERR_SHAPE;
+    if (st == JT_OK)
+        st = topw_shape(S * N, V, W, dtype);
+    if (st != JT_OK)
+        return st;
+    if (draft_row_stride < V || target_row_stride < V)
+        return JT_ERR_SHAPE;
+    if (S == 0)
+        return JT_OK;
+    if (!target_logits || !parent || !tokens || !q || !k_tree || !v_tree || !prefix_len ||
+        !anc || !depth || !out || !accept_len || !accept_path || !bonus)
+        return JT_ERR_NULL;
+    if (N > 0 && (!draft_logits || !ids || !logprob))
+        return JT_ERR_NULL;
+    if (max_prefix > 0 && (!k_prefix || !v_prefix))
+        return JT_ERR_NULL;
+    if (block_table) {
+        if (!is_pow2(block_size) || max_blocks_per_seq < 0 || num_blocks < 0 ||
+            (int64_t)max_blocks_per_seq * block_size < max_prefix)
+            return JT_ERR_SHAPE;
+    }
+    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
+        (k_prefix && !aligned16(k_prefix)) || (v_prefix && !aligned16(v_prefix)))
+        return JT_ERR_ALIGN;
+    if (!aligned16(target_logits) || target_row_stride % 8 != 0 ||
+        (N > 0 && (!aligned16(draft_logits) || draft_row_stride % 8 != 0)))
+        return JT_ERR_ALIGN;
+    const size_t need = step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix,
+                                       block_table ? block_size : 0);
+    if (!workspace || workspace_bytes < need)
+        return JT_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return JT_ERR_ALIGN;
+    StepLaunch in;
+    AttnArgs &a = in.attn;
+    a.q = q;
+    a.k_tree = k_tree;
+    a.v_tree = v_tree;
+    a.k_prefix = k_prefix;
+    a.v_prefix = v_prefix;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.block_size = block_table ? block_size : 1;
+    a.block_shift = block_table ? log2i(block_size) : 0;
+    a.num_blocks = num_blocks;
+    a.prefix_len = prefix_len;
+    a.max_prefix = max_prefix;
+    a.anc = nullptr;
+    a.parent = parent;
+    a.S = S;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.d = d;
+    a.G = Hq / Hkv;
+    a.dtype = dtype;
+    a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+    a.out = out;
+    a.lse = lse;
+    a.err = nullptr;
+    in.draft = draft_logits;
+    in.target = target_logits;
+    in.draft_stride = draft_row_stride;
+    in.target_stride = target_row_stride;
+    in.V = V;
+    in.W = W;
+    in.N = N;
+    in.ids = ids;
+    in.logprob = logprob;
+    in.row_lse = row_lse;
+    in.parent = parent;
+    in.tokens = tokens;
+    in.anc = anc;
+    in.depth = depth;
+    in.accept_len = accept_len;
+    in.accept_path = accept_path;
+    in.bonus = bonus;
+    in.argmax_out = argmax_out;
+    in.err = err;
+    return launch_step(in, workspace, as_stream(stream));
 }
 
 } // extern "C"

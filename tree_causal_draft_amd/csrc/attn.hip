@@ -360,28 +360,38 @@ __device__ __forceinline__ uint32_t lds_off(const void *p)
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
 
-// Four 16-byte LDS reads (ds_read_b128) at four row addresses plus one immediate
-// offset, then a wait for them -- the K fragments of QK^T.  Inline asm for the same
-// reason as the transposing reads below.
+// Four 16-byte LDS reads (ds_read_b128) at four row addresses plus one immediate offset
+// -- the K fragments of QK^T -- issued without a wait: they are in flight until an
+// lgkm_wait4 on them, so the reads of the next k-group overlap the current MFMAs.  Inline
+// asm for the same reason as the transposing reads below.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 template <int OFF>
-__device__ __forceinline__ void k_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                        uint4 &k0, uint4 &k1, uint4 &k2, uint4 &k3)
+__device__ __forceinline__ void k_issue4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                         u32x4_t &k0, u32x4_t &k1, u32x4_t &k2, u32x4_t &k3)
 {
     asm volatile("ds_read_b128 %0, %4 offset:%8\n\t"
                  "ds_read_b128 %1, %5 offset:%8\n\t"
                  "ds_read_b128 %2, %6 offset:%8\n\t"
-                 "ds_read_b128 %3, %7 offset:%8\n\t"
-                 "s_waitcnt lgkmcnt(0)"
+                 "ds_read_b128 %3, %7 offset:%8"
                  : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3)
                  : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF));
 }
+// Waits until at most N LDS operations are outstanding.  LDS reads complete in order, so
+// with N = the number of reads issued after these fragments they have arrived; naming
+// them as in/out operands keeps their uses after the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait4(u32x4_t &k0, u32x4_t &k1, u32x4_t &k2, u32x4_t &k3)
+{
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(k0), "+v"(k1), "+v"(k2), "+v"(k3) : "i"(N));
+}
 
 // Eight transposing LDS reads (ds_read_b64_tr_b16) from two row addresses at four row
-// offsets, then a wait for them.  Written as inline asm because the builtin's memory
-// operand carries no LDS alias information, which makes the compiler wait for every
-// pending HBM->LDS copy (including the next tile's) before the read.
+// offsets, issued without a wait (see k_issue4; lgkm_wait8 is the matching wait).  Inline
+// asm because the builtin's memory operand carries no LDS alias information, which makes
+// the compiler wait for every pending HBM->LDS copy (including the next tile's) before
+// the read.
 template <int O0, int O1, int O2, int O3>
-__device__ __forceinline__ void tr16_x8(uint32_t aa, uint32_t ab, i32x2_t (&r)[8])
+__device__ __forceinline__ void tr16_issue8(uint32_t aa, uint32_t ab, i32x2_t (&r)[8])
 {
     asm volatile("ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
                  "ds_read_b64_tr_b16 %1, %9 offset:%10\n\t"
@@ -390,11 +400,17 @@ __device__ __forceinline__ void tr16_x8(uint32_t aa, uint32_t ab, i32x2_t (&r)[8
                  "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
                  "ds_read_b64_tr_b16 %5, %9 offset:%12\n\t"
                  "ds_read_b64_tr_b16 %6, %8 offset:%13\n\t"
-                 "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
-                 "s_waitcnt lgkmcnt(0)"
+                 "ds_read_b64_tr_b16 %7, %9 offset:%13"
                  : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
                    "=&v"(r[6]), "=&v"(r[7])
                  : "v"(aa), "v"(ab), "i"(O0), "i"(O1), "i"(O2), "i"(O3));
+}
+template <int N> __device__ __forceinline__ void lgkm_wait8(i32x2_t (&r)[8])
+{
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                   "+v"(r[6]), "+v"(r[7])
+                 : "i"(N));
 }
 
 // Merge of one unit's split-KV partials for output items it .. (row, 8 columns), step
@@ -402,7 +418,7 @@ __device__ __forceinline__ void tr16_x8(uint32_t aa, uint32_t ab, i32x2_t (&r)[8
 // merged row is sum_c 2^(m_c - M) l_c (O_c/l_c) / sum_c 2^(m_c - M) l_c, M = max_c m_c.
 // NB chunks are loaded per round trip (the host picks NB >= the chunk count when it can).
 template <int D, int NB>
-__device__ void attn_merge_unit(const AttnArgs &a, const AttnPlan &pl, const AttnWs &w,
+__device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPlan &pl, const AttnWs &w,
                                 int unit, int it, int stride)
 {
     constexpr int SPR = D / 8;  // 8-column segments per row
@@ -490,11 +506,107 @@ __device__ __forceinline__ void barrier_keep_dma()
 }
 
 
-template <int D, int NWR>
-__global__ void __launch_bounds__(64 * NWR)
-attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
+// LDS accesses of the in-kernel ancestor rows, as inline asm for the same reason as the
+// tile reads: a compiler-visible LDS access would make it wait for the in-flight copies.
+__device__ __forceinline__ void lds_read_row(uint32_t addr, uint64_t (&r)[4])
 {
-    constexpr int NST = NWR == 8 ? 4 : 2;        // tile stages: 4 for the ping-pong, else 2
+    asm volatile("ds_read_b64 %0, %4\n\t"
+                 "ds_read_b64 %1, %4 offset:8\n\t"
+                 "ds_read_b64 %2, %4 offset:16\n\t"
+                 "ds_read_b64 %3, %4 offset:24\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                 : "v"(addr)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_write_row(uint32_t addr, const uint64_t (&r)[4])
+{
+    asm volatile("ds_write_b64 %0, %1\n\t"
+                 "ds_write_b64 %0, %2 offset:8\n\t"
+                 "ds_write_b64 %0, %3 offset:16\n\t"
+                 "ds_write_b64 %0, %4 offset:24"
+                 :
+                 : "v"(addr), "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3])
+                 : "memory");
+}
+__device__ __forceinline__ int lds_read_i32(uint32_t addr)
+{
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v)
+                 : "v"(addr)
+                 : "memory");
+    return v;
+}
+__device__ __forceinline__ void lds_write_i32(uint32_t addr, int v)
+{
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Ancestor rows of one sequence's tree in LDS (the mask step's rows, computed in place):
+// thread v holds node v (needs blockDim >= B) and `p` = parent[v].  Pointer doubling:
+// row v starts as {v} with jump parent[v]; every round ORs in the row of the jump target
+// and doubles the jump, so ceil(log2 B) rounds reach the root.  A parent outside
+// [0, v) is treated as the root's -1 here (that sequence is flagged by the mask
+// and verification steps; its attention output is unspecified).  Layout at byte
+// offset `base`: 256 rows of 32 bytes, then 256 jump pointers.
+__device__ __forceinline__ void tree_rows_lds(int p, int B, uint32_t base)
+{
+    const int v = threadIdx.x;
+    const bool mine = v < B;
+    int j = (mine && v > 0 && p >= 0 && p < v) ? p : -1;
+    uint64_t r[4] = {0ull, 0ull, 0ull, 0ull};
+    if (mine)
+        r[v >> 6] = 1ull << (v & 63);
+    const uint32_t row_at = base + (uint32_t)v * 32u, jmp_at = base + 256u * 32u + (uint32_t)v * 4u;
+    if (mine) {
+        lds_write_row(row_at, r);
+        lds_write_i32(jmp_at, j);
+    }
+    int rounds = 0;
+    while ((1 << rounds) < B)
+        ++rounds;
+    for (int k = 0; k < rounds; ++k) {
+        barrier_keep_dma();
+        uint64_t o[4] = {0ull, 0ull, 0ull, 0ull};
+        int nj = -1;
+        const bool act = mine && j >= 0;
+        if (act) {
+            lds_read_row(base + (uint32_t)j * 32u, o);
+            nj = lds_read_i32(base + 256u * 32u + (uint32_t)j * 4u);
+        }
+        barrier_keep_dma();
+        if (act) {
+            r[0] |= o[0];
+            r[1] |= o[1];
+            r[2] |= o[2];
+            r[3] |= o[3];
+            j = nj;
+            lds_write_row(row_at, r);
+            lds_write_i32(jmp_at, j);
+        }
+    }
+    barrier_keep_dma();
+}
+
+template <int D, int NWR> struct AttnLds {
+    static constexpr int NST = NWR == 8 ? 4 : 2;  // tile stages: 4 for the ping-pong, else 2
+    static constexpr int BUFB = 2 * 64 * D * 2;   // one stage: a K and a V tile of 64 keys
+    static constexpr int BT_OFF = NST * BUFB;
+    static constexpr int ANC_OFF = BT_OFF + kBtCap * 4;
+    static constexpr int BYTES = ANC_OFF + NWR * 32 * 5 * 8;
+};
+
+// The bf16 MFMA pass over one work item.  `blk` / `nblk`: this workgroup's index among
+// the workgroups running the pass and their number; `lds`: AttnLds<D, NWR>::BYTES of
+// LDS, 16-byte aligned.  kTreeRows: build the ancestor rows from the parent array here
+// (needs 64 * NWR >= B) instead of reading the mask step's rows.
+template <int D, int NWR, bool kTreeRows>
+__device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl, const AttnWs &ws,
+                                          int blk, int nblk, uint8_t *lds)
+{
+    constexpr int NST = AttnLds<D, NWR>::NST;
     constexpr int SEGS = D / 8;                  // 16-byte segments per K/V row
     constexpr int ROWB = D * 2;                  // bytes per K/V row
     constexpr int TILE = 64;                     // keys per tile
@@ -511,19 +623,21 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
     // The NST stage buffers.  Every LDS read of a tile is inline asm, so the compiler
     // sees no LDS load to order against the in-flight copies and adds no waits of its
     // own; a stage can therefore be chosen at run time (one loop body, small code).
-    __shared__ __attribute__((aligned(16))) uint8_t L0[NST * BUFB];
-    __shared__ int bt_lds[kBtCap];
-    __shared__ __attribute__((aligned(16))) uint64_t anc_lds[NWR][32][5];  // rows' ancestor bits (+pad)
+    static_assert(BUFB == AttnLds<D, NWR>::BUFB, "stage size");
+    uint8_t *const L0 = lds;
+    int *const bt_lds = reinterpret_cast<int *>(lds + AttnLds<D, NWR>::BT_OFF);
+    uint64_t(*const anc_lds)[32][5] =  // rows' ancestor bits (+pad)
+        reinterpret_cast<uint64_t(*)[32][5]>(lds + AttnLds<D, NWR>::ANC_OFF);
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wr = wid;  // the wave's 32-row block
     const int col = lane & 31, hh = lane >> 5;
 
     // ---- work item
-    int item = blockIdx.x;
+    int item = blk;
     if (pl.remap) {
-        const int per = gridDim.x >> 3;
-        item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+        const int per = nblk >> 3;
+        item = (blk & 7) * per + (blk >> 3);
     }
     const int rt = item % pl.n_rtiles;
     const int chunk = (item / pl.n_rtiles) % pl.n_chunks;
@@ -566,6 +680,40 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         }
     };
 
+    // ---- copy of a tile that lies inside a contiguous prefix: every lane's row sits at a
+    // fixed byte offset from the tile's first row, so the per-lane part is computed once
+    // and each copy adds it to a wave-uniform tile base (no per-tile 64-bit address math).
+    const uint32_t pre_rowb = (uint32_t)(Hkv * D * 2);  // bytes from one prefix key to the next
+    const bool fast_ok = !paged && (uint64_t)Hkv * D * 2 * TILE < (1ull << 31);
+    uint32_t lane_seg[NIW];
+    {
+        const int rrow = lane / SEGS, pslot = lane % SEGS;
+#pragma unroll
+        for (int ii = 0; ii < NIW; ++ii) {
+            const int row = (ii * NWR + wr) * RPI + rrow;
+            lane_seg[ii] = (uint32_t)rrow * pre_rowb + (uint32_t)((pslot ^ seg_swz<SEGS>(row)) * 16);
+        }
+    }
+    auto dma_prefix = [=](int kt, uint8_t *base) {
+        const uint64_t toff = (uint64_t)(((pre_s + kt) * Hkv + g) * D) * 2;
+#pragma unroll
+        for (int ii = 0; ii < NIW; ++ii) {
+            const int i = ii * NWR + wr;
+            const uint64_t ioff = toff + (uint64_t)(i * RPI) * pre_rowb;
+            lds_dma16(reinterpret_cast<const uint8_t *>(kpre_a + ioff) + lane_seg[ii], base + i * 1024);
+            lds_dma16(reinterpret_cast<const uint8_t *>(vpre_a + ioff) + lane_seg[ii],
+                      base + TILEB + i * 1024);
+        }
+    };
+
+    // node tid's parent, loaded before any tile copy so that waiting for it does not wait
+    // for the copies (memory operations complete in issue order)
+    int par_v = -1;
+    if constexpr (kTreeRows) {
+        if (tid < B)
+            par_v = a.parent[(int64_t)s * B + tid];
+    }
+
     // ---- speculative copies.  The prefix length is a device value: rather than wait
     // for it before the first copies, the first tiles of a contiguous prefix are fetched
     // as prefix keys right away (valid addresses for any key below max_prefix) and kept
@@ -578,11 +726,15 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         const int kt = kbeg + k * TILE;
         spec[k] = !paged && kt + TILE <= a.max_prefix;
         if (spec[k]) {
-            auto off_spec = [=](int key, bool &pre) -> int64_t {
-                pre = true;
-                return ((pre_s + key) * Hkv + g) * D;
-            };
-            dma_tile(kt, stage(k), off_spec);
+            if (fast_ok) {
+                dma_prefix(kt, stage(k));
+            } else {
+                auto off_spec = [=](int key, bool &pre) -> int64_t {
+                    pre = true;
+                    return ((pre_s + key) * Hkv + g) * D;
+                };
+                dma_tile(kt, stage(k), off_spec);
+            }
         }
     }
 
@@ -606,8 +758,21 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         }
     }
     // the wave's 32 ancestor rows, later parked in LDS (lane hh holds words 2hh, 2hh+1)
-    const uint64_t *anc_src = a.anc + ((int64_t)s * B + vrow) * 4 + 2 * hh;
-    const uint64_t anc_a = anc_src[0], anc_b = anc_src[1];
+    uint64_t anc_a, anc_b;
+    if constexpr (kTreeRows) {
+        // built in the stage that the speculative copies leave free; the loop's first
+        // copy into it is issued after the first barrier, when every wave has read it
+        const uint32_t tr_base = lds_off(stage(NPRO));
+        tree_rows_lds(par_v, B, tr_base);
+        uint64_t rw[4];
+        lds_read_row(tr_base + (uint32_t)vrow * 32u, rw);
+        anc_a = hh ? rw[2] : rw[0];
+        anc_b = hh ? rw[3] : rw[1];
+    } else {
+        const uint64_t *anc_src = a.anc + ((int64_t)s * B + vrow) * 4 + 2 * hh;
+        anc_a = anc_src[0];
+        anc_b = anc_src[1];
+    }
 
     if (a.err && rt == 0 && chunk == 0 && g == 0)
         attn_validate(a, s);
@@ -658,7 +823,13 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         }
         return off;
     };
-    auto issue_tile = [=](int kt, uint8_t *base) { dma_tile(kt, base, off_exact); };
+    const int fast_end = min(P, kend);  // tiles ending here or before are plain prefix tiles
+    auto issue_tile = [=](int kt, uint8_t *base) {
+        if (fast_ok && kt + TILE <= fast_end)
+            dma_prefix(kt, base);
+        else
+            dma_tile(kt, base, off_exact);
+    };
 
     // ---- settle the speculation: keep a copy only if every key is an in-range prefix
     // key; otherwise let it land and fetch the tile exactly.
@@ -730,24 +901,35 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         const uint32_t kbase =
             lds_off(kb) + opaque((uint32_t)(col * ROWB + (hh ^ (zs & 1)) * 16));
         const int zk = opaque(zs >> 1);
+        // k-groups of 4 MFMAs; the reads of group n+1 are in flight during group n's MFMAs
+        constexpr int NKG = 2 * (KS / 4);
+        u32x4_t kf[2][4];
+        auto kissue = [&](int n, u32x4_t (&dst)[4]) {
+            const int k4 = (n % (KS / 4)) * 4;
+            const uint32_t a0 = kbase + (uint32_t)(((k4 + 0) ^ zk) * 32);
+            const uint32_t a1 = kbase + (uint32_t)(((k4 + 1) ^ zk) * 32);
+            const uint32_t a2 = kbase + (uint32_t)(((k4 + 2) ^ zk) * 32);
+            const uint32_t a3 = kbase + (uint32_t)(((k4 + 3) ^ zk) * 32);
+            if (n < KS / 4)
+                k_issue4<0>(a0, a1, a2, a3, dst[0], dst[1], dst[2], dst[3]);
+            else
+                k_issue4<32 * ROWB>(a0, a1, a2, a3, dst[0], dst[1], dst[2], dst[3]);
+        };
+        kissue(0, kf[0]);
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk) {
-#pragma unroll
-            for (int k4 = 0; k4 < KS; k4 += 4) {
-                uint4 kf[4];
-                const uint32_t a0 = kbase + (uint32_t)(((k4 + 0) ^ zk) * 32);
-                const uint32_t a1 = kbase + (uint32_t)(((k4 + 1) ^ zk) * 32);
-                const uint32_t a2 = kbase + (uint32_t)(((k4 + 2) ^ zk) * 32);
-                const uint32_t a3 = kbase + (uint32_t)(((k4 + 3) ^ zk) * 32);
-                if (kbk == 0)
-                    k_read4<0>(a0, a1, a2, a3, kf[0], kf[1], kf[2], kf[3]);
-                else
-                    k_read4<32 * ROWB>(a0, a1, a2, a3, kf[0], kf[1], kf[2], kf[3]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, kf[q]), qf[k4 + q], sacc[kbk], 0, 0, 0);
+        for (int n = 0; n < NKG; ++n) {
+            u32x4_t (&cur)[4] = kf[n & 1];
+            if (n + 1 < NKG) {
+                kissue(n + 1, kf[(n + 1) & 1]);
+                lgkm_wait4<4>(cur[0], cur[1], cur[2], cur[3]);
+            } else {
+                lgkm_wait4<0>(cur[0], cur[1], cur[2], cur[3]);
             }
+            const int kbk = n / (KS / 4), k4 = (n % (KS / 4)) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8_t, cur[q]), qf[k4 + q], sacc[kbk], 0, 0, 0);
         }
         if (vis != ~0ull) {
 #pragma unroll
@@ -815,12 +997,23 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
         const uint32_t basea = vbase + opaque((uint32_t)(rowa * ROWB + (xs ^ (za & 3)) * 16 + half));
         const uint32_t baseb = vbase + opaque((uint32_t)(rowb * ROWB + (xs ^ (zb & 3)) * 16 + half));
         const int zda = opaque(za >> 2), zdb = opaque(zb >> 2);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        // the reads of output block db+1 are in flight during block db's MFMAs
+        i32x2_t vr[2][8];
+        auto vissue = [&](int db, i32x2_t (&dst)[8]) {
             const uint32_t aa = basea + (uint32_t)((db ^ zda) * 64);
             const uint32_t ab = baseb + (uint32_t)((db ^ zdb) * 64);
-            i32x2_t r[8];
-            tr16_x8<0, 16 * ROWB, 32 * ROWB, 48 * ROWB>(aa, ab, r);
+            tr16_issue8<0, 16 * ROWB, 32 * ROWB, 48 * ROWB>(aa, ab, dst);
+        };
+        vissue(0, vr[0]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            i32x2_t (&r)[8] = vr[db & 1];
+            if (db + 1 < DB) {
+                vissue(db + 1, vr[(db + 1) & 1]);
+                lgkm_wait8<8>(r);
+            } else {
+                lgkm_wait8<0>(r);
+            }
 #pragma unroll
             for (int f = 0; f < 4; ++f) {  // f = 2*kbk + m2
                 const bf16x8_t vf = __builtin_bit_cast(
@@ -901,20 +1094,25 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 
     // ---- epilogue: final output (one chunk), or a normalised bf16 partial plus (m, l)
     const float l = l_i + __shfl_xor(l_i, 32, kWave);
-    if (wave_has_rows && row_ok) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t *dst;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t slot0 = ((int64_t)unit * pl.n_chunks + chunk) * pl.rt + wr * 32;
+    if (wave_has_rows && row_ok && hh == 0) {
         if (pl.n_chunks == 1) {
-            dst = reinterpret_cast<uint16_t *>(a.out) + (int64_t)row_g * D;
-            if (a.lse && hh == 0)
+            if (a.lse)
                 a.lse[row_g] = l > 0.f ? (m_i + __log2f(l)) * kLn2 : -INFINITY;
         } else {
-            const int rl = wr * 32 + col;  // row within the unit's tile
-            const int64_t slot = ((int64_t)unit * pl.n_chunks + chunk) * pl.rt + rl;
-            dst = ws.o + slot * D;
-            if (hh == 0)
-                ws.ml[slot] = make_float2(m_i, l);
+            ws.ml[slot0 + col] = make_float2(m_i, l);
         }
+    }
+    // The accumulator spreads one row over the registers of 16 lanes.  A row-major copy of
+    // the wave's 32 rows in LDS (row pitch D*2 + 16 bytes, which staggers the banks) lets
+    // every lane store 16 contiguous bytes of a row instead of 8-byte pieces of 32 rows.
+    constexpr int OPITCH = D * 2 + 16;
+    static_assert(NWR * 32 * OPITCH <= NST * BUFB, "epilogue staging fits the tile stages");
+    wait_dma();       // no tile copy may still be landing in the stages
+    __syncthreads();  // every wave has finished reading the tiles
+    if (wave_has_rows) {
+        uint8_t *ob = L0 + wid * 32 * OPITCH;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -925,9 +1123,38 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
                        ((uint32_t)f32_to_bf16(o_acc[db][4 * q + 1] * inv) << 16);
                 pk.y = (uint32_t)f32_to_bf16(o_acc[db][4 * q + 2] * inv) |
                        ((uint32_t)f32_to_bf16(o_acc[db][4 * q + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(dst + d0) = pk;
+                *reinterpret_cast<uint2 *>(ob + col * OPITCH + d0 * 2) = pk;
             }
+        // the rows written by other lanes of this wave are read back below
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int RPS = 64 / SEGS;  // rows per store instruction
+#pragma unroll
+        for (int it = 0; it < 32 / RPS; ++it) {
+            const int row = it * RPS + lane / SEGS, sgm = lane % SEGS;
+            const int rr2 = wrow0 + row;
+            const uint4 val = *reinterpret_cast<const uint4 *>(ob + row * OPITCH + sgm * 16);
+            if (rr2 < R) {
+                uint16_t *dst;
+                if (pl.n_chunks == 1) {
+                    const int v2 = rr2 / G, h2 = g * G + rr2 % G;
+                    dst = reinterpret_cast<uint16_t *>(a.out) + (((int64_t)s * B + v2) * a.Hq + h2) * D;
+                } else {
+                    dst = ws.o + (slot0 + row) * D;
+                }
+                *reinterpret_cast<uint4 *>(dst + sgm * 8) = val;
+            }
+        }
     }
+}
+
+template <int D, int NWR>
+__global__ void __launch_bounds__(64 * NWR)
+attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[AttnLds<D, NWR>::BYTES];
+    attn_main<D, NWR, false>(a, pl, ws, blockIdx.x, gridDim.x, lds);
 }
 
 // Separate merge pass for large units: one thread per (unit, row, 8 output columns).

@@ -118,6 +118,7 @@ struct AttnArgs {
     const int32_t *prefix_len;
     int max_prefix;
     const uint64_t *anc;
+    const int32_t *parent;  // used instead of anc by the fused step (rows built in place)
     int S, B, Hq, Hkv, d, G;
     int dtype;
     float scale;
@@ -128,5 +129,22 @@ struct AttnArgs {
 size_t attention_workspace(int S, int B, int Hq, int Hkv, int d, int max_prefix, int block_size,
                            int dtype);
 jt_status launch_attention(const AttnArgs &a, void *ws, hipStream_t st);
+
+// the fused step: attention arguments (anc and err unused) plus those of the other steps
+struct StepLaunch {
+    AttnArgs attn;
+    const void *draft, *target;
+    int64_t draft_stride, target_stride;
+    int V, W, N;
+    int32_t *ids;
+    float *logprob, *row_lse;
+    const int32_t *parent, *tokens;
+    uint64_t *anc;
+    int32_t *depth;
+    int32_t *accept_len, *accept_path, *bonus, *argmax_out, *err;
+};
+size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d, int max_prefix,
+                      int block_size);
+jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st);
 
 } // namespace jt

@@ -14,16 +14,12 @@
 
 namespace jt {
 
-__global__ void __launch_bounds__(256) build_mask_kernel(const int32_t *__restrict__ parent, int B,
-                                                         uint64_t *__restrict__ anc,
-                                                         int32_t *__restrict__ depth,
-                                                         int32_t *__restrict__ err)
+// Rows and depths of sequence s by one workgroup of at least B threads (thread v = node v);
+// `row`, `jmp`, `dist` are JT_MAX_NODES entries of LDS.
+__device__ __forceinline__ void mask_block(const int32_t *__restrict__ parent, int B, uint64_t *__restrict__ anc,
+                           int32_t *__restrict__ depth, int32_t *__restrict__ err, int s,
+                           uint64_t (*row)[4], int32_t *jmp, int32_t *dist)
 {
-    __shared__ uint64_t row[JT_MAX_NODES][4];
-    __shared__ int32_t jmp[JT_MAX_NODES];
-    __shared__ int32_t dist[JT_MAX_NODES];
-
-    const int s = blockIdx.x;
     const int v = threadIdx.x;
     const int32_t *par = parent + (int64_t)s * B;
 
@@ -89,6 +85,17 @@ __global__ void __launch_bounds__(256) build_mask_kernel(const int32_t *__restri
     }
     if (v == 0 && err)
         err[s] = 0;
+}
+
+__global__ void __launch_bounds__(256) build_mask_kernel(const int32_t *__restrict__ parent, int B,
+                                                         uint64_t *__restrict__ anc,
+                                                         int32_t *__restrict__ depth,
+                                                         int32_t *__restrict__ err)
+{
+    __shared__ uint64_t row[JT_MAX_NODES][4];
+    __shared__ int32_t jmp[JT_MAX_NODES];
+    __shared__ int32_t dist[JT_MAX_NODES];
+    mask_block(parent, B, anc, depth, err, blockIdx.x, row, jmp, dist);
 }
 
 jt_status launch_build_mask(const int32_t *parent, int S, int B, uint64_t *anc, int32_t *depth,

@@ -1,0 +1,277 @@
+// The whole draft-and-verify step in two launches (jt_draft_verify_step).
+//
+// Each launch runs several steps side by side, one role per range of workgroup ids:
+//   phase 1  attention   the split-KV MFMA pass; its workgroups build the tree's ancestor
+//                        rows in LDS from the parent array while their first tile copies
+//                        are in flight, so they do not wait for the mask step
+//            top-W       the per-wave partial lists of the draft logit rows
+//            arg-max     the partial arg-max of the target logit rows
+//            mask        ancestor rows and depths to global memory
+//   phase 2  combine     the split-KV merge
+//            top-W       the per-row merge of the partial lists
+//            verify      the per-sequence walk (reads phase 1's rows, depths, arg-max keys)
+// The roles run the device code of the separate entry points, so every output equals
+// what the four calls produce one after the other.  The verification walk is the only
+// writer of err[s]: it ORs the mask and attention flags (kept in the workspace) into its
+// own.  Splitting the step into two dependent launches, rather than seven, removes five
+// kernel boundaries from its critical path and lets the bandwidth-bound logit scans run
+// beside the attention without relying on the stream scheduler.
+#include "jt_internal.h"
+
+namespace jt {
+
+struct StepArgs {
+    AttnArgs attn;
+    AttnWs aws;
+    const void *draft;
+    int64_t draft_stride;
+    const void *target;
+    int64_t target_stride;
+    int V, W, S, B, N;
+    int32_t *ids;
+    float *logprob, *row_lse;
+    uint64_t *tkeys;
+    float2 *tms;
+    uint64_t *gkeys;
+    uint32_t *gnan;
+    const int32_t *parent, *tokens;
+    uint64_t *anc;
+    int32_t *depth;
+    int32_t *accept_len, *accept_path, *bonus, *argmax_out, *err;
+    int32_t *err_mask, *err_attn;  // per-sequence flags of the mask and attention roles
+};
+
+struct StepPlan {
+    AttnPlan ap;     // nwr >= 4: the phase-1 workgroup is 64 * ap.nwr threads
+    TopwPlan tp;
+    ArgPlan gp;
+    int nA, nT, nG, nM;  // phase-1 workgroups per role
+    int nC, nR, nW;      // phase-2 workgroups per role
+};
+
+constexpr int kStepRowsPerBlock = 4;  // phase 2: top-W rows merged per workgroup (one per wave)
+
+template <int D, int NWR> struct StepLds {
+    static constexpr int MASK = JT_MAX_NODES * (32 + 4 + 4);
+    static constexpr int ARG = 2 * NWR * 8;
+    static constexpr int A = AttnLds<D, NWR>::BYTES;
+    static constexpr int BYTES = A > MASK ? A : MASK;
+    static_assert(ARG <= BYTES, "arg-max slice");
+};
+
+template <int D, int NWR>
+__device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepPlan &sp)
+{
+    constexpr int NT = 64 * NWR;
+    __shared__ __attribute__((aligned(16))) uint8_t pool[StepLds<D, NWR>::BYTES];
+    int b = blockIdx.x;
+    if (b < sp.nA) {
+        attn_main<D, NWR, true>(sa.attn, sp.ap, sa.aws, b, sp.nA, pool);
+        return;
+    }
+    b -= sp.nA;
+    if (b < sp.nT) {
+        topw_partial_wave<uint16_t, true>(
+            static_cast<const uint16_t *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
+            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, b * NWR + (threadIdx.x >> 6));
+        return;
+    }
+    b -= sp.nT;
+    if (b < sp.nG) {
+        argmax_partial_block<uint16_t, true, NT>(
+            static_cast<const uint16_t *>(sa.target), sa.target_stride, sa.V, sp.gp.nsub,
+            sp.gp.sub_per_wg, sp.gp.nchunk, sa.gkeys, sa.gnan, b,
+            reinterpret_cast<uint64_t *>(pool), reinterpret_cast<uint32_t *>(pool + NWR * 8));
+        return;
+    }
+    b -= sp.nG;
+    mask_block(sa.parent, sa.B, sa.anc, sa.depth, sa.err_mask, b,
+               reinterpret_cast<uint64_t(*)[4]>(pool),
+               reinterpret_cast<int32_t *>(pool + JT_MAX_NODES * 32),
+               reinterpret_cast<int32_t *>(pool + JT_MAX_NODES * 36));
+}
+
+// 4 waves: two workgroups per CU (register budget 256 per lane, LDS 2 x 74 KB)
+template <int D>
+__global__ void __launch_bounds__(256, 2) step_phase1_w4(StepArgs sa, StepPlan sp)
+{
+    step_phase1_body<D, 4>(sa, sp);
+}
+template <int D>
+__global__ void __launch_bounds__(512) step_phase1_w8(StepArgs sa, StepPlan sp)
+{
+    step_phase1_body<D, 8>(sa, sp);
+}
+
+template <int D, int NB>
+__global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
+{
+    __shared__ uint64_t mkeys[kStepRowsPerBlock][kMaxLists * JT_MAX_W];
+    __shared__ uint64_t mtop[kStepRowsPerBlock][JT_MAX_W];
+    int b = blockIdx.x;
+    if (b < sp.nC) {
+        const int64_t t = (int64_t)b * 256 + threadIdx.x;
+        const int64_t per_unit = (int64_t)sp.ap.rt * (D / 8);
+        const int unit = (int)(t / per_unit);
+        if (unit < sp.ap.units)
+            attn_merge_unit<D, NB>(sa.attn, sp.ap, sa.aws, unit, (int)(t % per_unit), (int)per_unit);
+        return;
+    }
+    b -= sp.nC;
+    if (b < sp.nR) {
+        const int wid = threadIdx.x >> 6;
+        const int r = b * kStepRowsPerBlock + wid;
+        if (r < sa.S * sa.N)
+            topw_merge_row(r, sa.W, sp.tp.nlist, sa.tkeys, sa.tms, sa.ids, sa.logprob, sa.row_lse,
+                           mkeys[wid], mtop[wid]);
+        return;
+    }
+    b -= sp.nR;
+    verify_walk_block(b, sa.B, sa.N, sp.gp.nchunk, sa.gkeys, sa.gnan, sa.parent, sa.tokens, sa.anc,
+                      sa.depth, sa.accept_len, sa.accept_path, sa.bonus, sa.argmax_out, sa.err,
+                      sa.err_mask, sa.err_attn);
+}
+
+// ------------------------------------------------------------------ host side --
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Work decomposition of the fused step.  For few rows the phase-1 grid should fit the
+// chip in one round (two 4-wave workgroups per CU), so the logit scans take two pieces
+// (top-W) per wave and up to four 8192-logit sub-chunks (arg-max) per workgroup.
+static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, int max_prefix,
+                          int block_size)
+{
+    StepPlan sp;
+    sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size);
+    if (sp.ap.nwr < 4) {
+        sp.ap.nwr = 4;  // same rows, chunks and results; the other two waves idle
+        sp.ap.rt = 128;
+    }
+    const int nwr = sp.ap.nwr;
+    const int rows_d = S * N, rows_t = S * B;
+    sp.tp.npiece = (V + kPiece - 1) / kPiece;
+    sp.tp.ppw = (sp.tp.npiece + kMaxLists - 1) / kMaxLists;
+    if (sp.tp.ppw < 2 && rows_d * sp.tp.npiece > 4 * 256)
+        sp.tp.ppw = 2;
+    sp.tp.nlist = (sp.tp.npiece + sp.tp.ppw - 1) / sp.tp.ppw;
+    sp.gp.nsub = (V + kArgSub - 1) / kArgSub;
+    int want = rows_t > 0 ? (256 + rows_t - 1) / rows_t : 1;  // chunks per row
+    want = max(want, (sp.gp.nsub + 3) / 4);                     // at most ~4 sub-chunks each
+    int spw = (sp.gp.nsub + want - 1) / want;
+    if (spw < 1)
+        spw = 1;
+    while ((sp.gp.nsub + spw - 1) / spw > kArgMaxChunks)
+        ++spw;
+    sp.gp.sub_per_wg = spw;
+    sp.gp.nchunk = (sp.gp.nsub + spw - 1) / spw;
+    sp.nA = sp.ap.units * sp.ap.n_chunks;
+    sp.nT = (rows_d * sp.tp.nlist + nwr - 1) / nwr;
+    sp.nG = rows_t * sp.gp.nchunk;
+    sp.nM = S;
+    sp.nC = sp.ap.n_chunks > 1
+                ? (int)(((long)sp.ap.units * sp.ap.rt * (d / 8) + 255) / 256)
+                : 0;
+    sp.nR = (rows_d + kStepRowsPerBlock - 1) / kStepRowsPerBlock;
+    sp.nW = S;
+    return sp;
+}
+
+struct StepWs {
+    size_t attn, tkeys, tms, gkeys, gnan, flags, total;
+};
+
+static StepWs step_ws_layout(const StepPlan &sp, int S, int N, int B, int W, int d)
+{
+    StepWs L;
+    size_t off = 0;
+    L.attn = off;
+    off += align256(attn_ws_bytes(sp.ap, d));
+    const size_t tparts = (size_t)S * N * sp.tp.nlist;
+    L.tkeys = off;
+    off += align256(tparts * W * sizeof(uint64_t));
+    L.tms = off;
+    off += align256(tparts * sizeof(float2));
+    const size_t gparts = (size_t)S * B * sp.gp.nchunk;
+    L.gkeys = off;
+    off += align256(gparts * sizeof(uint64_t));
+    L.gnan = off;
+    off += align256(gparts * sizeof(uint32_t));
+    L.flags = off;
+    off += align256((size_t)2 * S * sizeof(int32_t));
+    L.total = off;
+    return L;
+}
+
+size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d, int max_prefix,
+                      int block_size)
+{
+    const StepPlan sp = step_plan(S, B, N, V, Hq, Hkv, d, max_prefix, block_size);
+    return step_ws_layout(sp, S, N, B, W, d).total;
+}
+
+template <int D>
+static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st)
+{
+    const unsigned g1 = (unsigned)(sp.nA + sp.nT + sp.nG + sp.nM);
+    if (sp.ap.nwr == 8)
+        hipLaunchKernelGGL((step_phase1_w8<D>), dim3(g1), dim3(512), 0, st, sa, sp);
+    else
+        hipLaunchKernelGGL((step_phase1_w4<D>), dim3(g1), dim3(256), 0, st, sa, sp);
+    const unsigned g2 = (unsigned)(sp.nC + sp.nR + sp.nW);
+    if (sp.ap.n_chunks > 8 && sp.ap.n_chunks <= 16)
+        hipLaunchKernelGGL((step_phase2<D, 16>), dim3(g2), dim3(256), 0, st, sa, sp);
+    else
+        hipLaunchKernelGGL((step_phase2<D, 8>), dim3(g2), dim3(256), 0, st, sa, sp);
+}
+
+jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st)
+{
+    if (in.attn.S == 0)
+        return JT_OK;
+    const AttnArgs &aa = in.attn;
+    const StepPlan sp = step_plan(aa.S, aa.B, in.N, in.V, aa.Hq, aa.Hkv, aa.d, aa.max_prefix,
+                                  aa.block_table ? aa.block_size : 0);
+    const StepWs L = step_ws_layout(sp, aa.S, in.N, aa.B, in.W, aa.d);
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    StepArgs sa;
+    sa.attn = aa;
+    sa.attn.anc = nullptr;
+    sa.attn.parent = in.parent;
+    sa.err_mask = reinterpret_cast<int32_t *>(w + L.flags);
+    sa.err_attn = sa.err_mask + aa.S;
+    sa.attn.err = sa.err_attn;
+    sa.aws = attn_ws_split(sp.ap, w + L.attn);
+    sa.draft = in.draft;
+    sa.draft_stride = in.draft_stride;
+    sa.target = in.target;
+    sa.target_stride = in.target_stride;
+    sa.V = in.V;
+    sa.W = in.W;
+    sa.S = aa.S;
+    sa.B = aa.B;
+    sa.N = in.N;
+    sa.ids = in.ids;
+    sa.logprob = in.logprob;
+    sa.row_lse = in.row_lse;
+    sa.tkeys = reinterpret_cast<uint64_t *>(w + L.tkeys);
+    sa.tms = reinterpret_cast<float2 *>(w + L.tms);
+    sa.gkeys = reinterpret_cast<uint64_t *>(w + L.gkeys);
+    sa.gnan = reinterpret_cast<uint32_t *>(w + L.gnan);
+    sa.parent = in.parent;
+    sa.tokens = in.tokens;
+    sa.anc = in.anc;
+    sa.depth = in.depth;
+    sa.accept_len = in.accept_len;
+    sa.accept_path = in.accept_path;
+    sa.bonus = in.bonus;
+    sa.argmax_out = in.argmax_out;
+    sa.err = in.err;
+    if (aa.d == 128)
+        launch_step_d<128>(sa, sp, st);
+    else
+        launch_step_d<64>(sa, sp, st);
+    return launch_status(hipGetLastError());
+}
+
+} // namespace jt

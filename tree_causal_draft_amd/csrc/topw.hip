@@ -8,14 +8,14 @@
 //   * a row is cut into pieces of 2048 logits; each wave of a workgroup owns one piece
 //     (or a run of them for very long rows) and works alone, with no workgroup barrier,
 //     so the many small pieces spread the row over the whole chip;
-//   * a piece is pulled into registers with 16-byte loads (32 logits per lane) and
-//     reduced there: lane max, then sum of exp(x - max) (exact per-lane rescale);
-//   * a threshold tau (the W-th largest lane maximum, found by a 32-step ballot
-//     bisection on order codes) bounds the piece's W-th largest logit from below, so
-//     only logits >= tau become candidates;
-//   * candidates land in the wave's LDS slice as 64-bit keys (order code << 32 | ~id):
-//     value descending, id ascending in one integer compare, so bf16 ties resolve
-//     exactly like a full sort; W rounds of a DPP wave max extract the W largest;
+//   * a piece is pulled into registers with 16-byte loads (32 logits per lane; the next
+//     piece's loads are issued before the current one is processed) and reduced there:
+//     lane max, then sum of exp(x - max) (exact per-lane rescale);
+//   * elements become 64-bit keys (order code << 32 | ~id): value descending, id
+//     ascending in one integer compare, so bf16 ties resolve exactly like a full sort;
+//     each lane keeps its two largest keys (a pairwise tree, no LDS), and W rounds of a
+//     DPP wave max over the lanes' offers extract the W largest, merged on the fly with
+//     the wave's running list from its earlier pieces;
 //   * a merge kernel (one wave per row) combines the per-wave top-W lists and the
 //     (max, sum-exp) pairs into ids, log-probs and the row log-sum-exp.
 #include "jt_internal.h"
@@ -24,7 +24,6 @@ namespace jt {
 
 constexpr int kTopwThreads = 256;   // 4 independent waves per workgroup
 constexpr int kPiece = 2048;        // logits per wave piece (32 per lane)
-constexpr int kWaveCap = 512;       // candidate slots per wave in LDS
 constexpr int kMaxLists = 128;      // partial lists per row seen by the merge kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -32,11 +31,46 @@ template <typename T> struct Vec;
 template <> struct Vec<uint16_t> { static constexpr int kElems = 8; static constexpr int kLoads = 4; };
 template <> struct Vec<float> { static constexpr int kElems = 4; static constexpr int kLoads = 8; };
 
-// Loads a lane's 32 logits of one piece.  Element k of load i sits at index
-// base + (lane + 64*i)*E + k.  Out-of-row entries become -inf with valid = false.
+// The raw words of a lane's 32 logits of one piece: element k of load i sits at index
+// base + (lane + 64*i)*E + k.  Entries at or past V are never read (their bits stay 0);
+// unpack_piece marks them invalid.  Split from the unpacking so that the loads of the next
+// piece can be in flight while the current one is processed.
+template <typename T> struct RawPiece {
+    uint4 u[Vec<T>::kLoads];
+};
+
 template <typename T, bool kAligned>
-__device__ __forceinline__ void load_piece(const T *__restrict__ row, int64_t base, int V, int lane,
-                                           float (&x)[32], uint32_t &valid)
+__device__ __forceinline__ void load_piece_raw(const T *__restrict__ row, int64_t base, int V,
+                                               int lane, RawPiece<T> &r)
+{
+    constexpr int E = Vec<T>::kElems;
+    constexpr int L = Vec<T>::kLoads;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
+        if (kAligned && e0 + E <= V) {
+            r.u[i] = *reinterpret_cast<const uint4 *>(row + e0);
+        } else {
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const int64_t e = e0 + k;
+                if (e < V) {
+                    if constexpr (sizeof(T) == 2)
+                        w[k >> 1] |= (uint32_t)row[e] << (16 * (k & 1));
+                    else
+                        w[k] = __float_as_uint(row[e]);
+                }
+            }
+            r.u[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// Logit values of a raw piece; entries at or past V become -inf with valid = false.
+template <typename T>
+__device__ __forceinline__ void unpack_piece(const RawPiece<T> &r, int64_t base, int V, int lane,
+                                             float (&x)[32], uint32_t &valid)
 {
     constexpr int E = Vec<T>::kElems;
     constexpr int L = Vec<T>::kLoads;
@@ -44,31 +78,25 @@ __device__ __forceinline__ void load_piece(const T *__restrict__ row, int64_t ba
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
-        if (kAligned && e0 + E <= V) {
-            const uint4 u = *reinterpret_cast<const uint4 *>(row + e0);
-            if constexpr (sizeof(T) == 2) {
-                x[i * 8 + 0] = bf16_lo(u.x); x[i * 8 + 1] = bf16_hi(u.x);
-                x[i * 8 + 2] = bf16_lo(u.y); x[i * 8 + 3] = bf16_hi(u.y);
-                x[i * 8 + 4] = bf16_lo(u.z); x[i * 8 + 5] = bf16_hi(u.z);
-                x[i * 8 + 6] = bf16_lo(u.w); x[i * 8 + 7] = bf16_hi(u.w);
-            } else {
-                x[i * 4 + 0] = __uint_as_float(u.x); x[i * 4 + 1] = __uint_as_float(u.y);
-                x[i * 4 + 2] = __uint_as_float(u.z); x[i * 4 + 3] = __uint_as_float(u.w);
-            }
+        const uint4 u = r.u[i];
+        if constexpr (sizeof(T) == 2) {
+            x[i * 8 + 0] = bf16_lo(u.x); x[i * 8 + 1] = bf16_hi(u.x);
+            x[i * 8 + 2] = bf16_lo(u.y); x[i * 8 + 3] = bf16_hi(u.y);
+            x[i * 8 + 4] = bf16_lo(u.z); x[i * 8 + 5] = bf16_hi(u.z);
+            x[i * 8 + 6] = bf16_lo(u.w); x[i * 8 + 7] = bf16_hi(u.w);
+        } else {
+            x[i * 4 + 0] = __uint_as_float(u.x); x[i * 4 + 1] = __uint_as_float(u.y);
+            x[i * 4 + 2] = __uint_as_float(u.z); x[i * 4 + 3] = __uint_as_float(u.w);
+        }
+        if (e0 + E <= V) {
             valid |= ((1u << E) - 1u) << (i * E);
         } else {
 #pragma unroll
             for (int k = 0; k < E; ++k) {
-                const int64_t e = e0 + k;
-                if (e < V) {
-                    if constexpr (sizeof(T) == 2)
-                        x[i * E + k] = bf16_to_f32(row[e]);
-                    else
-                        x[i * E + k] = row[e];
+                if (e0 + k < V)
                     valid |= 1u << (i * E + k);
-                } else {
+                else
                     x[i * E + k] = -INFINITY;
-                }
             }
         }
     }
@@ -79,19 +107,6 @@ __device__ __forceinline__ uint32_t elem_id(int64_t base, int lane, int j)
 {
     constexpr int E = Vec<T>::kElems;
     return (uint32_t)(base + (int64_t)(lane + kWave * (j / E)) * E + (j % E));
-}
-
-// Largest code t such that at least W lanes of the wave hold a code >= t.
-__device__ __forceinline__ uint32_t wave_wth_code(uint32_t code, int W)
-{
-    uint32_t prefix = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = prefix | (1u << bit);
-        const int cnt = __popcll(__ballot(code >= cand));
-        if (cnt >= W)
-            prefix = cand;
-    }
-    return prefix;
 }
 
 // Orders the LDS accesses of one wave: writes by some lanes before reads by others.
@@ -124,38 +139,71 @@ __device__ void wave_select_topw(const uint64_t *keys, int n, int W, uint64_t *o
     wave_sync();
 }
 
-// Each wave owns `ppw` consecutive pieces of 2048 logits of one row and works alone (no
-// workgroup barrier): lane max and sum of exp(x - max); a threshold tau = the W-th
-// largest lane maximum of the piece, a lower bound on the piece's W-th largest logit;
-// the logits >= tau (and above the running W-th best) compacted into the wave's LDS
-// slice by ballot + mbcnt; W rounds of a wave max over those and the running top-W.
-// Output per wave: its W best keys and its (max, sum-exp) pair.
-template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kTopwThreads)
-topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, int V, int W,
-                    int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
-                    float2 *__restrict__ ws_ms)
+// Top two keys of a lane's elements below `lim` (keys are unique; 0 = none): a pairwise
+// tree over the 32 slots, so the comparisons of one level are independent of each other.
+template <typename KeyOf>
+__device__ __forceinline__ void lane_top2(KeyOf key_of, uint64_t lim, uint64_t &k1, uint64_t &k2)
 {
-    __shared__ uint64_t cand_all[4][kWaveCap + JT_MAX_W];
-    __shared__ uint64_t best_all[4][JT_MAX_W];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int gl = blockIdx.x * 4 + wid;  // list index = (row, list within the row)
+    uint64_t a[16], b[16];  // per pair: larger, smaller
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        uint64_t u = key_of(2 * p), v = key_of(2 * p + 1);
+        u = u < lim ? u : 0ull;
+        v = v < lim ? v : 0ull;
+        const bool gt = u > v;
+        a[p] = gt ? u : v;
+        b[p] = gt ? v : u;
+    }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int p = 0; p < w; ++p) {
+            const uint64_t a1 = a[p], a2 = b[p], b1 = a[p + w], b2 = b[p + w];
+            const bool gt = a1 > b1;
+            const uint64_t s1 = gt ? b1 : a1, s2 = gt ? a2 : b2;  // candidates for second
+            a[p] = gt ? a1 : b1;
+            b[p] = s1 > s2 ? s1 : s2;
+        }
+    }
+    k1 = a[0];
+    k2 = b[0];
+}
+
+// Each wave owns `ppw` consecutive pieces of 2048 logits of one row and works alone (no
+// LDS, no workgroup barrier).  Per piece: the lane's (max, sum of exp(x - max)), merged
+// into a running pair; the lane's two largest 64-bit keys (order code << 32 | ~id: value
+// descending, id ascending in one integer compare, so bf16 ties resolve like a full
+// sort); then W rounds of a DPP wave max over the lanes' offers -- a lane offers the
+// larger of its best unused key and its entry of the wave's running top-W list (lane r
+// holds entry r) -- which rebuild that list.  A lane whose two keys are used up and that
+// still holds elements recomputes its top two below the last key it gave (rare).
+// Output per wave: its W best keys, descending, 0-padded, and its (max, sum) pair.
+template <typename T, bool kAligned>
+__device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, int64_t row_stride,
+                                                  int rows, int V, int W, int npiece, int ppw,
+                                                  int nlist, uint64_t *__restrict__ ws_keys,
+                                                  float2 *__restrict__ ws_ms, int gl)
+{
+    constexpr int E = Vec<T>::kElems;
+    const int lane = threadIdx.x & 63;
     if (gl >= rows * nlist)
         return;
     const int row_idx = gl / nlist, li = gl % nlist;
     const T *row = logits + (int64_t)row_idx * row_stride;
-    uint64_t *cand = cand_all[wid];
-    uint64_t *best = best_all[wid];
-    if (lane < JT_MAX_W)
-        best[lane] = 0ull;
-    wave_sync();
     float run_m = -INFINITY, run_s = 0.f;  // lane's running (max, sum exp(x - max))
+    uint64_t run = 0ull;                   // lane r < W: entry r of the running top-W list
     const int p0 = li * ppw, p1 = min(npiece, p0 + ppw);
+    RawPiece<T> next;
+    if (p0 < p1)
+        load_piece_raw<T, kAligned>(row, (int64_t)p0 * kPiece, V, lane, next);
     for (int pc = p0; pc < p1; ++pc) {
         const int64_t base = (int64_t)pc * kPiece;
+        const RawPiece<T> cur = next;
+        if (pc + 1 < p1)  // the next piece's loads overlap this piece's work
+            load_piece_raw<T, kAligned>(row, base + kPiece, V, lane, next);
         float x[32];
         uint32_t valid;
-        load_piece<T, kAligned>(row, base, V, lane, x, valid);
+        unpack_piece<T>(cur, base, V, lane, x, valid);
         float m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 32; ++j)
@@ -163,9 +211,11 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
         float sx = 0.f;
         if (m != -INFINITY) {
             const float mb = m * kLog2e;
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 32; ++j)
-                sx += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+                part[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+            sx = (part[0] + part[1]) + (part[2] + part[3]);
         } else {
             // every entry is -inf, padding or NaN: only a NaN must still poison the sum
 #pragma unroll
@@ -185,62 +235,44 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
             run_s += sx * __builtin_amdgcn_exp2f((m - run_m) * kLog2e);
         }
 
-        // ---- threshold: a lane's code counts only if it holds a real (non-NaN) element
-        // equal to its maximum
-        bool real = m != -INFINITY;
-        if (!real) {
-#pragma unroll
-            for (int j = 0; j < 32; ++j)
-                real |= ((valid >> j) & 1u) && x[j] == -INFINITY;
-        }
-        uint32_t tau = wave_wth_code(real ? order_code(m) : 0u, W);
-        const uint64_t wth = best[W - 1];
-        if (wth != 0ull)
-            tau = max(tau, (uint32_t)(wth >> 32));
-        // tau == 0: fewer than W lane maxima, every valid element is a candidate
-        int n = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const uint32_t c = order_code(x[j]);
-            const bool pred = ((valid >> j) & 1u) && c >= tau;
-            const uint64_t b = __ballot(pred);
-            if (b) {
-                const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-                if (pred && slot < kWaveCap)
-                    cand[slot] = ((uint64_t)c << 32) | (uint64_t)(~elem_id<T>(base, lane, j));
-                n += __popcll(b);
-            }
-        }
-        wave_sync();
-        if (n <= kWaveCap) {
-            if (lane < W)
-                cand[n + lane] = best[lane];
-            wave_sync();
-            wave_select_topw(cand, n + W, W, best);
-        } else {
-            // rare overflow (huge ties): W rounds of exact arg-max over the registers
-            uint64_t prev = ~0ull;
-            for (int r = 0; r < W; ++r) {
-                uint64_t mine = 0ull;
-#pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    if (!((valid >> j) & 1u))
-                        continue;
-                    const uint64_t k = rank_key(x[j], elem_id<T>(base, lane, j));
-                    if (k < prev && k > mine)
-                        mine = k;
+        // ---- this piece's keys against the running list
+        const uint32_t idl = (uint32_t)(base + (int64_t)lane * E);
+        auto key_of = [&](int j) -> uint64_t {
+            if (!((valid >> j) & 1u))
+                return 0ull;
+            const uint32_t id = idl + (uint32_t)(kWave * E * (j / E) + j % E);
+            return ((uint64_t)order_code(x[j]) << 32) | (uint64_t)(~id);
+        };
+        uint64_t k1, k2;
+        lane_top2(key_of, ~0ull, k1, k2);
+        const int nval = __popc(valid);
+        int used = 0;             // keys of this piece this lane has given
+        uint64_t last = ~0ull;    // the last of them
+        uint64_t rk = lane < W ? run : 0ull;
+        uint64_t nrun = 0ull;
+        for (int r = 0; r < W; ++r) {
+            const uint64_t offer = k1 > rk ? k1 : rk;
+            const uint64_t K = wave_max_u64_dpp(offer);
+            if (K == 0ull)
+                break;  // fewer than W keys in all: the rest of the list stays empty
+            if (lane == r)
+                nrun = K;
+            if (offer == K) {  // this lane supplied K (keys are unique)
+                if (rk == K) {
+                    rk = 0ull;
+                } else {
+                    k1 = k2;
+                    k2 = 0ull;
+                    last = K;
+                    ++used;
                 }
-                mine = wave_max_u64_dpp(mine);
-                if (lane == 0)
-                    cand[r] = mine;
-                prev = mine;
             }
-            if (lane < W)
-                cand[W + lane] = best[lane];
-            wave_sync();
-            wave_select_topw(cand, 2 * W, W, best);
+            // known keys used up while elements remain: the next two below the last one
+            const bool refill = k1 == 0ull && used < nval;
+            if (__ballot(refill) && refill)
+                lane_top2(key_of, last, k1, k2);
         }
+        run = nrun;
     }
 
     // ---- (max, sum) over the wave
@@ -253,19 +285,28 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
     if (lane == 0)
         ws_ms[gl] = make_float2(m, sw);
     if (lane < W)
-        ws_keys[(int64_t)gl * W + lane] = best[lane];
+        ws_keys[(int64_t)gl * W + lane] = run;
 }
 
-// One wave per row: merge the partial lists and (max, sum) pairs.
-__global__ void __launch_bounds__(64)
-topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
-                  const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
-                  float *__restrict__ logprob, float *__restrict__ row_lse)
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kTopwThreads)
+topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, int V, int W,
+                    int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
+                    float2 *__restrict__ ws_ms)
 {
-    __shared__ uint64_t keys[kMaxLists * JT_MAX_W];
-    __shared__ uint64_t top[JT_MAX_W];
-    const int r = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int wid = threadIdx.x >> 6;
+    topw_partial_wave<T, kAligned>(logits, row_stride, rows, V, W, npiece, ppw, nlist, ws_keys,
+                                   ws_ms, blockIdx.x * 4 + wid);
+}
+
+// One wave per row: merge the partial lists and (max, sum) pairs of row r.  `keys` holds
+// kMaxLists * JT_MAX_W keys and `top` JT_MAX_W keys of this wave's LDS.
+__device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
+                               const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
+                               float *__restrict__ logprob, float *__restrict__ row_lse,
+                               uint64_t *keys, uint64_t *top)
+{
+    const int lane = threadIdx.x & 63;
     const int n = nchunk * W;
     // Every load is issued before any result is used (one memory round trip for lists of
     // up to 64 * kKeyBatch keys): the (max, sum) pairs, then the keys.
@@ -318,9 +359,8 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
         lse = -INFINITY;
     else
         lse = m + logf(s);
-    __syncthreads();
+    wave_sync();
     wave_select_topw(keys, n, W, top);
-    __syncthreads();
     if (lane < W) {
         const uint64_t k = top[lane];
         ids[(int64_t)r * W + lane] = (int32_t)key_id(k);
@@ -328,6 +368,16 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
     }
     if (lane == 0 && row_lse)
         row_lse[r] = lse;
+}
+
+__global__ void __launch_bounds__(64)
+topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
+                  const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
+                  float *__restrict__ logprob, float *__restrict__ row_lse)
+{
+    __shared__ uint64_t keys[kMaxLists * JT_MAX_W];
+    __shared__ uint64_t top[JT_MAX_W];
+    topw_merge_row(blockIdx.x, W, nchunk, ws_keys, ws_ms, ids, logprob, row_lse, keys, top);
 }
 
 struct TopwPlan {

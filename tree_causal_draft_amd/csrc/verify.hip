@@ -25,23 +25,25 @@ constexpr int kArgSub = 8192;
 constexpr int kArgMaxChunks = 64;
 
 template <typename T> struct AVec;
-template <> struct AVec<uint16_t> { static constexpr int kElems = 8; static constexpr int kLoads = 4; };
-template <> struct AVec<float> { static constexpr int kElems = 4; static constexpr int kLoads = 8; };
+template <> struct AVec<uint16_t> { static constexpr int kElems = 8; };
+template <> struct AVec<float> { static constexpr int kElems = 4; };
 
-template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kArgThreads)
-argmax_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, int nsub,
-                      int sub_per_wg, int nchunk, uint64_t *__restrict__ ws_keys,
-                      uint32_t *__restrict__ ws_nan)
+// Partial arg-max of (row, chunk) `vb` by a workgroup of NT threads; `wkey` / `wnan` hold
+// NT / 64 entries of LDS.
+template <typename T, bool kAligned, int NT>
+__device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logits, int64_t row_stride, int V,
+                                     int nsub, int sub_per_wg, int nchunk,
+                                     uint64_t *__restrict__ ws_keys, uint32_t *__restrict__ ws_nan,
+                                     int vb, uint64_t *wkey, uint32_t *wnan)
 {
     constexpr int E = AVec<T>::kElems;
-    constexpr int L = AVec<T>::kLoads;
-    __shared__ uint64_t wkey[4];
-    __shared__ uint32_t wnan[4];
+    constexpr int L = kArgSub / (E * NT);  // loads of 16 bytes per thread per sub-chunk
+    constexpr int NW = NT / 64;
+    static_assert(L * E * NT == kArgSub, "sub-chunk split");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
-    const int row_idx = blockIdx.x / nchunk;
-    const int chunk = blockIdx.x % nchunk;
+    const int row_idx = vb / nchunk;
+    const int chunk = vb % nchunk;
     const T *row = logits + (int64_t)row_idx * row_stride;
     const int sc0 = chunk * sub_per_wg;
     const int sc1 = min(nsub, sc0 + sub_per_wg);
@@ -52,44 +54,62 @@ argmax_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, i
     float best = -INFINITY;
     int64_t bi = first < V ? first : -1;
     bool nan = false;
-    for (int sc = sc0; sc < sc1; ++sc) {
+    // raw words of a sub-chunk (entries at or past V are not read); the loads of the next
+    // sub-chunk are issued before the current one is scanned
+    auto load_sub = [&](int sc, uint4 (&u)[L]) {
         const int64_t base = (int64_t)sc * kArgSub;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            const int64_t e0 = base + (int64_t)(tid + kArgThreads * i) * E;
+            const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
             if (kAligned && e0 + E <= V) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(row + e0);
-                float x[E];
-                if constexpr (sizeof(T) == 2) {
-                    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-                    x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
-                } else {
-                    x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
-                    x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
-                }
-#pragma unroll
-                for (int k = 0; k < E; ++k) {
-                    nan |= x[k] != x[k];
-                    if (x[k] > best) {
-                        best = x[k];
-                        bi = e0 + k;
-                    }
-                }
+                u[i] = *reinterpret_cast<const uint4 *>(row + e0);
             } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int k = 0; k < E; ++k) {
                     const int64_t e = e0 + k;
                     if (e < V) {
-                        float xv;
                         if constexpr (sizeof(T) == 2)
-                            xv = bf16_to_f32(row[e]);
+                            w[k >> 1] |= (uint32_t)row[e] << (16 * (k & 1));
                         else
-                            xv = row[e];
-                        nan |= xv != xv;
-                        if (xv > best) {
-                            best = xv;
-                            bi = e;
-                        }
+                            w[k] = __float_as_uint(row[e]);
+                    }
+                }
+                u[i] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
+    uint4 next[L];
+    if (sc0 < sc1)
+        load_sub(sc0, next);
+    for (int sc = sc0; sc < sc1; ++sc) {
+        const int64_t base = (int64_t)sc * kArgSub;
+        uint4 cur[L];
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            cur[i] = next[i];
+        if (sc + 1 < sc1)
+            load_sub(sc + 1, next);
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
+            const uint4 u = cur[i];
+            float x[E];
+            if constexpr (sizeof(T) == 2) {
+                x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+                x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+            } else {
+                x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+                x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+            }
+            const bool full = e0 + E <= V;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                if (full || e0 + k < V) {
+                    nan |= x[k] != x[k];
+                    if (x[k] > best) {
+                        best = x[k];
+                        bi = e0 + k;
                     }
                 }
             }
@@ -104,19 +124,39 @@ argmax_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, i
     }
     __syncthreads();
     if (tid == 0) {
-        const uint64_t k = max(max(wkey[0], wkey[1]), max(wkey[2], wkey[3]));
-        ws_keys[blockIdx.x] = k;
-        ws_nan[blockIdx.x] = wnan[0] | wnan[1] | wnan[2] | wnan[3];
+        uint64_t k = wkey[0];
+        uint32_t n = wnan[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            k = max(k, wkey[w]);
+            n |= wnan[w];
+        }
+        ws_keys[vb] = k;
+        ws_nan[vb] = n;
     }
 }
 
-__global__ void __launch_bounds__(256)
-verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_keys,
-                   const uint32_t *__restrict__ ws_nan, const int32_t *__restrict__ parent,
-                   const int32_t *__restrict__ tokens, const uint64_t *__restrict__ anc,
-                   const int32_t *__restrict__ depth, int32_t *__restrict__ accept_len,
-                   int32_t *__restrict__ accept_path, int32_t *__restrict__ bonus,
-                   int32_t *__restrict__ argmax_out, int32_t *__restrict__ err)
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kArgThreads)
+argmax_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, int nsub,
+                      int sub_per_wg, int nchunk, uint64_t *__restrict__ ws_keys,
+                      uint32_t *__restrict__ ws_nan)
+{
+    __shared__ uint64_t wkey[kArgThreads / 64];
+    __shared__ uint32_t wnan[kArgThreads / 64];
+    argmax_partial_block<T, kAligned, kArgThreads>(logits, row_stride, V, nsub, sub_per_wg, nchunk,
+                                                   ws_keys, ws_nan, blockIdx.x, wkey, wnan);
+}
+
+// Phase 2 for sequence s by a workgroup of 256 threads.  err[s] receives the verification
+// flags OR-ed with extra0[s] and extra1[s] (flags of other steps; either may be NULL).
+__device__ __forceinline__ void verify_walk_block(int s, int B, int N, int nchunk, const uint64_t *__restrict__ ws_keys,
+                                  const uint32_t *__restrict__ ws_nan, const int32_t *__restrict__ parent,
+                                  const int32_t *__restrict__ tokens, const uint64_t *__restrict__ anc,
+                                  const int32_t *__restrict__ depth, int32_t *__restrict__ accept_len,
+                                  int32_t *__restrict__ accept_path, int32_t *__restrict__ bonus,
+                                  int32_t *__restrict__ argmax_out, int32_t *__restrict__ err,
+                                  const int32_t *__restrict__ extra0, const int32_t *__restrict__ extra1)
 {
     __shared__ unsigned long long amk[JT_MAX_NODES];
     __shared__ uint32_t amn[JT_MAX_NODES];
@@ -124,10 +164,16 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
     __shared__ uint64_t okw[4];
     __shared__ uint32_t wbest[4];
     __shared__ int fl[4];
-    const int s = blockIdx.x;
     const int v = threadIdx.x;
     const int lane = v & 63, wid = v >> 6;
     const int64_t nb = (int64_t)s * B + v;
+    int extra = 0;
+    if (v == 0) {
+        if (extra0)
+            extra |= extra0[s];
+        if (extra1)
+            extra |= extra1[s];
+    }
 
     if (v < B) {
         amk[v] = 0ull;
@@ -218,7 +264,7 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
             accept_len[s] = 0;
             bonus[s] = am_v;
             if (err)
-                err[s] = f;
+                err[s] = f | extra;
         }
         return;
     }
@@ -252,8 +298,20 @@ verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_key
         accept_len[s] = len;
         bonus[s] = am_of(vstar);
         if (err)
-            err[s] = f;
+            err[s] = f | extra;
     }
+}
+
+__global__ void __launch_bounds__(256)
+verify_walk_kernel(int B, int N, int nchunk, const uint64_t *__restrict__ ws_keys,
+                   const uint32_t *__restrict__ ws_nan, const int32_t *__restrict__ parent,
+                   const int32_t *__restrict__ tokens, const uint64_t *__restrict__ anc,
+                   const int32_t *__restrict__ depth, int32_t *__restrict__ accept_len,
+                   int32_t *__restrict__ accept_path, int32_t *__restrict__ bonus,
+                   int32_t *__restrict__ argmax_out, int32_t *__restrict__ err)
+{
+    verify_walk_block(blockIdx.x, B, N, nchunk, ws_keys, ws_nan, parent, tokens, anc, depth,
+                      accept_len, accept_path, bonus, argmax_out, err, nullptr, nullptr);
 }
 
 struct ArgPlan {

@@ -12,8 +12,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (build_tree_mask, topw_per_depth, tree_attention, tree_attention_workspace_size,
-               topw_workspace_size, verify_greedy, verify_workspace_size, JT_BF16, JT_F32)
+from . import (build_tree_mask, draft_verify_step, step_workspace_size, topw_per_depth,
+               tree_attention, tree_attention_workspace_size, topw_workspace_size, verify_greedy,
+               verify_workspace_size, JT_BF16, JT_F32)
 from .workload import Workload
 
 
@@ -71,6 +72,12 @@ class DeviceStep:
             nb = verify_workspace_size(S, B, cfg.V, dt)
             self.verify_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
 
+        if parts == ("topw", "mask", "attn", "verify") and dt == JT_BF16:
+            self.err_step = torch.empty(S, dtype=torch.int32, device=dev)
+            nb = step_workspace_size(S, B, N, W, cfg.V, cfg.Hq, cfg.Hkv, cfg.d, w.max_prefix, dt,
+                                     cfg.block_size if w.block_table is not None else 0)
+            self.step_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
     # ---- the four calls
     def topw(self):
         topw_per_depth(self.draft, self.cfg.W, ids=self.ids, logprob=self.logprob,
@@ -127,3 +134,17 @@ class DeviceStep:
             cur.wait_stream(s_topw)
         if "verify" in self.parts:
             cur.wait_stream(s_verify)
+
+    def run_fused(self):
+        """The whole step through jt_draft_verify_step (two launches), into the same output
+        buffers as the four calls; err goes to err_step."""
+        w = self.w
+        draft_verify_step(self.draft, self.target, self.parent, self.tokens, self.cfg.N,
+                          self.cfg.W, self.q, self.k_tree, self.v_tree, self.k_prefix,
+                          self.v_prefix, self.prefix_len, block_table=self.block_table,
+                          block_size=self.cfg.block_size, num_blocks=w.num_blocks or None,
+                          max_prefix=w.max_prefix, out=self.attn_out, lse=self.lse, ids=self.ids,
+                          logprob=self.logprob, row_lse=self.row_lse, anc=self.anc,
+                          depth=self.depth, accept_len=self.accept_len,
+                          accept_path=self.accept_path, bonus=self.bonus, argmax_out=self.argmax,
+                          err=self.err_step, workspace=self.step_ws)
