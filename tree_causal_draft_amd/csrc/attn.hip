@@ -280,8 +280,12 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     const int gran = 64;
     const int keys = max_prefix + B;
     const int maxc = (keys + gran - 1) / gran;
-    // 8-wave workgroups hold 128 KB of LDS (one per CU); the smaller ones two per CU
-    const int target = p.nwr == 8 ? 256 : 512;
+    // Workgroups to aim for.  8-wave workgroups hold 128 KB of LDS, one per CU: one per
+    // CU.  Smaller ones (few rows, a latency-bound pass) take at least two tiles each:
+    // fewer, longer chunks cost less in the split-KV merge than they add to the pass
+    // (measured on the 16-node, 1024-key shape: 17 one-tile chunks per unit 17.5 us,
+    // 9 two-tile chunks 15.8 us), and they leave CUs to the logit scans of the fused step.
+    const int target = p.nwr == 8 ? 256 : 128;
     int want = (target + p.units - 1) / p.units;
     if (want > maxc)
         want = maxc;

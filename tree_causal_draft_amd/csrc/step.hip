@@ -52,10 +52,11 @@ struct StepPlan {
 constexpr int kStepRowsPerBlock = 4;  // phase 2: top-W rows merged per workgroup (one per wave)
 
 template <int D, int NWR> struct StepLds {
+    static constexpr int TOPW = NWR * (kWaveCap + 2 * JT_MAX_W) * 8;
     static constexpr int MASK = JT_MAX_NODES * (32 + 4 + 4);
     static constexpr int ARG = 2 * NWR * 8;
     static constexpr int A = AttnLds<D, NWR>::BYTES;
-    static constexpr int BYTES = A > MASK ? A : MASK;
+    static constexpr int BYTES = A > TOPW ? (A > MASK ? A : MASK) : (TOPW > MASK ? TOPW : MASK);
     static_assert(ARG <= BYTES, "arg-max slice");
 };
 
@@ -71,9 +72,12 @@ __device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepP
     }
     b -= sp.nA;
     if (b < sp.nT) {
+        const int wid = threadIdx.x >> 6;
+        uint64_t *cand = reinterpret_cast<uint64_t *>(pool) + wid * (kWaveCap + 2 * JT_MAX_W);
         topw_partial_wave<uint16_t, true>(
             static_cast<const uint16_t *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
-            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, b * NWR + (threadIdx.x >> 6));
+            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, b * NWR + wid, cand,
+            cand + kWaveCap + JT_MAX_W);
         return;
     }
     b -= sp.nT;

@@ -24,6 +24,7 @@ namespace jt {
 
 constexpr int kTopwThreads = 256;   // 4 independent waves per workgroup
 constexpr int kPiece = 2048;        // logits per wave piece (32 per lane)
+constexpr int kWaveCap = 512;       // candidate slots per wave in LDS
 constexpr int kMaxLists = 128;      // partial lists per row seen by the merge kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -139,50 +140,72 @@ __device__ void wave_select_topw(const uint64_t *keys, int n, int W, uint64_t *o
     wave_sync();
 }
 
-// Top two keys of a lane's elements below `lim` (keys are unique; 0 = none): a pairwise
-// tree over the 32 slots, so the comparisons of one level are independent of each other.
-template <typename KeyOf>
-__device__ __forceinline__ void lane_top2(KeyOf key_of, uint64_t lim, uint64_t &k1, uint64_t &k2)
+// Wave-wide maximum / OR of a 32-bit value through DPP row operations and the row
+// broadcasts; every lane receives the result.
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
-    uint64_t a[16], b[16];  // per pair: larger, smaller
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        uint64_t u = key_of(2 * p), v = key_of(2 * p + 1);
-        u = u < lim ? u : 0ull;
-        v = v < lim ? v : 0ull;
-        const bool gt = u > v;
-        a[p] = gt ? u : v;
-        b[p] = gt ? v : u;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+    v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+    v = max(v, dpp_u32<0x141, 0xF>(v));  // row_half_mirror
+    v = max(v, dpp_u32<0x140, 0xF>(v));  // row_mirror
+    v = max(v, dpp_u32<0x142, 0xA>(v));  // row_bcast:15
+    v = max(v, dpp_u32<0x143, 0xC>(v));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v)
+{
+    v |= dpp_u32<0xB1, 0xF>(v);
+    v |= dpp_u32<0x4E, 0xF>(v);
+    v |= dpp_u32<0x141, 0xF>(v);
+    v |= dpp_u32<0x140, 0xF>(v);
+    v |= dpp_u32<0x142, 0xA>(v);
+    v |= dpp_u32<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The W-th largest of the lanes' codes, counting equal codes as often as they occur (W
+// rounds of a wave max, each removing one occurrence); 0 if fewer than W codes are nonzero.
+__device__ __forceinline__ uint32_t wave_wth_code(uint32_t code, int W)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t t = 0u;
+    for (int r = 0; r < W; ++r) {
+        t = wave_max_u32(code);
+        if (t == 0u)
+            return 0u;
+        const uint64_t at = __ballot(code == t);
+        if (lane == __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(at)))
+            code = 0u;
     }
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int p = 0; p < w; ++p) {
-            const uint64_t a1 = a[p], a2 = b[p], b1 = a[p + w], b2 = b[p + w];
-            const bool gt = a1 > b1;
-            const uint64_t s1 = gt ? b1 : a1, s2 = gt ? a2 : b2;  // candidates for second
-            a[p] = gt ? a1 : b1;
-            b[p] = s1 > s2 ? s1 : s2;
-        }
-    }
-    k1 = a[0];
-    k2 = b[0];
+    return t;
 }
 
 // Each wave owns `ppw` consecutive pieces of 2048 logits of one row and works alone (no
-// LDS, no workgroup barrier).  Per piece: the lane's (max, sum of exp(x - max)), merged
-// into a running pair; the lane's two largest 64-bit keys (order code << 32 | ~id: value
-// descending, id ascending in one integer compare, so bf16 ties resolve like a full
-// sort); then W rounds of a DPP wave max over the lanes' offers -- a lane offers the
-// larger of its best unused key and its entry of the wave's running top-W list (lane r
-// holds entry r) -- which rebuild that list.  A lane whose two keys are used up and that
-// still holds elements recomputes its top two below the last key it gave (rare).
+// workgroup barrier).  Per piece:
+//   * the lane's (max, sum of exp(x - max)), merged into a running pair;
+//   * a threshold tau: the larger of the W-th largest lane maximum and the W-th entry of
+//     the wave's running list (a lower bound on the W-th largest key of the piece and the
+//     list together), so only logits >= tau can enter the list;
+//   * the lanes' candidate masks (one float compare per logit) and their wave-wide OR,
+//     which skips every slot j that no lane needs; the candidates of the remaining slots
+//     are compacted into the wave's LDS slice as 64-bit keys (order code << 32 | ~id:
+//     value descending, id ascending in one integer compare, so bf16 ties resolve like a
+//     full sort) by ballot + mbcnt;
+//   * the running list (lane r holds entry r) is appended and W rounds of a DPP wave max
+//     -- over registers when at most 64 keys compete, else over the LDS slice -- give the
+//     new list.
 // Output per wave: its W best keys, descending, 0-padded, and its (max, sum) pair.
+// `cand` holds kWaveCap + JT_MAX_W keys and `best` JT_MAX_W keys of this wave's LDS.
 template <typename T, bool kAligned>
 __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, int64_t row_stride,
                                                   int rows, int V, int W, int npiece, int ppw,
                                                   int nlist, uint64_t *__restrict__ ws_keys,
-                                                  float2 *__restrict__ ws_ms, int gl)
+                                                  float2 *__restrict__ ws_ms, int gl,
+                                                  uint64_t *cand, uint64_t *best)
 {
     constexpr int E = Vec<T>::kElems;
     const int lane = threadIdx.x & 63;
@@ -235,44 +258,86 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
             run_s += sx * __builtin_amdgcn_exp2f((m - run_m) * kLog2e);
         }
 
-        // ---- this piece's keys against the running list
-        const uint32_t idl = (uint32_t)(base + (int64_t)lane * E);
+        // ---- threshold: a lane's code counts only if it holds a real (non-NaN) element
+        // equal to its maximum
+        bool real = m != -INFINITY;
+        if (!real) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                real |= ((valid >> j) & 1u) && x[j] == -INFINITY;
+        }
+        uint32_t tau = wave_wth_code(real ? order_code(m) : 0u, W);
+        const uint32_t run_w =
+            (uint32_t)((uint64_t)__builtin_amdgcn_readlane((int)(run >> 32), W - 1));
+        tau = max(tau, run_w);
         auto key_of = [&](int j) -> uint64_t {
-            if (!((valid >> j) & 1u))
-                return 0ull;
-            const uint32_t id = idl + (uint32_t)(kWave * E * (j / E) + j % E);
+            const uint32_t id = (uint32_t)(base + (int64_t)lane * E) + (uint32_t)(kWave * E * (j / E) + j % E);
             return ((uint64_t)order_code(x[j]) << 32) | (uint64_t)(~id);
         };
-        uint64_t k1, k2;
-        lane_top2(key_of, ~0ull, k1, k2);
-        const int nval = __popc(valid);
-        int used = 0;             // keys of this piece this lane has given
-        uint64_t last = ~0ull;    // the last of them
-        uint64_t rk = lane < W ? run : 0ull;
-        uint64_t nrun = 0ull;
-        for (int r = 0; r < W; ++r) {
-            const uint64_t offer = k1 > rk ? k1 : rk;
-            const uint64_t K = wave_max_u64_dpp(offer);
-            if (K == 0ull)
-                break;  // fewer than W keys in all: the rest of the list stays empty
-            if (lane == r)
-                nrun = K;
-            if (offer == K) {  // this lane supplied K (keys are unique)
-                if (rk == K) {
-                    rk = 0ull;
-                } else {
-                    k1 = k2;
-                    k2 = 0ull;
-                    last = K;
-                    ++used;
-                }
-            }
-            // known keys used up while elements remain: the next two below the last one
-            const bool refill = k1 == 0ull && used < nval;
-            if (__ballot(refill) && refill)
-                lane_top2(key_of, last, k1, k2);
+        // tau == 0: fewer than W real lane maxima; every valid element is a candidate
+        uint32_t msk = valid;
+        if (tau != 0u) {
+            const float tf = order_decode(tau);  // x >= tf <=> code(x) >= tau, for non-NaN x
+            uint32_t mk = 0u;
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                mk |= (x[j] >= tf ? 1u : 0u) << j;
+            msk &= mk;
         }
-        run = nrun;
+        const uint32_t jmask = wave_or_u32(msk);
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            if (jmask & (1u << j)) {
+                const bool pred = (msk >> j) & 1u;
+                const uint64_t b = __ballot(pred);
+                const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                if (pred && slot < kWaveCap)
+                    cand[slot] = key_of(j);
+                n += __popcll(b);
+            }
+        }
+        if (n > kWaveCap) {
+            // rare overflow (huge ties): W rounds of exact arg-max over the registers
+            uint64_t prev = ~0ull;
+            for (int r = 0; r < W; ++r) {
+                uint64_t mine = 0ull;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    if (!((msk >> j) & 1u))
+                        continue;
+                    const uint64_t k = key_of(j);
+                    if (k < prev && k > mine)
+                        mine = k;
+                }
+                mine = wave_max_u64_dpp(mine);
+                if (lane == 0)
+                    cand[r] = mine;
+                prev = mine;
+            }
+            n = W;
+        }
+        if (lane < W)
+            cand[n + lane] = run;
+        wave_sync();
+        const int tot = n + W;
+        if (tot <= kWave) {
+            uint64_t v = lane < tot ? cand[lane] : 0ull;
+            uint64_t nrun = 0ull;
+            for (int r = 0; r < W; ++r) {
+                const uint64_t K = wave_max_u64_dpp(v);
+                if (lane == r)
+                    nrun = K;
+                if (v == K)
+                    v = 0ull;
+            }
+            run = nrun;
+        } else {
+            wave_select_topw(cand, tot, W, best);
+            run = lane < W ? best[lane] : 0ull;
+        }
+        wave_sync();  // the slice is rewritten by the next piece
     }
 
     // ---- (max, sum) over the wave
@@ -294,9 +359,11 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
                     int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
                     float2 *__restrict__ ws_ms)
 {
+    __shared__ uint64_t cand_all[4][kWaveCap + JT_MAX_W];
+    __shared__ uint64_t best_all[4][JT_MAX_W];
     const int wid = threadIdx.x >> 6;
     topw_partial_wave<T, kAligned>(logits, row_stride, rows, V, W, npiece, ppw, nlist, ws_keys,
-                                   ws_ms, blockIdx.x * 4 + wid);
+                                   ws_ms, blockIdx.x * 4 + wid, cand_all[wid], best_all[wid]);
 }
 
 // One wave per row: merge the partial lists and (max, sum) pairs of row r.  `keys` holds
