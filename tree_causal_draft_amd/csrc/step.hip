@@ -1,4 +1,5 @@
-// The whole draft-and-verify step in two launches (jt_draft_verify_step).
+// The whole draft-and-verify step in two launches (jt_draft_verify_step); three for
+// shapes whose attention needs 8-wave workgroups (see step_scan_kernel).
 //
 // Each launch runs several steps side by side, one role per range of workgroup ids:
 //   phase 1  attention   the split-KV MFMA pass; its workgroups build the tree's ancestor
@@ -7,9 +8,9 @@
 //            top-W       the per-wave partial lists of the draft logit rows
 //            arg-max     the partial arg-max of the target logit rows
 //            mask        ancestor rows and depths to global memory
-//   phase 2  combine     the split-KV merge
+//   phase 2  verify      the per-sequence walk (reads phase 1's rows, depths, arg-max keys)
 //            top-W       the per-row merge of the partial lists
-//            verify      the per-sequence walk (reads phase 1's rows, depths, arg-max keys)
+//            combine     the split-KV merge
 // The roles run the device code of the separate entry points, so every output equals
 // what the four calls produce one after the other.  The verification walk is the only
 // writer of err[s]: it ORs the mask and attention flags (kept in the workspace) into its
@@ -60,32 +61,27 @@ template <int D, int NWR> struct StepLds {
     static_assert(ARG <= BYTES, "arg-max slice");
 };
 
-template <int D, int NWR>
-__device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepPlan &sp)
+// The scan and mask roles, for workgroups of NW waves; `b` counts from the first scan
+// workgroup.
+template <int NW>
+__device__ __forceinline__ void step_scan_roles(const StepArgs &sa, const StepPlan &sp, int b,
+                                                uint8_t *pool)
 {
-    constexpr int NT = 64 * NWR;
-    __shared__ __attribute__((aligned(16))) uint8_t pool[StepLds<D, NWR>::BYTES];
-    int b = blockIdx.x;
-    if (b < sp.nA) {
-        attn_main<D, NWR, true>(sa.attn, sp.ap, sa.aws, b, sp.nA, pool);
-        return;
-    }
-    b -= sp.nA;
     if (b < sp.nT) {
         const int wid = threadIdx.x >> 6;
         uint64_t *cand = reinterpret_cast<uint64_t *>(pool) + wid * (kWaveCap + 2 * JT_MAX_W);
         topw_partial_wave<uint16_t, true>(
             static_cast<const uint16_t *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
-            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, b * NWR + wid, cand,
+            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, b * NW + wid, cand,
             cand + kWaveCap + JT_MAX_W);
         return;
     }
     b -= sp.nT;
     if (b < sp.nG) {
-        argmax_partial_block<uint16_t, true, NT>(
+        argmax_partial_block<uint16_t, true, 64 * NW>(
             static_cast<const uint16_t *>(sa.target), sa.target_stride, sa.V, sp.gp.nsub,
             sp.gp.sub_per_wg, sp.gp.nchunk, sa.gkeys, sa.gnan, b,
-            reinterpret_cast<uint64_t *>(pool), reinterpret_cast<uint32_t *>(pool + NWR * 8));
+            reinterpret_cast<uint64_t *>(pool), reinterpret_cast<uint32_t *>(pool + NW * 8));
         return;
     }
     b -= sp.nG;
@@ -95,33 +91,51 @@ __device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepP
                reinterpret_cast<int32_t *>(pool + JT_MAX_NODES * 36));
 }
 
+template <int D, int NWR>
+__device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepPlan &sp)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t pool[StepLds<D, NWR>::BYTES];
+    const int b = blockIdx.x;
+    if (b < sp.nA)
+        attn_main<D, NWR, true>(sa.attn, sp.ap, sa.aws, b, sp.nA, pool);
+    else
+        step_scan_roles<NWR>(sa, sp, b - sp.nA, pool);
+}
+
 // 4 waves: two workgroups per CU (register budget 256 per lane, LDS 2 x 74 KB)
 template <int D>
 __global__ void __launch_bounds__(256, 2) step_phase1_w4(StepArgs sa, StepPlan sp)
 {
     step_phase1_body<D, 4>(sa, sp);
 }
-template <int D>
-__global__ void __launch_bounds__(512) step_phase1_w8(StepArgs sa, StepPlan sp)
+
+// Shapes whose attention needs 8-wave workgroups (128 KB of LDS each, one per CU) would
+// leave the scans one workgroup slot per CU if they shared its launch.  There the scans and
+// the mask run first in a launch of their own (small LDS, many workgroups per CU), then
+// the attention pass (reading the mask's rows), then phase 2.
+constexpr int kScanLds = 4 * (kWaveCap + 2 * JT_MAX_W) * 8 > JT_MAX_NODES * 40
+                             ? 4 * (kWaveCap + 2 * JT_MAX_W) * 8
+                             : JT_MAX_NODES * 40;
+__global__ void __launch_bounds__(256) step_scan_kernel(StepArgs sa, StepPlan sp)
 {
-    step_phase1_body<D, 8>(sa, sp);
+    __shared__ __attribute__((aligned(16))) uint8_t pool[kScanLds];
+    step_scan_roles<4>(sa, sp, blockIdx.x, pool);
 }
 
 template <int D, int NB>
 __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
 {
-    __shared__ uint64_t mkeys[kStepRowsPerBlock][kMaxLists * JT_MAX_W];
+    __shared__ uint64_t mkeys[kStepRowsPerBlock][kMergeCand];
     __shared__ uint64_t mtop[kStepRowsPerBlock][JT_MAX_W];
+    // the per-row and per-sequence roles first: they are the longer ones
     int b = blockIdx.x;
-    if (b < sp.nC) {
-        const int64_t t = (int64_t)b * 256 + threadIdx.x;
-        const int64_t per_unit = (int64_t)sp.ap.rt * (D / 8);
-        const int unit = (int)(t / per_unit);
-        if (unit < sp.ap.units)
-            attn_merge_unit<D, NB>(sa.attn, sp.ap, sa.aws, unit, (int)(t % per_unit), (int)per_unit);
+    if (b < sp.nW) {
+        verify_walk_block(b, sa.B, sa.N, sp.gp.nchunk, sa.gkeys, sa.gnan, sa.parent, sa.tokens,
+                          sa.anc, sa.depth, sa.accept_len, sa.accept_path, sa.bonus,
+                          sa.argmax_out, sa.err, sa.err_mask, sa.err_attn);
         return;
     }
-    b -= sp.nC;
+    b -= sp.nW;
     if (b < sp.nR) {
         const int wid = threadIdx.x >> 6;
         const int r = b * kStepRowsPerBlock + wid;
@@ -131,9 +145,11 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
         return;
     }
     b -= sp.nR;
-    verify_walk_block(b, sa.B, sa.N, sp.gp.nchunk, sa.gkeys, sa.gnan, sa.parent, sa.tokens, sa.anc,
-                      sa.depth, sa.accept_len, sa.accept_path, sa.bonus, sa.argmax_out, sa.err,
-                      sa.err_mask, sa.err_attn);
+    const int64_t t = (int64_t)b * 256 + threadIdx.x;
+    const int64_t per_unit = (int64_t)sp.ap.rt * (D / 8);
+    const int unit = (int)(t / per_unit);
+    if (unit < sp.ap.units)
+        attn_merge_unit<D, NB>(sa.attn, sp.ap, sa.aws, unit, (int)(t % per_unit), (int)per_unit);
 }
 
 // ------------------------------------------------------------------ host side --
@@ -152,25 +168,31 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
         sp.ap.nwr = 4;  // same rows, chunks and results; the other two waves idle
         sp.ap.rt = 128;
     }
-    const int nwr = sp.ap.nwr;
+    const bool split = sp.ap.nwr == 8;  // scans in a launch of their own
+    const int nw = split ? 4 : sp.ap.nwr;  // waves per scan workgroup
     const int rows_d = S * N, rows_t = S * B;
-    sp.tp.npiece = (V + kPiece - 1) / kPiece;
-    sp.tp.ppw = (sp.tp.npiece + kMaxLists - 1) / kMaxLists;
-    if (sp.tp.ppw < 2 && rows_d * sp.tp.npiece > 4 * 256)
-        sp.tp.ppw = 2;
-    sp.tp.nlist = (sp.tp.npiece + sp.tp.ppw - 1) / sp.tp.ppw;
-    sp.gp.nsub = (V + kArgSub - 1) / kArgSub;
-    int want = rows_t > 0 ? (256 + rows_t - 1) / rows_t : 1;  // chunks per row
-    want = max(want, (sp.gp.nsub + 3) / 4);                     // at most ~4 sub-chunks each
-    int spw = (sp.gp.nsub + want - 1) / want;
-    if (spw < 1)
-        spw = 1;
-    while ((sp.gp.nsub + spw - 1) / spw > kArgMaxChunks)
-        ++spw;
-    sp.gp.sub_per_wg = spw;
-    sp.gp.nchunk = (sp.gp.nsub + spw - 1) / spw;
+    if (split) {
+        sp.tp = topw_plan(rows_d, V);
+        sp.gp = arg_plan(rows_t, V);
+    } else {
+        sp.tp.npiece = (V + kPiece - 1) / kPiece;
+        sp.tp.ppw = (sp.tp.npiece + kMaxLists - 1) / kMaxLists;
+        if (sp.tp.ppw < 2 && rows_d * sp.tp.npiece > 4 * 256)
+            sp.tp.ppw = 2;
+        sp.tp.nlist = (sp.tp.npiece + sp.tp.ppw - 1) / sp.tp.ppw;
+        sp.gp.nsub = (V + kArgSub - 1) / kArgSub;
+        int want = rows_t > 0 ? (256 + rows_t - 1) / rows_t : 1;  // chunks per row
+        want = max(want, (sp.gp.nsub + 3) / 4);                     // at most ~4 sub-chunks each
+        int spw = (sp.gp.nsub + want - 1) / want;
+        if (spw < 1)
+            spw = 1;
+        while ((sp.gp.nsub + spw - 1) / spw > kArgMaxChunks)
+            ++spw;
+        sp.gp.sub_per_wg = spw;
+        sp.gp.nchunk = (sp.gp.nsub + spw - 1) / spw;
+    }
     sp.nA = sp.ap.units * sp.ap.n_chunks;
-    sp.nT = (rows_d * sp.tp.nlist + nwr - 1) / nwr;
+    sp.nT = (rows_d * sp.tp.nlist + nw - 1) / nw;
     sp.nG = rows_t * sp.gp.nchunk;
     sp.nM = S;
     sp.nC = sp.ap.n_chunks > 1
@@ -217,11 +239,18 @@ size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d,
 template <int D>
 static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st)
 {
-    const unsigned g1 = (unsigned)(sp.nA + sp.nT + sp.nG + sp.nM);
-    if (sp.ap.nwr == 8)
-        hipLaunchKernelGGL((step_phase1_w8<D>), dim3(g1), dim3(512), 0, st, sa, sp);
-    else
+    if (sp.ap.nwr == 8) {
+        const unsigned gs = (unsigned)(sp.nT + sp.nG + sp.nM);
+        hipLaunchKernelGGL(step_scan_kernel, dim3(gs), dim3(256), 0, st, sa, sp);
+        AttnArgs a = sa.attn;
+        a.anc = sa.anc;  // the mask role's rows
+        a.parent = nullptr;
+        hipLaunchKernelGGL((attn_bf16_kernel<D, 8>), dim3((unsigned)sp.nA), dim3(512), 0, st, a,
+                           sp.ap, sa.aws);
+    } else {
+        const unsigned g1 = (unsigned)(sp.nA + sp.nT + sp.nG + sp.nM);
         hipLaunchKernelGGL((step_phase1_w4<D>), dim3(g1), dim3(256), 0, st, sa, sp);
+    }
     const unsigned g2 = (unsigned)(sp.nC + sp.nR + sp.nW);
     if (sp.ap.n_chunks > 8 && sp.ap.n_chunks <= 16)
         hipLaunchKernelGGL((step_phase2<D, 16>), dim3(g2), dim3(256), 0, st, sa, sp);

@@ -366,8 +366,14 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
                                    ws_ms, blockIdx.x * 4 + wid, cand_all[wid], best_all[wid]);
 }
 
-// One wave per row: merge the partial lists and (max, sum) pairs of row r.  `keys` holds
-// kMaxLists * JT_MAX_W keys and `top` JT_MAX_W keys of this wave's LDS.
+constexpr int kMergeCand = JT_MAX_W * JT_MAX_W;  // candidate keys a row merge can keep
+
+// One wave per row: merge the partial lists and (max, sum) pairs of row r.  With at most 8
+// keys per lane, W rounds of a DPP wave max run straight over the registers.  Otherwise:
+// every list is sorted descending, so the W-th largest list head bounds the row's W-th
+// largest key from below, and only keys at or above it (at most W per list with a head
+// there, W * W in all) compete.  They are compacted into `keys` (kMergeCand entries of this wave's LDS) and W
+// rounds of a DPP wave max pick the W largest -- over registers when at most 64 compete.
 __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
                                const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
                                float *__restrict__ logprob, float *__restrict__ row_lse,
@@ -375,30 +381,29 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
 {
     const int lane = threadIdx.x & 63;
     const int n = nchunk * W;
-    // Every load is issued before any result is used (one memory round trip for lists of
-    // up to 64 * kKeyBatch keys): the (max, sum) pairs, then the keys.
+    // Every load is issued before any result is used (one memory round trip): the (max,
+    // sum) pairs, the list heads and all keys.
     constexpr int kMsPerLane = kMaxLists / kWave;
-    constexpr int kKeyBatch = 16;
+    constexpr int kKeysPerLane = kMaxLists * JT_MAX_W / kWave;
     const float2 *msr = ws_ms + (int64_t)r * nchunk;
     const uint64_t *src = ws_keys + (int64_t)r * n;
     float2 ms[kMsPerLane];
+    uint64_t hd[kMsPerLane];
 #pragma unroll
     for (int j = 0; j < kMsPerLane; ++j) {
         const int c = lane + kWave * j;
         ms[j] = c < nchunk ? msr[c] : make_float2(-INFINITY, 0.f);
+        hd[j] = c < nchunk ? src[(int64_t)c * W] : 0ull;
     }
-    for (int i0 = 0; i0 < n; i0 += kWave * kKeyBatch) {
-        uint64_t kr[kKeyBatch];
+    const int nq = (n + kWave - 1) / kWave;  // key slots in use (wave-uniform)
+    uint64_t kr[kKeysPerLane];
 #pragma unroll
-        for (int q = 0; q < kKeyBatch; ++q) {
-            const int i = i0 + lane + kWave * q;
-            kr[q] = i < n ? src[i] : 0ull;
-        }
-#pragma unroll
-        for (int q = 0; q < kKeyBatch; ++q) {
-            const int i = i0 + lane + kWave * q;
+    for (int q = 0; q < kKeysPerLane; ++q) {
+        kr[q] = 0ull;
+        if (q < nq) {
+            const int i = lane + kWave * q;
             if (i < n)
-                keys[i] = kr[q];
+                kr[q] = src[i];
         }
     }
     // LSE over the row
@@ -426,12 +431,83 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
         lse = -INFINITY;
     else
         lse = m + logf(s);
+
+    if (nq <= 8) {
+        // few keys per lane: W rounds straight over the registers, each taking the largest
+        // key below the previous winner
+        uint64_t prev = ~0ull, mine_top = 0ull;
+        for (int k = 0; k < W; ++k) {
+            uint64_t mine = 0ull;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (q < nq)
+                    mine = (kr[q] < prev && kr[q] > mine) ? kr[q] : mine;
+            const uint64_t K = wave_max_u64_dpp(mine);
+            if (lane == k)
+                mine_top = K;
+            prev = K;
+        }
+        if (lane < W) {
+            ids[(int64_t)r * W + lane] = (int32_t)key_id(mine_top);
+            logprob[(int64_t)r * W + lane] = key_value(mine_top) - lse;
+        }
+        if (lane == 0 && row_lse)
+            row_lse[r] = lse;
+        return;
+    }
+    // threshold: the W-th largest head (keys are unique; 0 = empty), 0 if fewer than W
+    uint64_t tau = 0ull;
+    for (int k = 0; k < W; ++k) {
+        uint64_t mine = hd[0];
+#pragma unroll
+        for (int j = 1; j < kMsPerLane; ++j)
+            mine = hd[j] > mine ? hd[j] : mine;
+        const uint64_t K = wave_max_u64_dpp(mine);
+        tau = K;
+        if (K == 0ull)
+            break;
+#pragma unroll
+        for (int j = 0; j < kMsPerLane; ++j)
+            hd[j] = hd[j] == K ? 0ull : hd[j];
+    }
+    // candidates: nonzero keys >= tau, compacted slot by slot (slots no lane needs skipped)
+    uint32_t mk = 0u;
+#pragma unroll
+    for (int q = 0; q < kKeysPerLane; ++q)
+        if (q < nq)
+            mk |= (kr[q] != 0ull && kr[q] >= tau ? 1u : 0u) << q;
+    const uint32_t jm = wave_or_u32(mk);
+    int nc = 0;
+#pragma unroll
+    for (int q = 0; q < kKeysPerLane; ++q) {
+        if (jm & (1u << q)) {
+            const bool pred = (mk >> q) & 1u;
+            const uint64_t b = __ballot(pred);
+            const int slot = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            if (pred && slot < kMergeCand)
+                keys[slot] = kr[q];
+            nc += __popcll(b);
+        }
+    }
     wave_sync();
-    wave_select_topw(keys, n, W, top);
+    uint64_t mine_top = 0ull;
+    if (nc <= kWave) {
+        uint64_t v = lane < nc ? keys[lane] : 0ull;
+        for (int k = 0; k < W; ++k) {
+            const uint64_t K = wave_max_u64_dpp(v);
+            if (lane == k)
+                mine_top = K;
+            if (v == K)
+                v = 0ull;
+        }
+    } else {
+        wave_select_topw(keys, nc < kMergeCand ? nc : kMergeCand, W, top);
+        mine_top = lane < W ? top[lane] : 0ull;
+    }
     if (lane < W) {
-        const uint64_t k = top[lane];
-        ids[(int64_t)r * W + lane] = (int32_t)key_id(k);
-        logprob[(int64_t)r * W + lane] = key_value(k) - lse;
+        ids[(int64_t)r * W + lane] = (int32_t)key_id(mine_top);
+        logprob[(int64_t)r * W + lane] = key_value(mine_top) - lse;
     }
     if (lane == 0 && row_lse)
         row_lse[r] = lse;
@@ -442,7 +518,7 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
                   const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
                   float *__restrict__ logprob, float *__restrict__ row_lse)
 {
-    __shared__ uint64_t keys[kMaxLists * JT_MAX_W];
+    __shared__ uint64_t keys[kMergeCand];
     __shared__ uint64_t top[JT_MAX_W];
     topw_merge_row(blockIdx.x, W, nchunk, ws_keys, ws_ms, ids, logprob, row_lse, keys, top);
 }
