@@ -28,8 +28,15 @@ template <typename T> struct AVec;
 template <> struct AVec<uint16_t> { static constexpr int kElems = 8; };
 template <> struct AVec<float> { static constexpr int kElems = 4; };
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
 // Partial arg-max of (row, chunk) `vb` by a workgroup of NT threads; `wkey` / `wnan` hold
-// NT / 64 entries of LDS.
+// NT / 64 entries of LDS.  Two passes keep the per-logit work small: the scan keeps only
+// each thread's maximum (NaN skipped; a packed 16-bit maximum of the magnitudes detects
+// NaN) and the sub-chunk where it first reached it; after a block-wide maximum M, the
+// threads holding M re-read that sub-chunk (an L2 hit; the last one is still in
+// registers) for their first index of M, and a block-wide minimum gives the lowest.  With no value above -inf the chunk's first
+// element stands (a row of -inf keeps its first id).
 template <typename T, bool kAligned, int NT>
 __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logits, int64_t row_stride, int V,
                                      int nsub, int sub_per_wg, int nchunk,
@@ -48,14 +55,7 @@ __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logit
     const int sc0 = chunk * sub_per_wg;
     const int sc1 = min(nsub, sc0 + sub_per_wg);
 
-    // The thread's first element seeds the running best so that a row of -inf still
-    // yields its first id; later elements replace it only when strictly larger.
-    const int64_t first = (int64_t)sc0 * kArgSub + (int64_t)tid * E;
-    float best = -INFINITY;
-    int64_t bi = first < V ? first : -1;
-    bool nan = false;
-    // raw words of a sub-chunk (entries at or past V are not read); the loads of the next
-    // sub-chunk are issued before the current one is scanned
+    // raw words of a thread's share of one sub-chunk (entries at or past V are not read)
     auto load_sub = [&](int sc, uint4 (&u)[L]) {
         const int64_t base = (int64_t)sc * kArgSub;
 #pragma unroll
@@ -79,60 +79,116 @@ __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logit
             }
         }
     };
-    uint4 next[L];
-    if (sc0 < sc1)
-        load_sub(sc0, next);
+    auto unpack = [](const uint4 &u, float (&x)[E]) {
+        if constexpr (sizeof(T) == 2) {
+            x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+            x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+        } else {
+            x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+            x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+        }
+    };
+
+    float best = -INFINITY;  // thread maximum, NaN skipped
+    int sc_best = -1;        // sub-chunk where it was first reached (-1: nothing above -inf)
+    u16x2_t mag = {0, 0};    // bf16: maximum of the magnitude bits (NaN iff > 0x7f80)
+    uint32_t magf = 0u;      // fp32: the same on 32-bit words (NaN iff > 0x7f800000)
+    uint4 u[L];  // after the scan: the words of the last sub-chunk
     for (int sc = sc0; sc < sc1; ++sc) {
         const int64_t base = (int64_t)sc * kArgSub;
-        uint4 cur[L];
-#pragma unroll
-        for (int i = 0; i < L; ++i)
-            cur[i] = next[i];
-        if (sc + 1 < sc1)
-            load_sub(sc + 1, next);
+        load_sub(sc, u);
+        float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
-            const uint4 u = cur[i];
             float x[E];
-            if constexpr (sizeof(T) == 2) {
-                x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-                x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
-            } else {
-                x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
-                x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
-            }
-            const bool full = e0 + E <= V;
+            unpack(u[i], x);
+            if (e0 + E <= V) {
 #pragma unroll
-            for (int k = 0; k < E; ++k) {
-                if (full || e0 + k < V) {
-                    nan |= x[k] != x[k];
-                    if (x[k] > best) {
-                        best = x[k];
-                        bi = e0 + k;
+                for (int k = 0; k < E; ++k)
+                    m = fmaxf(m, x[k]);
+                if constexpr (sizeof(T) == 2) {
+                    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, u[i].x & 0x7fff7fffu));
+                    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, u[i].y & 0x7fff7fffu));
+                    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, u[i].z & 0x7fff7fffu));
+                    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2_t, u[i].w & 0x7fff7fffu));
+                } else {
+                    magf = max(magf, max(max(u[i].x & 0x7fffffffu, u[i].y & 0x7fffffffu),
+                                         max(u[i].z & 0x7fffffffu, u[i].w & 0x7fffffffu)));
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    if (e0 + k < V) {
+                        m = fmaxf(m, x[k]);
+                        const uint32_t b = __float_as_uint(x[k]) & 0x7fffffffu;
+                        if (b > 0x7f800000u)
+                            magf = 0xffffffffu;  // NaN (either dtype)
                     }
                 }
             }
         }
+        if (m > best) {
+            best = m;
+            sc_best = sc;
+        }
     }
-    uint64_t key = (bi >= 0) ? rank_key(best, (uint32_t)bi) : 0ull;
-    key = wave_max_u64(key);
+    bool nan = magf > 0x7f800000u;
+    if constexpr (sizeof(T) == 2)
+        nan |= mag[0] > 0x7f80 || mag[1] > 0x7f80;
+
+    // block maximum M and NaN flag
+    const float wm = wave_max_f32(best);
     const uint32_t wn = __ballot(nan) != 0ull;
     if (lane == 0) {
-        wkey[wid] = key;
+        reinterpret_cast<float *>(wkey)[wid] = wm;
         wnan[wid] = wn;
     }
     __syncthreads();
-    if (tid == 0) {
-        uint64_t k = wkey[0];
-        uint32_t n = wnan[0];
+    float M = reinterpret_cast<const float *>(wkey)[0];
+    uint32_t bn = wnan[0];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) {
-            k = max(k, wkey[w]);
-            n |= wnan[w];
+    for (int w = 1; w < NW; ++w) {
+        M = fmaxf(M, reinterpret_cast<const float *>(wkey)[w]);
+        bn |= wnan[w];
+    }
+    // first index of M among the threads that reached it
+    int first = INT_MAX;
+    if (sc_best >= 0 && best == M) {
+        if (sc_best != sc1 - 1)  // else its words are still in registers
+            load_sub(sc_best, u);
+        const int64_t base = (int64_t)sc_best * kArgSub;
+#pragma unroll
+        for (int i = L - 1; i >= 0; --i) {
+            const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
+            float x[E];
+            unpack(u[i], x);
+#pragma unroll
+            for (int k = E - 1; k >= 0; --k)
+                if (e0 + k < V && x[k] == M)
+                    first = (int)(e0 + k);
         }
-        ws_keys[vb] = k;
-        ws_nan[vb] = n;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        first = min(first, __shfl_xor(first, o, kWave));
+    __syncthreads();  // every thread has read M from the slice
+    if (lane == 0)
+        reinterpret_cast<int *>(wkey)[wid] = first;
+    __syncthreads();
+    if (tid == 0) {
+        int f = reinterpret_cast<const int *>(wkey)[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            f = min(f, reinterpret_cast<const int *>(wkey)[w]);
+        const int64_t f0 = (int64_t)sc0 * kArgSub;
+        uint64_t key;
+        if (f != INT_MAX)
+            key = rank_key(M, (uint32_t)f);
+        else
+            key = f0 < V ? rank_key(-INFINITY, (uint32_t)f0) : 0ull;
+        ws_keys[vb] = key;
+        ws_nan[vb] = bn;
     }
 }
 
