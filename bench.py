@@ -51,8 +51,12 @@ KERNELS = {
     "mask": ["build_mask_kernel"],
     "attention": ["attn_bf16_kernel", "attn_combine_kernel", "attn_simple_kernel"],
     "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
-    "step": ["step_phase1", "step_phase2"],
+    "step": ["step_phase1", "step_scan_kernel", "step_phase2"],
 }
+# the kernel whose dispatches count the launches of each entry point
+MARKER = {"topw": "topw_partial_kernel", "mask": "build_mask_kernel",
+          "attention": ("attn_bf16_kernel", "attn_simple_kernel"),
+          "verify": "argmax_partial_kernel", "step": "step_phase2"}
 
 
 def algorithmic(w):
@@ -367,14 +371,22 @@ def _counter_rows(path, counter):
 
 
 def traffic_summarize(name, fetch_dir, write_dir):
-    """Per entry point, HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE) KiB summed over the
-    entry point's kernels, divided by its launch count, each counter scaled by
-    (bytes the calibration copy moved) / (what the counter read for it)."""
+    """Per entry point, HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE) KiB over the entry
+    point's dispatches, divided by its launch count, each counter scaled by (bytes the
+    calibration copy moved) / (what the counter read for it).  The traffic run launches the
+    entry points one after the other (top-W, mask, attention, verify, then the fused step,
+    whose 8-wave shapes also run attn_bf16_kernel), so dispatches are assigned in order."""
+    order = list(CALLS) + ["step"]
+    def hits(kname, call):
+        return any(k in kname for k in KERNELS[call])
+    def is_marker(kname, call):
+        m = MARKER[call]
+        return any(k in kname for k in (m if isinstance(m, tuple) else (m,)))
     out = {"counters": {}}
     per = {}
     for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(path, counter)
-        ours = [r for r in rows if any(k in r[1] for ks in KERNELS.values() for k in ks)]
+        ours = [r for r in rows if any(hits(r[1], c) for c in order)]
         last = max(r[0] for r in ours)
         calib = [r for r in rows if r[0] > last and "copyBuffer" in r[1]]
         if not calib:
@@ -382,15 +394,21 @@ def traffic_summarize(name, fetch_dir, write_dir):
         kib = sum(r[2] for r in calib)
         factor = CALIB_BYTES / (kib * 1024.0)
         out["counters"][counter] = {"calibration_kib": kib, "scale": factor}
-        for call, ks in KERNELS.items():
-            first = [r for r in ours if ks[0] in r[1] or (call == "attention" and ks[2] in r[1])]
-            if call == "attention":  # the fused step's phase kernels inline attn_* code only
-                first = [r for r in first if "step_phase" not in r[1]]
-            tot = sum(r[2] for r in ours if any(k in r[1] for k in ks))
-            n = len(first)
-            if n:
-                per.setdefault(call, {})[counter] = tot * 1024.0 * factor / n
-                per[call]["launches"] = n
+        cur = 0
+        tot = {c: 0.0 for c in order}
+        cnt = {c: 0 for c in order}
+        for did, kname, val in ours:
+            for k in range(cur + 1, len(order)):
+                if hits(kname, order[k]):
+                    cur = k
+                    break
+            call = order[cur]
+            tot[call] += val
+            cnt[call] += 1 if is_marker(kname, call) else 0
+        for call in order:
+            if cnt[call]:
+                per.setdefault(call, {})[counter] = tot[call] * 1024.0 * factor / cnt[call]
+                per[call]["launches"] = cnt[call]
     out["entries"] = {}
     for call, d in per.items():
         if "FETCH_SIZE" in d and "WRITE_SIZE" in d:
@@ -473,7 +491,8 @@ def main():
     dom = dominant(prim)
     c = prim["w"].cfg
     fused = prim.get("fused_us") is not None
-    timing = ("hipGraph replay of one jt_draft_verify_step (two launches) per cold input set"
+    timing = ("hipGraph replay of one jt_draft_verify_step (two kernel launches; three when "
+              "attention runs 8-wave groups) per cold input set"
               if fused else "hipGraph replay of one step per cold input set; top-W and "
               "verification on side streams")
     line = {

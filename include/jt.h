@@ -192,8 +192,11 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
  * documented above, in two kernel launches instead of seven: the bandwidth-bound logit
  * scans (top-W partials, target arg-max partials), the mask and the attention's main pass
  * share the first launch; the split-KV merge, the top-W merge and the verification walk
- * share the second.  The attention builds the ancestor rows it needs from `parent`
- * itself, so it does not wait for the mask.  Every output equals what the four separate
+ * share the second.  When a KV group holds more than 128 query rows (G*B > 128), the
+ * attention runs 256-row workgroups whose LDS leaves no room beside them, and the scans
+ * and the mask take a launch of their own before it (three launches).  In the two-launch
+ * form the attention builds the ancestor rows it needs from `parent` itself, so it does
+ * not wait for the mask.  Every output equals what the four separate
  * calls produce; `err` (int32 [S], optional) receives the OR of the flags the mask,
  * attention and verification calls would report.
  *

@@ -74,3 +74,17 @@ def test_config_draft_logits(name):
 def test_config_unplanted_ties():
     w = wl.make("moe_verify", 203, parts=("draft",), plant=False, S=4)
     _check(w.draft_logits, 8, what="unplanted")
+
+
+@pytest.mark.parametrize("W", [4, 5, 9, 16])
+def test_long_rows_rank_paths(W):
+    """Rows of 151936 logits (75 partial lists, two list heads per lane in the merge).  A
+    constant row and a heavily tied row put more than 64 keys at or above the merge's
+    bound for W >= 9; a row whose largest logits all sit in one list puts the bound on
+    that list's head."""
+    rng = np.random.default_rng(77 + W)
+    x = wl.to_dtype(rng.normal(0, 3, (4, 151936)).astype(np.float32), "bf16")
+    x[1] = wl.scalar_in_dtype(1.5, "bf16")
+    x[2, ::13] = wl.scalar_in_dtype(40.0, "bf16")
+    x[3, 7 * 2048 + 3: 7 * 2048 + 43] = wl.scalar_in_dtype(50.0, "bf16")
+    _check(x, W, what=f"long rows W={W}")

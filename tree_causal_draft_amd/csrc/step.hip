@@ -125,8 +125,7 @@ __global__ void __launch_bounds__(256) step_scan_kernel(StepArgs sa, StepPlan sp
 template <int D, int NB>
 __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
 {
-    __shared__ uint64_t mkeys[kStepRowsPerBlock][kMergeCand];
-    __shared__ uint64_t mtop[kStepRowsPerBlock][JT_MAX_W];
+    __shared__ __attribute__((aligned(16))) uint64_t mkeys[kStepRowsPerBlock][kMergeLds];
     // the per-row and per-sequence roles first: they are the longer ones
     int b = blockIdx.x;
     if (b < sp.nW) {
@@ -141,7 +140,7 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
         const int r = b * kStepRowsPerBlock + wid;
         if (r < sa.S * sa.N)
             topw_merge_row(r, sa.W, sp.tp.nlist, sa.tkeys, sa.tms, sa.ids, sa.logprob, sa.row_lse,
-                           mkeys[wid], mtop[wid]);
+                           mkeys[wid]);
         return;
     }
     b -= sp.nR;

@@ -367,17 +367,43 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
 }
 
 constexpr int kMergeCand = JT_MAX_W * JT_MAX_W;  // candidate keys a row merge can keep
+constexpr int kMergeLds = kMergeCand + 8;          // LDS keys per merging wave (8 of padding)
 
-// One wave per row: merge the partial lists and (max, sum) pairs of row r.  With at most 8
-// keys per lane, W rounds of a DPP wave max run straight over the registers.  Otherwise:
-// every list is sorted descending, so the W-th largest list head bounds the row's W-th
-// largest key from below, and only keys at or above it (at most W per list with a head
-// there, W * W in all) compete.  They are compacted into `keys` (kMergeCand entries of this wave's LDS) and W
-// rounds of a DPP wave max pick the W largest -- over registers when at most 64 compete.
+// For each of a lane's K keys, the number of entries of keys[0..n) greater than it.  n is a
+// multiple of 8 (the caller pads with zero keys) and keys is 16-byte aligned.  Every lane
+// reads the same entries, so each read is an LDS broadcast.  (Issuing the next reads
+// before comparing the current ones measured slower: more registers and copies.)
+template <int K>
+__device__ __forceinline__ void count_greater(const uint64_t *keys, int n, const uint64_t (&mine)[K],
+                                              int (&cnt)[K])
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        cnt[k] = 0;
+#pragma unroll 4
+    for (int i = 0; i < n; i += 2) {
+        const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(keys + i);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            cnt[k] += (p.x > mine[k] ? 1 : 0) + (p.y > mine[k] ? 1 : 0);
+    }
+}
+
+// One wave per row: merge the partial lists and (max, sum) pairs of row r.  Every list is
+// sorted descending and nonzero keys are unique, so the W-th largest list head bounds the
+// row's W-th largest key from below: only keys at or above it compete, at most W from
+// each of the W lists whose head reaches it (all keys compete when there are at most W
+// lists).  Selection is by rank: a key's place in the output is the number of competing
+// keys above it, counted over LDS broadcast reads, first for the list heads (the head
+// ranked W - 1 is the bound), then for the competitors.  `keys`: kMergeLds entries of
+// this wave's LDS, 16-byte aligned.
+//
+// With at most 8 keys per lane and W <= 4, W rounds of a DPP wave max straight over the
+// registers are cheaper than the two counting passes, and are used instead.
 __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
                                const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
                                float *__restrict__ logprob, float *__restrict__ row_lse,
-                               uint64_t *keys, uint64_t *top)
+                               uint64_t *keys)
 {
     const int lane = threadIdx.x & 63;
     const int n = nchunk * W;
@@ -432,9 +458,8 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
     else
         lse = m + logf(s);
 
-    if (nq <= 8) {
-        // few keys per lane: W rounds straight over the registers, each taking the largest
-        // key below the previous winner
+    if (nq <= 8 && W <= 4) {
+        // W rounds, each taking the largest key below the previous winner
         uint64_t prev = ~0ull, mine_top = 0ull;
         for (int k = 0; k < W; ++k) {
             uint64_t mine = 0ull;
@@ -455,22 +480,32 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
             row_lse[r] = lse;
         return;
     }
-    // threshold: the W-th largest head (keys are unique; 0 = empty), 0 if fewer than W
+    // bound: the head ranked W - 1 (0 when there are at most W lists)
     uint64_t tau = 0ull;
-    for (int k = 0; k < W; ++k) {
-        uint64_t mine = hd[0];
-#pragma unroll
-        for (int j = 1; j < kMsPerLane; ++j)
-            mine = hd[j] > mine ? hd[j] : mine;
-        const uint64_t K = wave_max_u64_dpp(mine);
-        tau = K;
-        if (K == 0ull)
-            break;
+    if (nchunk > W) {
 #pragma unroll
         for (int j = 0; j < kMsPerLane; ++j)
-            hd[j] = hd[j] == K ? 0ull : hd[j];
+            if (lane + kWave * j < nchunk)
+                keys[lane + kWave * j] = hd[j];
+        if (lane < 8)
+            keys[nchunk + lane] = 0ull;  // pad to a multiple of 8
+        wave_sync();
+        int cnt[kMsPerLane];
+        count_greater<kMsPerLane>(keys, (nchunk + 7) & ~7, hd, cnt);
+        uint64_t t = 0ull;
+#pragma unroll
+        for (int j = 0; j < kMsPerLane; ++j)
+            if (hd[j] != 0ull && cnt[j] == W - 1)
+                t = hd[j];
+        const uint64_t own = __ballot(t != 0ull);
+        if (own) {
+            const int src_lane = (int)__builtin_ctzll(own);
+            tau = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(t >> 32), src_lane) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)t, src_lane);
+        }
+        wave_sync();  // the heads are overwritten by the competitors
     }
-    // candidates: nonzero keys >= tau, compacted slot by slot (slots no lane needs skipped)
+    // competitors: nonzero keys >= tau, compacted slot by slot (slots no lane needs skipped)
     uint32_t mk = 0u;
 #pragma unroll
     for (int q = 0; q < kKeysPerLane; ++q)
@@ -490,24 +525,34 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
             nc += __popcll(b);
         }
     }
+    if (nc > kMergeCand)
+        nc = kMergeCand;  // not reached: at most W * W keys reach the bound
+    if (lane < 8)
+        keys[nc + lane] = 0ull;  // pad to a multiple of 8
     wave_sync();
-    uint64_t mine_top = 0ull;
-    if (nc <= kWave) {
-        uint64_t v = lane < nc ? keys[lane] : 0ull;
-        for (int k = 0; k < W; ++k) {
-            const uint64_t K = wave_max_u64_dpp(v);
-            if (lane == k)
-                mine_top = K;
-            if (v == K)
-                v = 0ull;
+    const int ne = (nc + 7) & ~7;
+    auto emit = [&](uint64_t k, int rank) {
+        if (k != 0ull && rank < W) {
+            ids[(int64_t)r * W + rank] = (int32_t)key_id(k);
+            logprob[(int64_t)r * W + rank] = key_value(k) - lse;
         }
+    };
+    if (nc <= kWave) {
+        const uint64_t mine[1] = {lane < nc ? keys[lane] : 0ull};
+        int cnt[1];
+        count_greater<1>(keys, ne, mine, cnt);
+        emit(mine[0], cnt[0]);
     } else {
-        wave_select_topw(keys, nc < kMergeCand ? nc : kMergeCand, W, top);
-        mine_top = lane < W ? top[lane] : 0ull;
-    }
-    if (lane < W) {
-        ids[(int64_t)r * W + lane] = (int32_t)key_id(mine_top);
-        logprob[(int64_t)r * W + lane] = key_value(mine_top) - lse;
+        constexpr int K = kMergeCand / kWave;
+        uint64_t mine[K];
+#pragma unroll
+        for (int q = 0; q < K; ++q)
+            mine[q] = lane + kWave * q < nc ? keys[lane + kWave * q] : 0ull;
+        int cnt[K];
+        count_greater<K>(keys, ne, mine, cnt);
+#pragma unroll
+        for (int q = 0; q < K; ++q)
+            emit(mine[q], cnt[q]);
     }
     if (lane == 0 && row_lse)
         row_lse[r] = lse;
@@ -518,9 +563,8 @@ topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_k
                   const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
                   float *__restrict__ logprob, float *__restrict__ row_lse)
 {
-    __shared__ uint64_t keys[kMergeCand];
-    __shared__ uint64_t top[JT_MAX_W];
-    topw_merge_row(blockIdx.x, W, nchunk, ws_keys, ws_ms, ids, logprob, row_lse, keys, top);
+    __shared__ __attribute__((aligned(16))) uint64_t keys[kMergeLds];
+    topw_merge_row(blockIdx.x, W, nchunk, ws_keys, ws_ms, ids, logprob, row_lse, keys);
 }
 
 struct TopwPlan {
