@@ -11,13 +11,13 @@
 //   * a piece is pulled into registers with 16-byte loads (32 logits per lane; the next
 //     piece's loads are issued before the current one is processed) and reduced there:
 //     lane max, then sum of exp(x - max) (exact per-lane rescale);
-//   * elements become 64-bit keys (order code << 32 | ~id): value descending, id
-//     ascending in one integer compare, so bf16 ties resolve exactly like a full sort;
-//     each lane keeps its two largest keys (a pairwise tree, no LDS), and W rounds of a
-//     DPP wave max over the lanes' offers extract the W largest, merged on the fly with
-//     the wave's running list from its earlier pieces;
+//   * only logits at or above a threshold (a lower bound on the piece's W-th largest)
+//     become 64-bit keys (order code << 32 | ~id): value descending, id ascending in one
+//     integer compare, so bf16 ties resolve exactly like a full sort; W rounds of a DPP
+//     wave max over them and the wave's running list give the new list;
 //   * a merge kernel (one wave per row) combines the per-wave top-W lists and the
-//     (max, sum-exp) pairs into ids, log-probs and the row log-sum-exp.
+//     (max, sum-exp) pairs into ids, log-probs and the row log-sum-exp, selecting by
+//     rank counts.
 #include "jt_internal.h"
 
 namespace jt {
