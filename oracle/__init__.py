@@ -187,3 +187,38 @@ def verify_greedy(target_logits, parent, tokens, N: int, V=None):
     if rc:
         raise ValueError(f"jto_verify_greedy rc={rc}")
     return out
+
+
+def build_tree(ids, logprob, N: int, B: int, *, entropy=None, w_lp: float = 1.0,
+               w_ent: float = 0.0, root_token=None):
+    """Best-first tree construction from per-depth candidate lists.
+
+    ``ids`` int32 and ``logprob`` float32, [S*N, W] (row s*N + d: the candidates for
+    depth d + 1 of sequence s); ``entropy`` float32 [S*N] or None.  Scores are float32.
+    Returns dict(parent [S,B], tokens [S,B], score [S,B] float32, n_nodes [S]).
+    """
+    ids = _c(ids, np.int32)
+    logprob = _c(logprob, np.float32)
+    rows, W = ids.shape
+    if logprob.shape != ids.shape:
+        raise ValueError("ids and logprob differ in shape")
+    if N < 1 and rows:
+        raise ValueError("rows given but N < 1")
+    S = rows // N if N >= 1 else 0
+    if S * N != rows:
+        raise ValueError("rows is not a multiple of N")
+    ent = None if entropy is None else _c(entropy, np.float32).reshape(-1)
+    root = None if root_token is None else _c(root_token, np.int32).reshape(-1)
+    out = dict(parent=np.zeros((S, B), np.int32), tokens=np.zeros((S, B), np.int32),
+               score=np.zeros((S, B), np.float32), n_nodes=np.zeros(S, np.int32))
+    lib = _load()
+    lib.jto_build_tree.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int] + \
+        [ctypes.c_void_p] * 4
+    rc = lib.jto_build_tree(_p(ids), _p(logprob), _p(ent), w_lp, w_ent, _p(root), S, N, W, B,
+                            _p(out["parent"]), _p(out["tokens"]), _p(out["score"]),
+                            _p(out["n_nodes"]))
+    if rc:
+        raise ValueError(f"jto_build_tree rc={rc}")
+    return out

@@ -21,6 +21,9 @@
  *    (paperlayer.ai JetSpec summary, appendix E "Verification").
  *  - per-position top-k tokens and log-probabilities (same page, appendix E
  *    "Drafting"); top-W per depth (paper.rainbus.top summary, method steps).
+ *  - best-first tree construction by cumulative path score from the per-depth
+ *    candidate lists (paperlayer.ai JetSpec summary, appendix B; review,
+ *    inference, path-score equation; paper.rainbus.top summary, method steps).
  *  - acceptance of the longest valid prefix plus a bonus token (paperlayer.ai
  *    JetSpec summary section 2; JetSpec++ summary section 3); at temperature 0
  *    the min(1, p/q) rule of the review's inference section reduces to
@@ -35,7 +38,9 @@
  *  - top-W order is value descending, token id ascending; -0 equals +0;
  *    NaN ranks below -inf;
  *  - argmax ties go to the lowest token id; NaN entries are skipped and flagged;
- *  - among accepted nodes the deepest wins, ties to the lowest node index.
+ *  - among accepted nodes the deepest wins, ties to the lowest node index;
+ *  - tree construction pops ties in node-index order, accumulates scores in
+ *    float (they decide integers), and pads unfilled slots (parent 0, token -1).
  */
 #include <math.h>
 #include <stdint.h>
@@ -416,5 +421,107 @@ int jto_verify_greedy(const void *target_logits, int64_t row_stride, int V, int 
         bonus[s] = am[best_v];
         err[s] = flags;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------- tree construction -- */
+
+/*
+ * Does node (a, ia) leave the queue before node (b, ib)?  Larger score first,
+ * then the lower node index; a NaN score ranks below every other score (the
+ * top-W reading).  -0 equals +0.
+ */
+static int pops_before(float a, int ia, float b, int ib)
+{
+    int an = isnan(a), bn = isnan(b);
+    if (an != bn)
+        return bn;
+    if (!an && a != b)
+        return a > b;
+    return ia < ib;
+}
+
+/*
+ * Best-first construction of the draft tree from the per-depth candidate lists
+ * (paperlayer.ai JetSpec summary, appendix B "Tree-Drafting Algorithm Details"
+ * and appendix E "Drafting"; review of JetSpec, "inference", the path-score
+ * equation; paper.rainbus.top summary, method steps).  The root (node 0, depth
+ * 0, score 0) starts in the queue.  Repeatedly the queued node that pops first
+ * (pops_before) leaves the queue; a node at depth N is not expanded; otherwise
+ * it gains up to W children, rank r = 0..W-1 in order, while the tree holds
+ * fewer than B nodes.  Child r of a node at depth d carries token ids[d][r] of
+ * its sequence (row d gives the candidates for depth d+1, shared by every node
+ * at depth d) and the score
+ *     score(parent) + (w_lp * logprob[d][r] - w_ent * entropy[d]),
+ * each product, the difference and the sum rounded to float in that order (the
+ * scores decide integers, so they are accumulated in the precision the device
+ * path uses).  w_lp = 1, w_ent = 0 is the cumulative log-probability of the
+ * path; w_lp = 0, w_ent = 1 scores by per-depth entropy alone; w_lp = 1,
+ * w_ent = alpha is the hybrid (appendix C of the same summary names all three;
+ * the combination is a reading).  entropy may be NULL (taken as 0).
+ * Construction ends when B nodes exist or the queue is empty; then slots
+ * n..B-1 are padding: parent 0, token -1, score -inf.
+ *
+ *   ids, logprob  [S*N, W]     entropy [S*N] or NULL   root_token [S] or NULL (-1)
+ *   parent, tokens [S, B]      score [S, B] or NULL     n_nodes [S] or NULL
+ */
+int jto_build_tree(const int32_t *ids, const float *logprob, const float *entropy,
+                   float w_lp, float w_ent, const int32_t *root_token, int S, int N,
+                   int W, int B, int32_t *parent, int32_t *tokens, float *score,
+                   int32_t *n_nodes)
+{
+    if (S < 0 || N < 0 || W < 1 || B < 1)
+        return 2;
+    float *sc = (float *)malloc(sizeof(float) * (size_t)B);
+    int *dep = (int *)malloc(sizeof(int) * (size_t)B);
+    int *queued = (int *)malloc(sizeof(int) * (size_t)B);
+    if (!sc || !dep || !queued) {
+        free(sc); free(dep); free(queued);
+        return 3;
+    }
+    for (int s = 0; s < S; s++) {
+        int32_t *par = parent + (int64_t)s * B, *tok = tokens + (int64_t)s * B;
+        par[0] = -1;
+        tok[0] = root_token ? root_token[s] : -1;
+        sc[0] = 0.0f;
+        dep[0] = 0;
+        queued[0] = 1;
+        int n = 1;
+        while (n < B) {
+            int v = -1;
+            for (int i = 0; i < n; i++)
+                if (queued[i] && (v < 0 || pops_before(sc[i], i, sc[v], v)))
+                    v = i;
+            if (v < 0)
+                break;
+            queued[v] = 0;
+            if (dep[v] >= N)
+                continue;
+            const int64_t row = (int64_t)s * N + dep[v];
+            const float h = entropy ? entropy[row] : 0.0f;
+            const float eterm = w_ent * h;
+            for (int r = 0; r < W && n < B; r++) {
+                const float lterm = w_lp * logprob[row * W + r];
+                const float inc = lterm - eterm;
+                par[n] = v;
+                tok[n] = ids[row * W + r];
+                dep[n] = dep[v] + 1;
+                sc[n] = sc[v] + inc;
+                queued[n] = 1;
+                n++;
+            }
+        }
+        if (n_nodes)
+            n_nodes[s] = n;
+        for (int i = n; i < B; i++) {
+            par[i] = 0;
+            tok[i] = -1;
+            sc[i] = -INFINITY;
+        }
+        if (score)
+            for (int i = 0; i < B; i++)
+                score[(int64_t)s * B + i] = sc[i];
+    }
+    free(sc); free(dep); free(queued);
     return 0;
 }

@@ -1,0 +1,180 @@
+"""Pins for the oracle's best-first tree construction (CPU only).
+
+The draft tree grows best-first: the queued node with the highest path score is
+popped and gains up to W children until the node budget B is spent; nodes at depth
+N are not expanded; a child's score adds its candidate's log-probability to its
+parent's (paperlayer.ai JetSpec summary, appendix B and section 2; JetSpec review,
+inference, path-score equation; paper.rainbus.top summary, method steps).  Every
+node at depth d draws its children from the one candidate list of depth d + 1
+(paperlayer.ai JetSpec summary, appendix E "Drafting").
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    with open(os.path.join(GOLD, "bestfirst_hand.json")) as fh:
+        return json.load(fh)
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_hand_worked_cases(k):
+    g = _golden()
+    c = g["cases"][k]
+    o = oracle.build_tree(np.array(g["ids"]), np.array(g["logprob"], np.float32), g["N"],
+                          c["B"], entropy=c["entropy"], w_lp=c["w_lp"], w_ent=c["w_ent"],
+                          root_token=[g["root_token"]])
+    want = [float("-inf") if x == "-inf" else x for x in c["score"]]
+    assert o["parent"][0].tolist() == c["parent"], c["why"]
+    assert o["tokens"][0].tolist() == c["tokens"], c["why"]
+    assert o["score"][0].tolist() == want, c["why"]
+    assert int(o["n_nodes"][0]) == c["n_nodes"], c["why"]
+
+
+def _by_global_sort(ids, lp, N, W, B, root):
+    """The same tree by a different route, for distinct scores: scores only fall along a
+    path (log-probabilities are <= 0), so best-first pops every node after its parent
+    and in score order.  Enumerate the complete W-ary tree below depth N, sort the nodes
+    of depth < N by score, and give the children of the k-th of them the next indices,
+    in rank order, until B nodes exist."""
+    nodes = [((), np.float32(0.0))]          # (path of ranks, score)
+    frontier = [nodes[0]]
+    for d in range(N):
+        nxt = []
+        for path, sc in frontier:
+            for r in range(W):
+                nxt.append((path + (r,), np.float32(sc + np.float32(lp[d, r]))))
+        nodes += nxt
+        frontier = nxt
+    scores = [float(sc) for _, sc in nodes]
+    assert len(set(scores)) == len(scores), "scores must be distinct for this pin"
+    expand = sorted((n for n in nodes if len(n[0]) < N), key=lambda n: -float(n[1]))
+    index = {(): 0}
+    parent, tokens, score = [-1], [root], [0.0]
+    for path, sc in expand:
+        if len(parent) >= B:
+            break
+        for r in range(W):
+            if len(parent) >= B:
+                break
+            child = path + (r,)
+            index[child] = len(parent)
+            parent.append(index[path])
+            tokens.append(int(ids[len(path), r]))
+            score.append(float(np.float32(sc + np.float32(lp[len(path), r]))))
+    n = len(parent)
+    parent += [0] * (B - n)
+    tokens += [-1] * (B - n)
+    score += [float("-inf")] * (B - n)
+    return parent, tokens, score, n
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_matches_global_sort_on_small_trees(seed):
+    rng = np.random.default_rng(seed)
+    W = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 5))
+    full = sum(W ** d for d in range(N + 1))
+    B = int(rng.integers(1, full + 3))
+    lp = (-rng.exponential(1.0, (N, W))).astype(np.float32)
+    lp = -np.sort(-lp, axis=1)                      # a top-W list is sorted descending
+    ids = rng.integers(0, 1000, (N, W)).astype(np.int32)
+    try:
+        want = _by_global_sort(ids, lp, N, W, B, 7)
+    except AssertionError:
+        pytest.skip("tied scores in this draw")
+    o = oracle.build_tree(ids, lp, N, B, root_token=[7])
+    assert o["parent"][0].tolist() == want[0]
+    assert o["tokens"][0].tolist() == want[1]
+    assert o["score"][0].tolist() == want[2]
+    assert int(o["n_nodes"][0]) == want[3] == min(B, full)
+
+
+def _check_invariants(ids, lp, N, W, B, o, ent=None, w_lp=1.0, w_ent=0.0):
+    S = o["parent"].shape[0]
+    for s in range(S):
+        par, tok, sc, n = o["parent"][s], o["tokens"][s], o["score"][s], int(o["n_nodes"][s])
+        depth = np.zeros(B, np.int64)
+        for i in range(1, n):
+            assert 0 <= par[i] < i
+            depth[i] = depth[par[i]] + 1
+            assert depth[i] <= N
+        # children of one parent are contiguous, in rank order, with that depth's candidates
+        expanded = []
+        i = 1
+        while i < n:
+            p = par[i]
+            j = i
+            while j < n and par[j] == p:
+                j += 1
+            assert p not in expanded, "a node expanded twice"
+            expanded.append(p)
+            row = s * N + depth[p]
+            e = np.float32(0.0) if ent is None else np.float32(ent[row])
+            for r in range(j - i):
+                assert tok[i + r] == ids[row, r]
+                inc = np.float32(np.float32(w_lp) * lp[row, r]) - np.float32(np.float32(w_ent) * e)
+                assert sc[i + r] == np.float32(sc[p] + np.float32(inc))
+            assert j - i == W or j == n      # only the last expansion may be cut short
+            i = j
+        # expansions leave the queue in (score desc, index asc) order
+        keys = [(-float(sc[p]), p) for p in expanded]
+        assert keys == sorted(keys)
+        # nothing left unexpanded above depth N pops before the last expansion
+        if n == B and expanded:
+            last = keys[-1]
+            for v in range(n):
+                if v not in expanded and depth[v] < N:
+                    assert (-float(sc[v]), v) > last
+        if n < B:
+            assert all(depth[v] == N or v in expanded for v in range(n))
+            assert (par[n:] == 0).all() and (tok[n:] == -1).all() and np.isneginf(sc[n:]).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_invariants_with_ties(seed):
+    """Candidate log-probs from a small set of dyadic values: many equal scores."""
+    rng = np.random.default_rng(100 + seed)
+    S, N, W = 3, int(rng.integers(1, 9)), int(rng.integers(1, 17))
+    B = int(rng.integers(1, 257))
+    vals = np.array([-0.0, -0.25, -0.5, -1.0, -2.0], np.float32)
+    lp = -np.sort(-rng.choice(vals, (S * N, W)), axis=1).astype(np.float32)
+    ids = rng.integers(0, 151936, (S * N, W)).astype(np.int32)
+    o = oracle.build_tree(ids, lp, N, B)
+    _check_invariants(ids, lp, N, W, B, o)
+    ent = rng.choice(np.array([0.0, 0.5, 1.5], np.float32), S * N)
+    o = oracle.build_tree(ids, lp, N, B, entropy=ent, w_lp=1.0, w_ent=0.5)
+    _check_invariants(ids, lp, N, W, B, o, ent, 1.0, 0.5)
+
+
+def test_sequences_use_their_own_lists():
+    rng = np.random.default_rng(3)
+    N, W, B = 4, 3, 30
+    lp = -np.sort(rng.exponential(1.0, (2 * N, W)), axis=1).astype(np.float32)
+    ids = rng.integers(0, 100, (2 * N, W)).astype(np.int32)
+    both = oracle.build_tree(ids, lp, N, B, root_token=[1, 2])
+    for s in range(2):
+        one = oracle.build_tree(ids[s * N:(s + 1) * N], lp[s * N:(s + 1) * N], N, B,
+                                root_token=[s + 1])
+        for k in ("parent", "tokens", "score", "n_nodes"):
+            assert np.array_equal(both[k][s], one[k][0])
+
+
+def test_degenerate_shapes():
+    ids = np.array([[4, 5]], np.int32)
+    lp = np.array([[-1.0, -2.0]], np.float32)
+    o = oracle.build_tree(ids, lp, 1, 1)             # budget 1: the root alone
+    assert o["parent"].tolist() == [[-1]] and int(o["n_nodes"][0]) == 1
+    o = oracle.build_tree(ids[:, :1], lp[:, :1], 1, 4)   # W = 1, N = 1: root and one child
+    assert o["parent"].tolist() == [[-1, 0, 0, 0]] and o["tokens"].tolist() == [[-1, 4, -1, -1]]
+    # W = 1 is a chain down to depth N
+    o = oracle.build_tree(np.arange(6, dtype=np.int32)[:, None], np.full((6, 1), -0.5, np.float32),
+                          6, 10)
+    assert o["parent"][0, :7].tolist() == [-1, 0, 1, 2, 3, 4, 5] and int(o["n_nodes"][0]) == 7
