@@ -52,11 +52,12 @@ KERNELS = {
     "attention": ["attn_bf16_kernel", "attn_combine_kernel", "attn_simple_kernel"],
     "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
     "step": ["step_phase1", "step_scan_kernel", "step_phase2"],
+    "tree": ["tree_build_kernel"],
 }
 # the kernel whose dispatches count the launches of each entry point
 MARKER = {"topw": "topw_partial_kernel", "mask": "build_mask_kernel",
           "attention": ("attn_bf16_kernel", "attn_simple_kernel"),
-          "verify": "argmax_partial_kernel", "step": "step_phase2"}
+          "verify": "argmax_partial_kernel", "step": "step_phase2", "tree": "tree_build_kernel"}
 
 
 def algorithmic(w):
@@ -75,6 +76,9 @@ def algorithmic(w):
     vis = (P[:, None] + w.depth.astype(np.int64) + 1).sum()
     flops = 4 * c.Hq * c.d * int(vis)
     b["step"] = b["topw"] + b["mask"] + b["attention"] + b["verify"]
+    # best-first tree from the top-W lists: ids + log-probs read; parent, tokens, score
+    # and the node count written
+    b["tree"] = S * N * W * 8 + S * B * 12 + S * 4
     return b, flops
 
 
@@ -216,7 +220,9 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
     import torch
     # ---- each entry point alone: one graph of nsets launches (one per cold input set)
     per_call_us = {}
-    calls_here = CALLS + (("step",) if hasattr(st, "step_ws") else ())
+    calls_here = CALLS + (("step",) if hasattr(st, "step_ws") else ()) + \
+        (("tree",) if hasattr(st, "tree_parent") else ())
+    st.topw()  # the tree call reads the top-W lists
     for c in calls_here:
         g = _capture([getattr(s, "run_fused" if c == "step" else c) for s in rot.steps])
         per_call_us[c], _ = _time_graph(g, nsets, steps, warmup)
@@ -298,7 +304,8 @@ def _kernel_hash(call):
     import hashlib
     files = {"topw": ["topw.hip"], "mask": ["mask.hip"], "attention": ["attn.hip"],
              "verify": ["verify.hip"],
-             "step": ["mask.hip", "topw.hip", "verify.hip", "attn.hip", "step.hip"]}[call]
+             "step": ["mask.hip", "topw.hip", "verify.hip", "attn.hip", "step.hip"],
+             "tree": ["tree.hip"]}[call]
     import re
     h = hashlib.sha256()
     for f in files + ["jt_internal.h"]:
@@ -346,7 +353,7 @@ def traffic_run(name, seed, reps=3, log=print):
     st = DeviceStep(w, "cuda:0")
     nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(footprint(st), 1))))
     rot = Rotation(st, nsets)
-    for c in CALLS + (("run_fused",) if hasattr(st, "step_ws") else ()):
+    for c in CALLS + (("run_fused",) if hasattr(st, "step_ws") else ()) + ("tree",):
         for i in range(reps * nsets):
             getattr(rot.steps[i % nsets], c)()
         torch.cuda.synchronize()
@@ -381,7 +388,7 @@ def traffic_summarize(name, fetch_dir, write_dir):
     calibration copy moved) / (what the counter read for it).  The traffic run launches the
     entry points one after the other (top-W, mask, attention, verify, then the fused step,
     whose 8-wave shapes also run attn_bf16_kernel), so dispatches are assigned in order."""
-    order = list(CALLS) + ["step"]
+    order = list(CALLS) + ["step", "tree"]
     def hits(kname, call):
         return any(k in kname for k in KERNELS[call])
     def is_marker(kname, call):

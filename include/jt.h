@@ -225,6 +225,38 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
                                int32_t *err, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/*
+ * Best-first construction of the draft tree from the per-depth candidate lists that
+ * jt_topw_per_depth produces (paperlayer.ai JetSpec summary, appendix B "Tree-Drafting
+ * Algorithm Details", section 2 and appendix E "Drafting"; JetSpec review, inference,
+ * path-score equation; paper.rainbus.top summary, method steps).  Per sequence: node 0
+ * is the root (depth 0, score 0, token root_token[s]); the queued node that pops first --
+ * larger score, then lower node index, a NaN score last -- leaves the queue; a node at
+ * depth N is not expanded; otherwise it gains children of rank r = 0..W-1 in order while
+ * the tree holds fewer than B nodes.  Child r of a node at depth d carries token
+ * ids[s*N + d][r] and the score
+ *     score(parent) + (w_lp * logprob[s*N + d][r] - w_ent * entropy[s*N + d]),
+ * each product, the difference and the sum rounded to float in turn (no fused
+ * multiply-add).  w_lp = 1, w_ent = 0 scores by the path's cumulative draft
+ * log-probability; w_lp = 0, w_ent = 1 by per-depth entropy alone; w_lp = 1, w_ent =
+ * alpha is the hybrid.  When the queue empties before B nodes exist, slots n..B-1 are
+ * padding: parent 0, token -1, score -inf (a node that can never be accepted).
+ *
+ *   ids, logprob  [S*N, W] int32 / float32 (row s*N + d: the candidates of depth d+1)
+ *   entropy       [S*N] float32, or NULL (taken as 0)
+ *   root_token    [S] int32, or NULL (root token -1)
+ *   parent, tokens [S, B] int32 out: parent[s,0] = -1 and 0 <= parent[s,i] < i, the
+ *                 layout the mask, attention and verification calls take
+ *   score         [S, B] float32 out, or NULL      n_nodes [S] int32 out, or NULL
+ * Supported: 1 <= W <= 16, 1 <= B <= 256, 0 <= N <= 255.  No workspace; one wave per
+ * sequence.
+ */
+jt_status jt_build_tree_best_first(const int32_t *ids, const float *logprob,
+                                   const float *entropy, float w_lp, float w_ent,
+                                   const int32_t *root_token, int32_t S, int32_t N, int32_t W,
+                                   int32_t B, int32_t *parent, int32_t *tokens, float *score,
+                                   int32_t *n_nodes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

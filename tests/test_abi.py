@@ -70,6 +70,15 @@ def test_host_validation_returns_before_launch():
                                   nul, nul, nul, 0, nul)
     assert ver(N=256) == 2
     assert ver() == 1
+    # tree construction: W, B, N out of range, NULLs, empty batch
+    def tree(S=1, N=4, W=2, B=16):
+        return L.jt_build_tree_best_first(nul, nul, nul, ctypes.c_float(1.0), ctypes.c_float(0.0),
+                                          nul, S, N, W, B, nul, nul, nul, nul, nul)
+    assert tree(W=0) == 2 and tree(W=17) == 2
+    assert tree(B=0) == 2 and tree(B=257) == 2
+    assert tree(N=-1) == 2 and tree(N=256) == 2
+    assert tree() == 1
+    assert tree(S=0) == 0
 
 
 def test_workspace_queries_are_pure():

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tree_util import check_invariants as _check_invariants
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -95,47 +96,6 @@ def test_matches_global_sort_on_small_trees(seed):
     assert o["tokens"][0].tolist() == want[1]
     assert o["score"][0].tolist() == want[2]
     assert int(o["n_nodes"][0]) == want[3] == min(B, full)
-
-
-def _check_invariants(ids, lp, N, W, B, o, ent=None, w_lp=1.0, w_ent=0.0):
-    S = o["parent"].shape[0]
-    for s in range(S):
-        par, tok, sc, n = o["parent"][s], o["tokens"][s], o["score"][s], int(o["n_nodes"][s])
-        depth = np.zeros(B, np.int64)
-        for i in range(1, n):
-            assert 0 <= par[i] < i
-            depth[i] = depth[par[i]] + 1
-            assert depth[i] <= N
-        # children of one parent are contiguous, in rank order, with that depth's candidates
-        expanded = []
-        i = 1
-        while i < n:
-            p = par[i]
-            j = i
-            while j < n and par[j] == p:
-                j += 1
-            assert p not in expanded, "a node expanded twice"
-            expanded.append(p)
-            row = s * N + depth[p]
-            e = np.float32(0.0) if ent is None else np.float32(ent[row])
-            for r in range(j - i):
-                assert tok[i + r] == ids[row, r]
-                inc = np.float32(np.float32(w_lp) * lp[row, r]) - np.float32(np.float32(w_ent) * e)
-                assert sc[i + r] == np.float32(sc[p] + np.float32(inc))
-            assert j - i == W or j == n      # only the last expansion may be cut short
-            i = j
-        # expansions leave the queue in (score desc, index asc) order
-        keys = [(-float(sc[p]), p) for p in expanded]
-        assert keys == sorted(keys)
-        # nothing left unexpanded above depth N pops before the last expansion
-        if n == B and expanded:
-            last = keys[-1]
-            for v in range(n):
-                if v not in expanded and depth[v] < N:
-                    assert (-float(sc[v]), v) > last
-        if n < B:
-            assert all(depth[v] == N or v in expanded for v in range(n))
-            assert (par[n:] == 0).all() and (tok[n:] == -1).all() and np.isneginf(sc[n:]).all()
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -23,7 +23,7 @@ DEV_BAD_PARENT, DEV_DEPTH_GT_N, DEV_BAD_BLOCK, DEV_NAN, DEV_BAD_PREFIX = 1, 2, 4
 EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
            "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
            "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy",
-           "jt_step_workspace_size", "jt_draft_verify_step")
+           "jt_step_workspace_size", "jt_draft_verify_step", "jt_build_tree_best_first")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -67,8 +67,10 @@ def lib() -> ctypes.CDLL:
             [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _i32] + [_vp] * 6 +
             [_i32, _i32, _i32, _vp] + [_i32] * 4 + [ctypes.c_float, ctypes.c_int] + [_vp] * 13 +
             [_sz, _vp])
+        L.jt_build_tree_best_first.argtypes = ([_vp] * 3 + [ctypes.c_float] * 2 + [_vp] +
+                                               [_i32] * 4 + [_vp] * 5)
         for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
-                   "jt_verify_greedy", "jt_draft_verify_step"):
+                   "jt_verify_greedy", "jt_draft_verify_step", "jt_build_tree_best_first"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -283,3 +285,36 @@ def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tr
     return dict(ids=ids, logprob=logprob, row_lse=row_lse, anc=anc, depth=depth, out=out,
                 lse=lse, accept_len=accept_len, accept_path=accept_path, bonus=bonus,
                 argmax=argmax_out, err=err)
+
+
+def build_tree_best_first(ids, logprob, N, B, *, entropy=None, w_lp=1.0, w_ent=0.0,
+                          root_token=None, parent=None, tokens=None, score=None, n_nodes=None,
+                          stream=None):
+    """Best-first draft tree from the per-depth top-W lists.
+
+    ids int32 / logprob float32 [S*N, W] (as jt_topw_per_depth returns them), entropy
+    float32 [S*N] or None, root_token int32 [S] or None.  Returns (parent, tokens, score,
+    n_nodes): int32 [S,B], int32 [S,B], float32 [S,B], int32 [S].
+    """
+    _need(ids, "ids")
+    _need(logprob, "logprob")
+    if ids.dtype != torch.int32 or logprob.dtype != torch.float32:
+        raise JTError("ids must be int32 and logprob float32")
+    rows, W = ids.shape
+    if tuple(logprob.shape) != (rows, W) or N < 1 or rows % N:
+        raise JTError("ids / logprob must be [S*N, W] with N >= 1")
+    S = rows // N
+    dev = ids.device
+    for t, n in ((entropy, "entropy"), (root_token, "root_token")):
+        if t is not None:
+            _need(t, n)
+    parent = torch.empty((S, B), dtype=torch.int32, device=dev) if parent is None else parent
+    tokens = torch.empty((S, B), dtype=torch.int32, device=dev) if tokens is None else tokens
+    score = torch.empty((S, B), dtype=torch.float32, device=dev) if score is None else score
+    n_nodes = torch.empty(S, dtype=torch.int32, device=dev) if n_nodes is None else n_nodes
+    _check(lib().jt_build_tree_best_first(_ptr(ids), _ptr(logprob), _ptr(entropy), float(w_lp),
+                                          float(w_ent), _ptr(root_token), S, N, W, B,
+                                          _ptr(parent), _ptr(tokens), _ptr(score),
+                                          _ptr(n_nodes), _stream(stream)),
+           "jt_build_tree_best_first")
+    return parent, tokens, score, n_nodes

@@ -334,4 +334,20 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
     return launch_step(in, workspace, as_stream(stream));
 }
 
+jt_status jt_build_tree_best_first(const int32_t *ids, const float *logprob,
+                                   const float *entropy, float w_lp, float w_ent,
+                                   const int32_t *root_token, int32_t S, int32_t N, int32_t W,
+                                   int32_t B, int32_t *parent, int32_t *tokens, float *score,
+                                   int32_t *n_nodes, void *stream)
+{
+    if (S < 0 || N < 0 || N > 255 || W < 1 || W > JT_MAX_W || B < 1 || B > JT_MAX_NODES)
+        return JT_ERR_SHAPE;
+    if (S == 0)
+        return JT_OK;
+    if (!parent || !tokens || (N > 0 && (!ids || !logprob)))
+        return JT_ERR_NULL;
+    return launch_build_tree(ids, logprob, entropy, w_lp, w_ent, root_token, S, N, W, B, parent,
+                             tokens, score, n_nodes, as_stream(stream));
+}
+
 } // extern "C"

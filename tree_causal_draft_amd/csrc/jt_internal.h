@@ -143,6 +143,11 @@ struct StepLaunch {
     int32_t *depth;
     int32_t *accept_len, *accept_path, *bonus, *argmax_out, *err;
 };
+jt_status launch_build_tree(const int32_t *ids, const float *logprob, const float *entropy,
+                            float w_lp, float w_ent, const int32_t *root_token, int S, int N,
+                            int W, int B, int32_t *parent, int32_t *tokens, float *score,
+                            int32_t *n_nodes, hipStream_t st);
+
 size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d, int max_prefix,
                       int block_size);
 jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st);

@@ -6,3 +6,4 @@
 #include "verify.hip"
 #include "attn.hip"
 #include "step.hip"
+#include "tree.hip"

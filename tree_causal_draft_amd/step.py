@@ -5,14 +5,16 @@
 Used by the benchmark, the smoke check and the tests.  Nothing here computes: it moves a
 seeded workload (numpy) to device memory, preallocates every output and workspace, and
 calls the libjt entry points in stream order.  The tree (parent, tokens) is an input of
-the step, built by the workload generator.
+the step, built by the workload generator; tree() builds the best-first tree of the
+step's top-W lists on the device into separate buffers.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from . import (build_tree_mask, draft_verify_step, step_workspace_size, topw_per_depth,
+from . import (build_tree_best_first, build_tree_mask, draft_verify_step, step_workspace_size,
+               topw_per_depth,
                tree_attention, tree_attention_workspace_size, topw_workspace_size, verify_greedy,
                verify_workspace_size, JT_BF16, JT_F32)
 from .workload import Workload
@@ -62,6 +64,11 @@ class DeviceStep:
             self.row_lse = torch.empty(S * N, dtype=torch.float32, device=dev)
             nb = topw_workspace_size(S * N, cfg.V, W, dt)
             self.topw_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+            # the best-first tree of the top-W lists (kept apart from the step's own tree)
+            self.tree_parent = torch.empty((S, B), dtype=torch.int32, device=dev)
+            self.tree_tokens = torch.empty((S, B), dtype=torch.int32, device=dev)
+            self.tree_score = torch.empty((S, B), dtype=torch.float32, device=dev)
+            self.tree_n = torch.empty(S, dtype=torch.int32, device=dev)
         if "verify" in parts:
             self.target = to_device(w.target_logits, dev)
             self.accept_len = torch.empty(S, dtype=torch.int32, device=dev)
@@ -82,6 +89,12 @@ class DeviceStep:
     def topw(self):
         topw_per_depth(self.draft, self.cfg.W, ids=self.ids, logprob=self.logprob,
                        row_lse=self.row_lse, workspace=self.topw_ws)
+
+    def tree(self):
+        """Best-first tree construction from this step's top-W lists (not part of run())."""
+        build_tree_best_first(self.ids, self.logprob, self.cfg.N, self.cfg.B,
+                              parent=self.tree_parent, tokens=self.tree_tokens,
+                              score=self.tree_score, n_nodes=self.tree_n)
 
     def mask(self):
         build_tree_mask(self.parent, self.anc, self.depth, self.err_mask)
