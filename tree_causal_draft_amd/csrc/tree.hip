@@ -11,11 +11,12 @@
 // One wave per sequence.  The queue is never materialised as a heap: lane L keeps the
 // score, depth and queued bit of nodes L, L+64, L+128, L+192 in registers, and a pop is
 // one wave-wide maximum of 32-bit order codes (DPP) followed by at most four ballots that
-// find the lowest node index holding it.  The owners of the new children compute their
-// scores themselves from the increment table in LDS, so a pop moves no data between
-// lanes beyond the popped node's score and depth.  Pops are inherently sequential (a
-// child may outrank every queued node), so the kernel is bound by the latency of one
-// pop, about a hundred dependent instructions.
+// find the lowest node index holding it.  An expansion creates at most 16 children, so
+// each lane owns at most one of them and computes its score itself from the increment
+// table in LDS: a pop moves no data between lanes beyond the popped node's score and
+// depth.  Parent and token stay in registers until the end.  Pops are inherently
+// sequential (a child may outrank every queued node), so the kernel is bound by the
+// latency of one pop, about a hundred dependent instructions (0.3 us measured).
 #include "jt_internal.h"
 
 namespace jt {
@@ -71,36 +72,30 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
         inc[i] = tree_increment(a.w_lp, a.logprob[tb + i], a.w_ent, h);
         cid[i] = a.ids[tb + i];
     }
-    int32_t *par = a.parent + (int64_t)s * B;
-    int32_t *tok = a.tokens + (int64_t)s * B;
-    if (lane == 0) {
-        par[0] = -1;
-        tok[0] = a.root_token ? a.root_token[s] : -1;
-    }
     __syncthreads();
 
+    // lane state: node lane + 64k in slot k -- score, depth, pop key (0: not queued),
+    // parent and token (stored once at the end)
     float sc[kTreeSlots];
-    int dp[kTreeSlots];
-    bool q[kTreeSlots];
+    int dp[kTreeSlots], pa[kTreeSlots], tk[kTreeSlots];
+    uint32_t key[kTreeSlots];
 #pragma unroll
     for (int k = 0; k < kTreeSlots; ++k) {
         sc[k] = -INFINITY;
         dp[k] = 0;
-        q[k] = false;
+        pa[k] = 0;
+        tk[k] = -1;
+        key[k] = 0u;
     }
     if (lane == 0) {
         sc[0] = 0.f;
-        q[0] = true;
+        pa[0] = -1;
+        tk[0] = a.root_token ? a.root_token[s] : -1;
+        key[0] = tree_key(true, 0.f);
     }
     int n = 1;
     while (n < B) {
-        uint32_t key[kTreeSlots], mine = 0u;
-#pragma unroll
-        for (int k = 0; k < kTreeSlots; ++k) {
-            key[k] = tree_key(q[k], sc[k]);
-            mine = max(mine, key[k]);
-        }
-        const uint32_t M = wave_max_u32(mine);
+        const uint32_t M = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
         if (M == 0u)
             break;  // queue empty
         // the lowest node index holding M: slot k first (lower k, lower index), then lane
@@ -126,41 +121,49 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
             }
         const float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sel), ln));
         const int dv = __builtin_amdgcn_readlane(d_sel, ln);
+        if (lane == ln) {
 #pragma unroll
-        for (int k = 0; k < kTreeSlots; ++k)
-            if (k == kk && lane == ln)
-                q[k] = false;
+            for (int k = 0; k < kTreeSlots; ++k)
+                if (k == kk)
+                    key[k] = 0u;
+        }
         if (dv >= N)
             continue;  // at the depth limit: popped, not expanded
+        // children n .. n+cnt-1; cnt <= 16, so a lane receives at most one of them
         const int cnt = min(W, B - n);
-        const int row = dv * W;
+        const int r = (lane - n) & (kWave - 1);
+        if (r < cnt) {
+            const int e = dv * W + r;
+            const float cs = tree_add(sv, inc[e]);
+            const int ct = cid[e];
+            const int k = (n + r) >> 6;
+            const uint32_t ck = tree_key(true, cs);
 #pragma unroll
-        for (int k = 0; k < kTreeSlots; ++k) {
-            const int idx = lane + kWave * k;
-            const int r = idx - n;
-            if (r >= 0 && r < cnt) {
-                sc[k] = tree_add(sv, inc[row + r]);
-                dp[k] = dv + 1;
-                q[k] = true;
-                par[idx] = v;
-                tok[idx] = cid[row + r];
-            }
+            for (int q = 0; q < kTreeSlots; ++q)
+                if (q == k) {
+                    sc[q] = cs;
+                    dp[q] = dv + 1;
+                    key[q] = ck;
+                    pa[q] = v;
+                    tk[q] = ct;
+                }
         }
         n += cnt;
     }
     if (lane == 0 && a.n_nodes)
         a.n_nodes[s] = n;
+    int32_t *par = a.parent + (int64_t)s * B;
+    int32_t *tok = a.tokens + (int64_t)s * B;
 #pragma unroll
     for (int k = 0; k < kTreeSlots; ++k) {
         const int idx = lane + kWave * k;
         if (idx >= B)
             continue;
-        if (idx >= n) {
-            par[idx] = 0;
-            tok[idx] = -1;
-        }
+        // slots at or past n keep their initial padding: parent 0, token -1, score -inf
+        par[idx] = pa[k];
+        tok[idx] = tk[k];
         if (a.score)
-            a.score[(int64_t)s * B + idx] = idx < n ? sc[k] : -INFINITY;
+            a.score[(int64_t)s * B + idx] = sc[k];
     }
 }
 
