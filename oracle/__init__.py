@@ -136,8 +136,10 @@ def tree_attention(q, k_tree, v_tree, k_prefix, v_prefix, prefix_len, parent, *,
     return out, lse, err
 
 
-def topw(logits, W: int, rows: int | None = None, V: int | None = None, row_stride=None):
-    """Per-row top-W ids (value desc, id asc), fp64 log-probs and row LSE.
+def topw(logits, W: int, rows: int | None = None, V: int | None = None, row_stride=None,
+         entropy: bool = False):
+    """Per-row top-W ids (value desc, id asc), fp64 log-probs and row LSE (and, with
+    ``entropy=True``, the row's softmax entropy as a fourth result).
 
     ``logits`` is a 2-D array [rows, row_stride]; ``V`` defaults to its width.
     """
@@ -150,14 +152,16 @@ def topw(logits, W: int, rows: int | None = None, V: int | None = None, row_stri
     ids = np.zeros((rows, W), np.int32)
     lp = np.zeros((rows, W), np.float64)
     lse = np.zeros(rows, np.float64)
+    ent = np.zeros(rows, np.float64) if entropy else None
     lib = _load()
     lib.jto_topw.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                              ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                             ctypes.c_void_p]
-    rc = lib.jto_topw(_p(logits), row_stride, rows, V, W, dt, _p(ids), _p(lp), _p(lse))
+                             ctypes.c_void_p, ctypes.c_void_p]
+    rc = lib.jto_topw(_p(logits), row_stride, rows, V, W, dt, _p(ids), _p(lp), _p(lse),
+                      _p(ent))
     if rc:
         raise ValueError(f"jto_topw rc={rc}")
-    return ids, lp, lse
+    return (ids, lp, lse, ent) if entropy else (ids, lp, lse)
 
 
 def verify_greedy(target_logits, parent, tokens, N: int, V=None):

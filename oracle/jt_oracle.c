@@ -285,13 +285,37 @@ static int item_cmp(const void *pa, const void *pb)
 }
 
 /*
+ * Entropy of the row's softmax distribution, H = -sum_t p_t log p_t with
+ * log p_t = x_t - lse (the per-depth entropy that entropy-guided and hybrid
+ * scoring rank by: paperlayer.ai JetSpec summary, appendices C and E).  Terms
+ * with p_t = 0 contribute 0 (the limit).  NaN if the row holds a NaN; 0 for a
+ * row whose every entry is -inf (lse = -inf: no distribution, read as a point).
+ */
+static double row_entropy(const ora_item *it, int V, double L)
+{
+    if (isnan(L))
+        return NAN;
+    if (L == -INFINITY)
+        return 0.0;
+    double H = 0.0;
+    for (int t = 0; t < V; t++) {
+        const double lp = it[t].x - L;
+        const double p = exp(lp);
+        if (p > 0.0)
+            H -= p * lp;
+    }
+    return H;
+}
+
+/*
  * Per row: the W largest logits in (value desc, id asc) order, by a full sort
  * of the row; lse = m + log(sum exp(x - m)) over the whole row (m = row max);
- * logprob = x - lse.  Row r starts at logits + r*row_stride elements.
- * A row whose finite maximum is -inf has lse = -inf.
+ * logprob = x - lse; entropy (optional) as row_entropy.  Row r starts at
+ * logits + r*row_stride elements.  A row whose finite maximum is -inf has
+ * lse = -inf.
  */
 int jto_topw(const void *logits, int64_t row_stride, int rows, int V, int W,
-             int dtype, int32_t *ids, double *logprob, double *lse)
+             int dtype, int32_t *ids, double *logprob, double *lse, double *entropy)
 {
     if (rows < 0 || V < 1 || W < 1 || W > V || row_stride < V)
         return 2;
@@ -321,6 +345,8 @@ int jto_topw(const void *logits, int64_t row_stride, int rows, int V, int W,
         }
         if (lse)
             lse[r] = L;
+        if (entropy)
+            entropy[r] = row_entropy(it, V, L);
         qsort(it, (size_t)V, sizeof(ora_item), item_cmp);
         for (int w = 0; w < W; w++) {
             ids[(int64_t)r * W + w] = it[w].i;

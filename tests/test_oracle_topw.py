@@ -88,3 +88,53 @@ def test_row_stride_and_sub_vocab():
     for r in range(4):
         assert ids[r].tolist() == _brute(big[r, :40], 3)
         np.testing.assert_allclose(lse[r], logsumexp(big[r, :40].astype(np.float64)), rtol=1e-14)
+
+
+# ---- row entropy: H = -sum p log p of the row's softmax (the per-depth entropy that
+# entropy-guided and hybrid tree scoring rank by; paperlayer.ai JetSpec summary,
+# appendices C and E)
+
+def test_entropy_uniform_row_is_log_v():
+    for V in (1, 7, 1000, 151936):
+        x = np.full((1, V), 0.75, np.float32)
+        *_, H = oracle.topw(x, 1, entropy=True)
+        assert abs(H[0] - np.log(V)) <= 1e-12 * max(1.0, np.log(V))
+
+
+def test_entropy_two_way_tie_and_point_mass():
+    x = np.full((3, 50), -np.inf, np.float32)
+    x[0, [3, 41]] = 2.0                 # two equal entries, the rest -inf: ln 2
+    x[1, 17] = -5.0                     # a single finite entry: 0
+    *_, H = oracle.topw(x, 1, entropy=True)
+    assert abs(H[0] - np.log(2.0)) < 1e-15 and H[1] == 0.0
+    assert H[2] == 0.0                  # every entry -inf: no distribution, read as a point
+    y = np.zeros((1, 10), np.float32)
+    y[0, 4] = np.nan
+    *_, H = oracle.topw(y, 1, entropy=True)
+    assert np.isnan(H[0])
+
+
+def test_entropy_geometric_row_closed_form():
+    """x_t = -beta t, t < V: p_t = (1-q) q^t / (1-q^V) with q = e^-beta, so
+    H = -log((1-q)/(1-q^V)) + beta E[t],  E[t] = q/(1-q) - V q^V/(1-q^V)."""
+    for beta, V in ((0.5, 64), (0.03125, 4096), (2.0, 11)):
+        t = np.arange(V, dtype=np.float64)
+        x = (-beta * t).astype(np.float32)
+        assert np.array_equal(x.astype(np.float64), -beta * t)   # exact in float
+        q = np.exp(-beta)
+        Et = q / (1 - q) - V * q ** V / (1 - q ** V)
+        want = -np.log((1 - q) / (1 - q ** V)) + beta * Et
+        *_, H = oracle.topw(x[None, :], 1, entropy=True)
+        assert abs(H[0] - want) <= 1e-10 * max(1.0, want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_entropy_matches_scipy(dtype):
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    rng = np.random.default_rng(41)
+    x = wl.to_dtype(rng.normal(0, 3, (5, 3001)).astype(np.float32), dtype)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64) if dtype == "bf16" else x.astype(np.float64)
+    *_, H = oracle.topw(x, 2, entropy=True)
+    for r in range(5):
+        assert abs(H[r] - entropy(softmax(xf[r]))) <= 1e-10
