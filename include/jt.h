@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define JT_ABI_VERSION 1
+#define JT_ABI_VERSION 2
 
 typedef enum {
     JT_OK = 0,
@@ -146,13 +146,18 @@ jt_status jt_tree_attention(const void *q, const void *k_tree, const void *v_tre
  *   logprob   float [rows,W] out: logit - row_lse.
  *   row_lse   float [rows] (optional) out: log sum_t exp(logit_t) over the whole row
  *             (NaN if the row holds a NaN, -inf if every entry is -inf).
+ *   row_entropy float [rows] (optional) out: the entropy -sum_t p_t log p_t of the row's
+ *             softmax, computed in the same pass (the per-depth entropy that
+ *             entropy-guided and hybrid tree scoring rank by: paperlayer.ai JetSpec
+ *             summary, appendices C and E); NaN for a row holding a NaN, 0 for a row of
+ *             -inf.  Leaving it NULL skips the extra sums.
  * Supported: rows >= 0, 1 <= W <= min(16, V), V < 2^31, row_stride >= V.
  */
 size_t jt_topw_workspace_size(int32_t rows, int32_t V, int32_t W, jt_dtype dtype);
 jt_status jt_topw_per_depth(const void *logits, int64_t row_stride, int32_t rows, int32_t V,
                             int32_t W, jt_dtype dtype, int32_t *ids, float *logprob,
-                            float *row_lse, void *workspace, size_t workspace_bytes,
-                            void *stream);
+                            float *row_lse, float *row_entropy, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /*
  * Step 4 -- greedy tree verification.
@@ -196,13 +201,17 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
  * attention runs 256-row workgroups whose LDS leaves no room beside them, and the scans
  * and the mask take a launch of their own before it (three launches).  In the two-launch
  * form the attention builds the ancestor rows it needs from `parent` itself, so it does
- * not wait for the mask.  Every output equals what the four separate
- * calls produce; `err` (int32 [S], optional) receives the OR of the flags the mask,
+ * not wait for the mask.  The integer outputs (ids, anc, depth, the accepted path, bonus,
+ * arg-max) and the attention outputs equal bit for bit what the four separate calls
+ * produce; logprob, row_lse and row_entropy agree to float rounding, because the step
+ * may cut a logit row into pieces differently from jt_topw_per_depth (the sums then add
+ * in another order).  `err` (int32 [S], optional) receives the OR of the flags the mask,
  * attention and verification calls would report.
  *
  *   draft_logits   [S*N, draft_row_stride]   target_logits [S*B, target_row_stride]
  *   (both dtype, V used columns, 16-byte aligned with row strides a multiple of 8)
  *   W, N           as for jt_topw_per_depth (rows = S*N) and jt_verify_greedy
+ *   row_entropy    optional, as for jt_topw_per_depth
  *   attention args as for jt_tree_attention (anc is produced here)
  * Supported: dtype JT_BF16 only; d in {64, 128}; the ranges of the four calls.  Anything
  * else returns JT_ERR_DTYPE / JT_ERR_ALIGN / JT_ERR_SHAPE: use the four calls instead.
@@ -219,7 +228,8 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
                                int32_t max_blocks_per_seq, int32_t block_size,
                                int32_t num_blocks, const int32_t *prefix_len, int32_t max_prefix,
                                int32_t Hq, int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
-                               int32_t *ids, float *logprob, float *row_lse, uint64_t *anc,
+                               int32_t *ids, float *logprob, float *row_lse,
+                               float *row_entropy, uint64_t *anc,
                                int32_t *depth, void *out, float *lse, int32_t *accept_len,
                                int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
                                int32_t *err, void *workspace, size_t workspace_bytes,

@@ -59,5 +59,9 @@ def assert_attention_close(got, ref, dtype, what=""):
 def assert_lp_close(got, ref, what=""):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    bad = np.abs(got - ref) > LP_ATOL + LP_RTOL * np.abs(ref)
-    assert not bad.any(), f"{what}: max err {np.abs(got - ref).max():.3e}"
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{what}: NaN positions differ"
+    ok = ~np.isnan(ref)
+    g, r = got[ok], ref[ok]
+    same_inf = np.isinf(r) & (g == r)
+    bad = ~same_inf & ~(np.abs(g - r) <= LP_ATOL + LP_RTOL * np.abs(r))
+    assert not bad.any(), f"{what}: max err {np.nanmax(np.abs(g - r)) if g.size else 0:.3e}"

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = jt.lib()
-    assert L.jt_abi_version() == 1
+    assert L.jt_abi_version() == 2
     assert L.jt_status_string(0) == b"ok"
     assert b"NULL" in L.jt_status_string(1)
     assert L.jt_status_string(99) == b"unknown status"
@@ -48,7 +48,7 @@ def test_host_validation_returns_before_launch():
     assert L.jt_build_tree_mask(nul, 0, 16, nul, nul, nul, nul) == 0   # empty batch: no-op
     # top-W: W > 16, W > V, bad dtype, stride < V, NULLs
     args = lambda rows, V, W, dt, stride=None: (nul, stride or V, rows, V, W, dt, nul, nul, nul,
-                                                 nul, 0, nul)
+                                                 nul, nul, 0, nul)
     assert L.jt_topw_per_depth(*args(4, 100, 17, 1)) == 2
     assert L.jt_topw_per_depth(*args(4, 3, 4, 1)) == 2
     assert L.jt_topw_per_depth(*args(4, 100, 4, 7)) == 3

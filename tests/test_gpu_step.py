@@ -1,9 +1,11 @@
-"""GPU parity of jt_draft_verify_step (the four steps in two launches).
+"""GPU parity of jt_draft_verify_step (the four steps in two or three launches).
 
-The fused call must reproduce, bit for bit, every output of the four separate calls on the
-same inputs (those are held to the oracle by the other GPU tests), and its err must be the
-OR of their flags.  One case is also compared with the oracle directly.  Attention outputs
-of a sequence with a bad parent array are unspecified and are not compared.
+The fused call must reproduce, bit for bit, every integer and attention output of the
+four separate calls on the same inputs (those are held to the oracle by the other GPU
+tests), and its err must be the OR of their flags.  Log-probs and row LSE agree to the
+log-prob tolerance: the step may cut a row into pieces differently, so its sums add in
+another order.  One case is also compared with the oracle directly.  Attention outputs of
+a sequence with a bad parent array are unspecified and are not compared.
 """
 import numpy as np
 import pytest
@@ -12,13 +14,14 @@ import torch
 import oracle
 from tree_causal_draft_amd import workload as wl
 from tree_causal_draft_amd.step import DeviceStep
-from gpu_util import BF16_ATOL, BF16_RTOL, LP_ATOL, LP_RTOL, host, need_gpu
+from gpu_util import BF16_ATOL, BF16_RTOL, LP_ATOL, LP_RTOL, assert_lp_close, host, need_gpu
 
 pytestmark = pytest.mark.gpu
 
 OUTS = ("ids", "logprob", "row_lse", "anc", "depth", "accept_len", "accept_path", "bonus",
         "argmax", "attn_out", "lse")
 ATTN = ("attn_out", "lse")
+SUMS = ("logprob", "row_lse")  # float sums over a logit row
 
 
 def _bits(t):
@@ -45,6 +48,9 @@ def _compare(w, what, tamper=None):
     assert torch.equal(st.err_step, err_sep), (what, host(st.err_step), host(err_sep))
     bad_parent = (err_sep & 1) != 0
     for k in OUTS:
+        if k in SUMS:
+            assert_lp_close(host(getattr(st, k)), host(sep[k]), f"{what} {k}")
+            continue
         a, b = _bits(getattr(st, k)), _bits(sep[k])
         if k in ATTN and bool(bad_parent.any()):
             keep = ~bad_parent
@@ -140,3 +146,20 @@ def test_rejects_fp32_and_misaligned_rows():
         jt.draft_verify_step(shifted, st.target, st.parent, st.tokens, w.cfg.N, w.cfg.W, st.q,
                              st.k_tree, st.v_tree, st.k_prefix, st.v_prefix, st.prefix_len,
                              workspace=st.step_ws)
+
+
+@pytest.mark.parametrize("name", ["low_budget", "high_budget"])
+def test_fused_entropy_against_oracle(name):
+    """row_entropy from the step's own top-W pass, against the oracle's softmax entropy."""
+    need_gpu()
+    import tree_causal_draft_amd as jt
+    w = wl.make(name, 818, V=151936, plant=False)
+    c = w.cfg
+    st = DeviceStep(w, "cuda:0")
+    ent = torch.empty(c.S * c.N, dtype=torch.float32, device="cuda:0")
+    jt.draft_verify_step(st.draft, st.target, st.parent, st.tokens, c.N, c.W, st.q, st.k_tree,
+                         st.v_tree, st.k_prefix, st.v_prefix, st.prefix_len,
+                         max_prefix=w.max_prefix, workspace=st.step_ws, row_entropy=ent)
+    torch.cuda.synchronize()
+    *_, r_ent = oracle.topw(w.draft_logits, c.W, entropy=True)
+    assert_lp_close(host(ent), r_ent, name)

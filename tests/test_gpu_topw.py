@@ -16,12 +16,19 @@ def _check(logits, W, V=None, what=""):
     rows, stride = logits.shape
     V = stride if V is None else V
     print(f"[topw] {what} rows={rows} V={V} stride={stride} W={W} {logits.dtype}", flush=True)
-    ids, lp, lse = jt.topw_per_depth(dev(logits), W, V=V)
+    x = dev(logits)
+    ids, lp, lse = jt.topw_per_depth(x, W, V=V)
+    ent = torch.empty(rows, dtype=torch.float32, device=x.device)
+    ids2, lp2, lse2 = jt.topw_per_depth(x, W, V=V, row_entropy=ent)
     torch.cuda.synchronize()
-    r_ids, r_lp, r_lse = oracle.topw(logits, W, V=V)
+    r_ids, r_lp, r_lse, r_ent = oracle.topw(logits, W, V=V, entropy=True)
     assert np.array_equal(host(ids), r_ids), what
     assert_lp_close(host(lp), r_lp, what)
     assert_lp_close(host(lse), r_lse, what)
+    # asking for the entropy changes nothing else, bit for bit
+    for a, b in ((ids, ids2), (lp, lp2), (lse, lse2)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), what
+    assert_lp_close(host(ent), r_ent, what + " entropy")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -58,11 +65,13 @@ def test_neg_inf_rows():
     x = np.full((2, 5000), -np.inf, np.float32)
     x[1, 4000] = 1.0
     need_gpu()
-    ids, lp, lse = jt.topw_per_depth(dev(x), 3)
+    ent = torch.empty(2, dtype=torch.float32, device="cuda:0")
+    ids, lp, lse = jt.topw_per_depth(dev(x), 3, row_entropy=ent)
     torch.cuda.synchronize()
-    r_ids, _, r_lse = oracle.topw(x, 3)
+    r_ids, _, r_lse, r_ent = oracle.topw(x, 3, entropy=True)
     assert np.array_equal(host(ids), r_ids)
     assert np.array_equal(np.isneginf(host(lse)), np.isneginf(r_lse))
+    assert np.array_equal(host(ent), r_ent)  # 0 for the row of -inf, 0 for the point mass
 
 
 @pytest.mark.parametrize("name", ["tiny", "low_budget", "high_budget", "ragged", "moe_verify"])
@@ -88,3 +97,10 @@ def test_long_rows_rank_paths(W):
     x[2, ::13] = wl.scalar_in_dtype(40.0, "bf16")
     x[3, 7 * 2048 + 3: 7 * 2048 + 43] = wl.scalar_in_dtype(50.0, "bf16")
     _check(x, W, what=f"long rows W={W}")
+
+
+def test_entropy_nan_and_uniform_rows():
+    x = np.zeros((3, 151936), np.float32)
+    x[1, 77] = np.nan                    # a NaN: NaN entropy
+    x[2, :5] = 30.0                      # five equal maxima far above the rest: ~ln 5
+    _check(wl.to_dtype(x, "bf16"), 4, what="nan / uniform / 5-way")

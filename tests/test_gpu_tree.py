@@ -137,3 +137,25 @@ def test_composed_with_device_topw(name):
     out = dict(parent=host(par), tokens=host(tok), score=host(sc), n_nodes=host(n))
     check_invariants(host(ids), host(lp), c.N, c.W, c.B, out)
     assert (out["n_nodes"] == c.B).all()
+
+
+@pytest.mark.parametrize("name", ["low_budget", "high_budget"])
+def test_hybrid_tree_from_device_entropy(name):
+    """Entropy from the device top-W pass feeding hybrid and entropy-only scoring: the
+    entropy matches the oracle's, and each tree is a valid best-first tree of its score."""
+    need_gpu()
+    w = wl.make(name, 703, parts=("draft",), plant=False)
+    c = w.cfg
+    x = dev(w.draft_logits)
+    ent = torch.empty(c.S * c.N, dtype=torch.float32, device=x.device)
+    ids, lp, _ = jt.topw_per_depth(x, c.W, row_entropy=ent)
+    *_, r_ent = oracle.topw(w.draft_logits, c.W, entropy=True)
+    torch.cuda.synchronize()
+    from gpu_util import assert_lp_close
+    assert_lp_close(host(ent), r_ent, name)
+    for w_lp, w_ent in ((1.0, 0.5), (0.0, 1.0)):
+        par, tok, sc, n = jt.build_tree_best_first(ids, lp, c.N, c.B, entropy=ent, w_lp=w_lp,
+                                                   w_ent=w_ent)
+        torch.cuda.synchronize()
+        out = dict(parent=host(par), tokens=host(tok), score=host(sc), n_nodes=host(n))
+        check_invariants(host(ids), host(lp), c.N, c.W, c.B, out, host(ent), w_lp, w_ent)

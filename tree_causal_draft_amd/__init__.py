@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.jt_topw_workspace_size.restype = _sz
         L.jt_topw_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
         L.jt_topw_per_depth.argtypes = [_vp, _i64, _i32, _i32, _i32, ctypes.c_int, _vp, _vp, _vp,
-                                        _vp, _sz, _vp]
+                                        _vp, _vp, _sz, _vp]
         L.jt_verify_workspace_size.restype = _sz
         L.jt_verify_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
         L.jt_verify_greedy.argtypes = ([_vp, _i64, _i32, ctypes.c_int] + [_vp] * 4 +
@@ -65,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.jt_step_workspace_size.argtypes = [_i32] * 10 + [ctypes.c_int]
         L.jt_draft_verify_step.argtypes = (
             [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _i32] + [_vp] * 6 +
-            [_i32, _i32, _i32, _vp] + [_i32] * 4 + [ctypes.c_float, ctypes.c_int] + [_vp] * 13 +
+            [_i32, _i32, _i32, _vp] + [_i32] * 4 + [ctypes.c_float, ctypes.c_int] + [_vp] * 14 +
             [_sz, _vp])
         L.jt_build_tree_best_first.argtypes = ([_vp] * 3 + [ctypes.c_float] * 2 + [_vp] +
                                                [_i32] * 4 + [_vp] * 5)
@@ -172,8 +172,11 @@ def topw_workspace_size(rows, V, W, dtype) -> int:
 
 
 def topw_per_depth(logits, W, *, V=None, ids=None, logprob=None, row_lse=None, workspace=None,
-                   want_lse=True, stream=None):
-    """logits [rows, row_stride] -> (ids int32 [rows,W], logprob fp32 [rows,W], row_lse)."""
+                   want_lse=True, row_entropy=None, stream=None):
+    """logits [rows, row_stride] -> (ids int32 [rows,W], logprob fp32 [rows,W], row_lse).
+
+    ``row_entropy``: an fp32 [rows] tensor to receive each row's softmax entropy, or None.
+    """
     _need(logits, "logits")
     rows, stride = logits.shape
     V = stride if V is None else V
@@ -185,7 +188,8 @@ def topw_per_depth(logits, W, *, V=None, ids=None, logprob=None, row_lse=None, w
         row_lse = torch.empty(rows, dtype=torch.float32, device=dev)
     ws, wsb = _workspace(topw_workspace_size(rows, V, W, dt), dev, workspace)
     _check(lib().jt_topw_per_depth(_ptr(logits), stride, rows, V, W, dt, _ptr(ids), _ptr(logprob),
-                                   _ptr(row_lse), _ptr(ws), wsb, _stream(stream)),
+                                   _ptr(row_lse), _ptr(row_entropy), _ptr(ws), wsb,
+                                   _stream(stream)),
            "jt_topw_per_depth")
     return ids, logprob, row_lse
 
@@ -235,7 +239,7 @@ def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tr
                       num_blocks=None, max_prefix=None, scale=0.0, out=None, lse=None, ids=None,
                       logprob=None, row_lse=None, anc=None, depth=None, accept_len=None,
                       accept_path=None, bonus=None, argmax_out=None, err=None, workspace=None,
-                      stream=None):
+                      row_entropy=None, stream=None):
     """The four steps in one call (two launches).  draft_logits [S*N, stride] and
     target_logits [S*B, stride] bf16; the rest as for the separate calls.  Returns a dict
     of every output."""
@@ -279,12 +283,13 @@ def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tr
         _ptr(draft_logits), dstride, _ptr(target_logits), tstride, V, W, _ptr(parent),
         _ptr(tokens), S, B, N, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
         _ptr(v_prefix), _ptr(block_table), maxblk, block_size, nblk, _ptr(prefix_len), Pmax, Hq,
-        Hkv, d, float(scale), dt, _ptr(ids), _ptr(logprob), _ptr(row_lse), _ptr(anc),
+        Hkv, d, float(scale), dt, _ptr(ids), _ptr(logprob), _ptr(row_lse), _ptr(row_entropy),
+        _ptr(anc),
         _ptr(depth), _ptr(out), _ptr(lse), _ptr(accept_len), _ptr(accept_path), _ptr(bonus),
         _ptr(argmax_out), _ptr(err), _ptr(ws), wsb, _stream(stream)), "jt_draft_verify_step")
-    return dict(ids=ids, logprob=logprob, row_lse=row_lse, anc=anc, depth=depth, out=out,
-                lse=lse, accept_len=accept_len, accept_path=accept_path, bonus=bonus,
-                argmax=argmax_out, err=err)
+    return dict(ids=ids, logprob=logprob, row_lse=row_lse, row_entropy=row_entropy, anc=anc,
+                depth=depth, out=out, lse=lse, accept_len=accept_len, accept_path=accept_path,
+                bonus=bonus, argmax=argmax_out, err=err)
 
 
 def build_tree_best_first(ids, logprob, N, B, *, entropy=None, w_lp=1.0, w_ent=0.0,

@@ -156,8 +156,8 @@ size_t jt_topw_workspace_size(int32_t rows, int32_t V, int32_t W, jt_dtype dtype
 
 jt_status jt_topw_per_depth(const void *logits, int64_t row_stride, int32_t rows, int32_t V,
                             int32_t W, jt_dtype dtype, int32_t *ids, float *logprob,
-                            float *row_lse, void *workspace, size_t workspace_bytes,
-                            void *stream)
+                            float *row_lse, float *row_entropy, void *workspace,
+                            size_t workspace_bytes, void *stream)
 {
     jt_status st = topw_shape(rows, V, W, dtype);
     if (st != JT_OK)
@@ -173,8 +173,8 @@ jt_status jt_topw_per_depth(const void *logits, int64_t row_stride, int32_t rows
         return JT_ERR_WORKSPACE;
     if (!aligned16(workspace))
         return JT_ERR_ALIGN;
-    return launch_topw(logits, row_stride, rows, V, W, dtype, ids, logprob, row_lse, workspace,
-                       as_stream(stream));
+    return launch_topw(logits, row_stride, rows, V, W, dtype, ids, logprob, row_lse, row_entropy,
+                       workspace, as_stream(stream));
 }
 
 static jt_status verify_shape(int32_t S, int32_t B, int32_t V, int32_t N, jt_dtype dtype)
@@ -240,7 +240,8 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
                                int32_t max_blocks_per_seq, int32_t block_size,
                                int32_t num_blocks, const int32_t *prefix_len, int32_t max_prefix,
                                int32_t Hq, int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
-                               int32_t *ids, float *logprob, float *row_lse, uint64_t *anc,
+                               int32_t *ids, float *logprob, float *row_lse,
+                               float *row_entropy, uint64_t *anc,
                                int32_t *depth, void *out, float *lse, int32_t *accept_len,
                                int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
                                int32_t *err, void *workspace, size_t workspace_bytes,
@@ -322,6 +323,7 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
     in.ids = ids;
     in.logprob = logprob;
     in.row_lse = row_lse;
+    in.row_entropy = row_entropy;
     in.parent = parent;
     in.tokens = tokens;
     in.anc = anc;

@@ -102,7 +102,8 @@ jt_status launch_build_mask(const int32_t *parent, int S, int B, uint64_t *anc, 
 
 size_t topw_workspace(int rows, int V, int W, int dtype);
 jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, int W, int dtype,
-                      int32_t *ids, float *logprob, float *row_lse, void *ws, hipStream_t st);
+                      int32_t *ids, float *logprob, float *row_lse, float *row_entropy, void *ws,
+                      hipStream_t st);
 
 size_t verify_workspace(int S, int B, int V, int dtype);
 jt_status launch_verify(const void *logits, int64_t row_stride, int V, int dtype,
@@ -137,7 +138,7 @@ struct StepLaunch {
     int64_t draft_stride, target_stride;
     int V, W, N;
     int32_t *ids;
-    float *logprob, *row_lse;
+    float *logprob, *row_lse, *row_entropy;
     const int32_t *parent, *tokens;
     uint64_t *anc;
     int32_t *depth;

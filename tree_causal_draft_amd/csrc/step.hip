@@ -30,9 +30,10 @@ struct StepArgs {
     int64_t target_stride;
     int V, W, S, B, N;
     int32_t *ids;
-    float *logprob, *row_lse;
+    float *logprob, *row_lse, *row_entropy;
     uint64_t *tkeys;
     float2 *tms;
+    float *tt;  // the lists' entropy sums, or null when no entropy is asked for
     uint64_t *gkeys;
     uint32_t *gnan;
     const int32_t *parent, *tokens;
@@ -72,7 +73,7 @@ __device__ __forceinline__ void step_scan_roles(const StepArgs &sa, const StepPl
         uint64_t *cand = reinterpret_cast<uint64_t *>(pool) + wid * (kWaveCap + 2 * JT_MAX_W);
         topw_partial_wave<uint16_t, true>(
             static_cast<const uint16_t *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
-            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, b * NW + wid, cand,
+            sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, sa.tt, b * NW + wid, cand,
             cand + kWaveCap + JT_MAX_W);
         return;
     }
@@ -139,8 +140,8 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
         const int wid = threadIdx.x >> 6;
         const int r = b * kStepRowsPerBlock + wid;
         if (r < sa.S * sa.N)
-            topw_merge_row(r, sa.W, sp.tp.nlist, sa.tkeys, sa.tms, sa.ids, sa.logprob, sa.row_lse,
-                           mkeys[wid]);
+            topw_merge_row(r, sa.W, sp.tp.nlist, sa.tkeys, sa.tms, sa.tt, sa.ids, sa.logprob,
+                           sa.row_lse, sa.row_entropy, mkeys[wid]);
         return;
     }
     b -= sp.nR;
@@ -203,7 +204,7 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
 }
 
 struct StepWs {
-    size_t attn, tkeys, tms, gkeys, gnan, flags, total;
+    size_t attn, tkeys, tms, tt, gkeys, gnan, flags, total;
 };
 
 static StepWs step_ws_layout(const StepPlan &sp, int S, int N, int B, int W, int d)
@@ -217,6 +218,8 @@ static StepWs step_ws_layout(const StepPlan &sp, int S, int N, int B, int W, int
     off += align256(tparts * W * sizeof(uint64_t));
     L.tms = off;
     off += align256(tparts * sizeof(float2));
+    L.tt = off;
+    off += align256(tparts * sizeof(float));
     const size_t gparts = (size_t)S * B * sp.gp.nchunk;
     L.gkeys = off;
     off += align256(gparts * sizeof(uint64_t));
@@ -286,6 +289,8 @@ jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st)
     sa.ids = in.ids;
     sa.logprob = in.logprob;
     sa.row_lse = in.row_lse;
+    sa.row_entropy = in.row_entropy;
+    sa.tt = in.row_entropy ? reinterpret_cast<float *>(w + L.tt) : nullptr;
     sa.tkeys = reinterpret_cast<uint64_t *>(w + L.tkeys);
     sa.tms = reinterpret_cast<float2 *>(w + L.tms);
     sa.gkeys = reinterpret_cast<uint64_t *>(w + L.gkeys);

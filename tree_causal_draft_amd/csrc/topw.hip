@@ -17,7 +17,12 @@
 //     wave max over them and the wave's running list give the new list;
 //   * a merge kernel (one wave per row) combines the per-wave top-W lists and the
 //     (max, sum-exp) pairs into ids, log-probs and the row log-sum-exp, selecting by
-//     rank counts.
+//     rank counts;
+//   * on request the same pass gives the row's softmax entropy (the per-depth entropy of
+//     entropy-guided and hybrid tree scoring, paperlayer.ai JetSpec summary, appendices C
+//     and E): with S = sum exp(x - m) and T = sum exp(x - m) (x - m) over a set of logits,
+//     H = log S - T / S, and both sums move to a new reference m' exactly as
+//     S' = c S, T' = c (T + (m - m') S) with c = exp(m - m').
 #include "jt_internal.h"
 
 namespace jt {
@@ -198,22 +203,26 @@ __device__ __forceinline__ uint32_t wave_wth_code(uint32_t code, int W)
 //   * the running list (lane r holds entry r) is appended and W rounds of a DPP wave max
 //     -- over registers when at most 64 keys compete, else over the LDS slice -- give the
 //     new list.
-// Output per wave: its W best keys, descending, 0-padded, and its (max, sum) pair.
+// Output per wave: its W best keys, descending, 0-padded, its (max, sum) pair and, when
+// ws_t is not null, the entropy sum T of its logits (relative to the same max).
 // `cand` holds kWaveCap + JT_MAX_W keys and `best` JT_MAX_W keys of this wave's LDS.
 template <typename T, bool kAligned>
 __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, int64_t row_stride,
                                                   int rows, int V, int W, int npiece, int ppw,
                                                   int nlist, uint64_t *__restrict__ ws_keys,
-                                                  float2 *__restrict__ ws_ms, int gl,
+                                                  float2 *__restrict__ ws_ms,
+                                                  float *__restrict__ ws_t, int gl,
                                                   uint64_t *cand, uint64_t *best)
 {
     constexpr int E = Vec<T>::kElems;
+    const bool want_t = ws_t != nullptr;
     const int lane = threadIdx.x & 63;
     if (gl >= rows * nlist)
         return;
     const int row_idx = gl / nlist, li = gl % nlist;
     const T *row = logits + (int64_t)row_idx * row_stride;
     float run_m = -INFINITY, run_s = 0.f;  // lane's running (max, sum exp(x - max))
+    float run_t = 0.f;                     // and sum exp(x - max) (x - max), on request
     uint64_t run = 0ull;                   // lane r < W: entry r of the running top-W list
     const int p0 = li * ppw, p1 = min(npiece, p0 + ppw);
     RawPiece<T> next;
@@ -231,13 +240,24 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
 #pragma unroll
         for (int j = 0; j < 32; ++j)
             m = fmaxf(m, x[j]);
-        float sx = 0.f;
+        float sx = 0.f, tx = 0.f;
         if (m != -INFINITY) {
             const float mb = m * kLog2e;
             float part[4] = {0.f, 0.f, 0.f, 0.f};
+            if (want_t) {
+                float tp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 32; ++j)
-                part[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+                for (int j = 0; j < 32; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+                    part[j & 3] += e;
+                    tp[j & 3] += e > 0.f ? e * (x[j] - m) : 0.f;  // p = 0 adds 0
+                }
+                tx = (tp[0] + tp[1]) + (tp[2] + tp[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    part[j & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+            }
             sx = (part[0] + part[1]) + (part[2] + part[3]);
         } else {
             // every entry is -inf, padding or NaN: only a NaN must still poison the sum
@@ -247,15 +267,23 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
                     sx = x[j];
         }
         if (m > run_m) {
-            const float prev = (run_m == -INFINITY)
-                                   ? ((run_s != run_s) ? run_s : 0.f)
-                                   : run_s * __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
-            run_s = prev + sx;
+            if (run_m == -INFINITY) {
+                run_s = ((run_s != run_s) ? run_s : 0.f) + sx;
+                run_t = tx;
+            } else {
+                const float c = __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
+                if (want_t)
+                    run_t = c * (run_t + (run_m - m) * run_s) + tx;
+                run_s = run_s * c + sx;
+            }
             run_m = m;
         } else if (m == -INFINITY) {
             run_s += sx;  // adds 0, or propagates a NaN
         } else {
-            run_s += sx * __builtin_amdgcn_exp2f((m - run_m) * kLog2e);
+            const float c = __builtin_amdgcn_exp2f((m - run_m) * kLog2e);
+            if (want_t)
+                run_t += c * (tx + (m - run_m) * sx);
+            run_s += sx * c;
         }
 
         // ---- threshold: a lane's code counts only if it holds a real (non-NaN) element
@@ -340,15 +368,30 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
         wave_sync();  // the slice is rewritten by the next piece
     }
 
-    // ---- (max, sum) over the wave
+    // ---- (max, sum) and T over the wave
     const float m = wave_max_f32(run_m);
-    float sw = (run_m == -INFINITY) ? ((run_s != run_s) ? run_s : 0.f)
-                                    : run_s * __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
+    float sw, tw = 0.f;
+    if (run_m == -INFINITY) {
+        sw = (run_s != run_s) ? run_s : 0.f;
+    } else {
+        const float c = __builtin_amdgcn_exp2f((run_m - m) * kLog2e);
+        sw = run_s * c;
+        if (want_t)
+            tw = c * (run_t + (run_m - m) * run_s);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         sw += __shfl_xor(sw, o, kWave);
-    if (lane == 0)
+    if (want_t) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            tw += __shfl_xor(tw, o, kWave);
+    }
+    if (lane == 0) {
         ws_ms[gl] = make_float2(m, sw);
+        if (want_t)
+            ws_t[gl] = tw;
+    }
     if (lane < W)
         ws_keys[(int64_t)gl * W + lane] = run;
 }
@@ -357,13 +400,14 @@ template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kTopwThreads)
 topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, int V, int W,
                     int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
-                    float2 *__restrict__ ws_ms)
+                    float2 *__restrict__ ws_ms, float *__restrict__ ws_t)
 {
     __shared__ uint64_t cand_all[4][kWaveCap + JT_MAX_W];
     __shared__ uint64_t best_all[4][JT_MAX_W];
     const int wid = threadIdx.x >> 6;
     topw_partial_wave<T, kAligned>(logits, row_stride, rows, V, W, npiece, ppw, nlist, ws_keys,
-                                   ws_ms, blockIdx.x * 4 + wid, cand_all[wid], best_all[wid]);
+                                   ws_ms, ws_t, blockIdx.x * 4 + wid, cand_all[wid],
+                                   best_all[wid]);
 }
 
 constexpr int kMergeCand = JT_MAX_W * JT_MAX_W;  // candidate keys a row merge can keep
@@ -401,8 +445,9 @@ __device__ __forceinline__ void count_greater(const uint64_t *keys, int n, const
 // With at most 8 keys per lane and W <= 4, W rounds of a DPP wave max straight over the
 // registers are cheaper than the two counting passes, and are used instead.
 __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
-                               const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
-                               float *__restrict__ logprob, float *__restrict__ row_lse,
+                               const float2 *__restrict__ ws_ms, const float *__restrict__ ws_t,
+                               int32_t *__restrict__ ids, float *__restrict__ logprob,
+                               float *__restrict__ row_lse, float *__restrict__ row_entropy,
                                uint64_t *keys)
 {
     const int lane = threadIdx.x & 63;
@@ -414,11 +459,13 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
     const float2 *msr = ws_ms + (int64_t)r * nchunk;
     const uint64_t *src = ws_keys + (int64_t)r * n;
     float2 ms[kMsPerLane];
+    float ts[kMsPerLane];
     uint64_t hd[kMsPerLane];
 #pragma unroll
     for (int j = 0; j < kMsPerLane; ++j) {
         const int c = lane + kWave * j;
         ms[j] = c < nchunk ? msr[c] : make_float2(-INFINITY, 0.f);
+        ts[j] = (row_entropy && c < nchunk) ? ws_t[(int64_t)r * nchunk + c] : 0.f;
         hd[j] = c < nchunk ? src[(int64_t)c * W] : 0ull;
     }
     const int nq = (n + kWave - 1) / kWave;  // key slots in use (wave-uniform)
@@ -438,14 +485,17 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
     for (int j = 0; j < kMsPerLane; ++j)
         m = fmaxf(m, ms[j].x);
     m = wave_max_f32(m);
-    float s = 0.f;
+    float s = 0.f, t = 0.f;
 #pragma unroll
     for (int j = 0; j < kMsPerLane; ++j) {
         const float2 p = ms[j];
-        if (p.x == -INFINITY)
+        if (p.x == -INFINITY) {
             s += (p.y != p.y) ? p.y : 0.f;
-        else
-            s += p.y * __builtin_amdgcn_exp2f((p.x - m) * kLog2e);
+        } else {
+            const float c = __builtin_amdgcn_exp2f((p.x - m) * kLog2e);
+            s += p.y * c;
+            t += c * (ts[j] + (p.x - m) * p.y);
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
@@ -457,6 +507,15 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
         lse = -INFINITY;
     else
         lse = m + logf(s);
+    if (row_entropy) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            t += __shfl_xor(t, o, kWave);
+        // H = log S - T / S; a NaN row gives NaN, a row of -inf (no distribution) 0
+        const float h = (s != s) ? s : (m == -INFINITY ? 0.f : logf(s) - t / s);
+        if (lane == 0)
+            row_entropy[r] = h;
+    }
 
     if (nq <= 8 && W <= 4) {
         // W rounds, each taking the largest key below the previous winner
@@ -560,11 +619,13 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
 
 __global__ void __launch_bounds__(64)
 topw_merge_kernel(int rows, int W, int nchunk, const uint64_t *__restrict__ ws_keys,
-                  const float2 *__restrict__ ws_ms, int32_t *__restrict__ ids,
-                  float *__restrict__ logprob, float *__restrict__ row_lse)
+                  const float2 *__restrict__ ws_ms, const float *__restrict__ ws_t,
+                  int32_t *__restrict__ ids, float *__restrict__ logprob,
+                  float *__restrict__ row_lse, float *__restrict__ row_entropy)
 {
     __shared__ __attribute__((aligned(16))) uint64_t keys[kMergeLds];
-    topw_merge_row(blockIdx.x, W, nchunk, ws_keys, ws_ms, ids, logprob, row_lse, keys);
+    topw_merge_row(blockIdx.x, W, nchunk, ws_keys, ws_ms, ws_t, ids, logprob, row_lse,
+                   row_entropy, keys);
 }
 
 struct TopwPlan {
@@ -584,11 +645,13 @@ size_t topw_workspace(int rows, int V, int W, int /*dtype*/)
 {
     const TopwPlan p = topw_plan(rows, V);
     const size_t parts = (size_t)rows * p.nlist;
-    return parts * (size_t)W * sizeof(uint64_t) + parts * sizeof(float2) + 256;
+    return parts * (size_t)W * sizeof(uint64_t) + parts * sizeof(float2) +
+           parts * sizeof(float) + 512;
 }
 
 jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, int W, int dtype,
-                      int32_t *ids, float *logprob, float *row_lse, void *ws, hipStream_t st)
+                      int32_t *ids, float *logprob, float *row_lse, float *row_entropy, void *ws,
+                      hipStream_t st)
 {
     if (rows == 0)
         return JT_OK;
@@ -598,6 +661,9 @@ jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, i
     uintptr_t mp = reinterpret_cast<uintptr_t>(wk + parts * W);
     mp = (mp + 15) & ~(uintptr_t)15;
     float2 *wm = reinterpret_cast<float2 *>(mp);
+    uintptr_t tp = reinterpret_cast<uintptr_t>(wm + parts);
+    tp = (tp + 15) & ~(uintptr_t)15;
+    float *wt = row_entropy ? reinterpret_cast<float *>(tp) : nullptr;
     const dim3 grid((unsigned)((parts + 3) / 4)), block(kTopwThreads);
     const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
     if (dtype == JT_BF16) {
@@ -605,27 +671,27 @@ jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, i
         if (al)
             hipLaunchKernelGGL((topw_partial_kernel<uint16_t, true>), grid, block, 0, st,
                                (const uint16_t *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm);
+                               p.nlist, wk, wm, wt);
         else
             hipLaunchKernelGGL((topw_partial_kernel<uint16_t, false>), grid, block, 0, st,
                                (const uint16_t *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm);
+                               p.nlist, wk, wm, wt);
     } else {
         const bool al = (addr % 16 == 0) && (row_stride % 4 == 0);
         if (al)
             hipLaunchKernelGGL((topw_partial_kernel<float, true>), grid, block, 0, st,
                                (const float *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm);
+                               p.nlist, wk, wm, wt);
         else
             hipLaunchKernelGGL((topw_partial_kernel<float, false>), grid, block, 0, st,
                                (const float *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm);
+                               p.nlist, wk, wm, wt);
     }
     jt_status e = launch_status(hipGetLastError());
     if (e != JT_OK)
         return e;
     hipLaunchKernelGGL(topw_merge_kernel, dim3(rows), dim3(64), 0, st, rows, W, p.nlist, wk, wm,
-                       ids, logprob, row_lse);
+                       wt, ids, logprob, row_lse, row_entropy);
     return launch_status(hipGetLastError());
 }
 
