@@ -226,3 +226,41 @@ def build_tree(ids, logprob, N: int, B: int, *, entropy=None, w_lp: float = 1.0,
     if rc:
         raise ValueError(f"jto_build_tree rc={rc}")
     return out
+
+
+def commit_kv(accept_len, accept_path, N: int, k_tree, v_tree, k_cache, v_cache, prefix_len, *,
+              block_table=None, block_size: int = 16):
+    """Write the accepted root path's K/V rows into copies of the prefix caches.
+
+    ``k_tree``/``v_tree`` [S,B,Hkv,d]; caches contiguous [S,Pmax,Hkv,d] or, with
+    ``block_table`` [S,max_blocks], paged [num_blocks,block_size,Hkv,d]; float32 or bf16
+    words (uint16).  Returns (k_cache, v_cache, new_prefix_len [S], err [S]).
+    """
+    k_tree = np.ascontiguousarray(k_tree)
+    v_tree = np.ascontiguousarray(v_tree)
+    if k_tree.dtype not in (np.float32, np.uint16) or v_tree.dtype != k_tree.dtype:
+        raise TypeError("K/V must be float32 or bf16 words")
+    kc = np.array(k_cache, dtype=k_tree.dtype, copy=True, order="C")
+    vc = np.array(v_cache, dtype=k_tree.dtype, copy=True, order="C")
+    S, B, Hkv, d = k_tree.shape
+    al = _c(accept_len, np.int32)
+    ap = _c(accept_path, np.int32)
+    pl = _c(prefix_len, np.int32)
+    bt = None if block_table is None else _c(block_table, np.int32)
+    if bt is None:
+        max_prefix, max_blocks, nblk = kc.shape[1], 0, 0
+    else:
+        max_prefix, max_blocks, nblk = 0, bt.shape[1], kc.shape[0]
+    newp = np.zeros(S, np.int32)
+    err = np.zeros(S, np.int32)
+    lib = _load()
+    lib.jto_commit_kv.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + \
+        [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_int] + \
+        [ctypes.c_void_p] * 2
+    rc = lib.jto_commit_kv(_p(al), _p(ap), N, _p(k_tree), _p(v_tree), S, B, Hkv, d,
+                           k_tree.dtype.itemsize, _p(kc), _p(vc), _p(bt), max_blocks, block_size,
+                           nblk, _p(pl), max_prefix, _p(newp), _p(err))
+    if rc:
+        raise ValueError(f"jto_commit_kv rc={rc}")
+    return kc, vc, newp, err

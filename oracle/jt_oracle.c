@@ -551,3 +551,82 @@ int jto_build_tree(const int32_t *ids, const float *logprob, const float *entrop
     free(sc); free(dep); free(queued);
     return 0;
 }
+
+/* ------------------------------------------------------ accepted-path commit -- */
+
+/*
+ * After verification the accepted root path becomes part of the prefix: the
+ * verifier commits the longest accepted prefix (paperlayer.ai JetSpec summary,
+ * section 2; JetSpec++ summary, section 3), whose keys and values this pass
+ * already computed in the tree buffers.  Node 0 is the root (the last
+ * committed token, computed in this pass), so path nodes path[0..L] (L =
+ * accept_len[s], path[0] = 0) are written to prefix positions P .. P + L of
+ * sequence s, P = prefix_len[s]; node path[i] has depth i, so its rotary
+ * position P + i is its slot and nothing is re-rotated.  new_prefix_len[s] =
+ * P + L + 1.  Plain byte copies of each (position, KV head) row of d elements.
+ *
+ * Cache layout: contiguous [S, max_prefix, Hkv, d] when block_table is NULL,
+ * else paged [num_blocks, block_size, Hkv, d] with position j of sequence s in
+ * block block_table[s*max_blocks + j/block_size], row j % block_size.
+ * Flags per sequence (err, optional): accept_len outside [0, N] -> DEPTH_GT_N
+ * (2), nothing written; P < 0 or P + L + 1 beyond the capacity (max_prefix, or
+ * max_blocks * block_size) -> BAD_PREFIX (16), nothing written; a path entry
+ * outside [0, B) -> BAD_PARENT (1), that row skipped; a block id outside
+ * [0, num_blocks) -> BAD_BLOCK (4), that row skipped.  A flagged sequence
+ * keeps new_prefix_len = P.
+ */
+int jto_commit_kv(const int32_t *accept_len, const int32_t *accept_path, int N,
+                  const void *k_tree, const void *v_tree, int S, int B, int Hkv, int d,
+                  int elem_bytes, void *k_cache, void *v_cache,
+                  const int32_t *block_table, int max_blocks, int block_size,
+                  int num_blocks, const int32_t *prefix_len, int max_prefix,
+                  int32_t *new_prefix_len, int32_t *err)
+{
+    if (S < 0 || B < 1 || N < 0 || Hkv < 1 || d < 1 || (elem_bytes != 2 && elem_bytes != 4))
+        return 2;
+    const size_t row = (size_t)d * (size_t)elem_bytes;
+    for (int s = 0; s < S; s++) {
+        int flag = 0;
+        const int L = accept_len[s];
+        const int P = prefix_len[s];
+        const long cap = block_table ? (long)max_blocks * block_size : (long)max_prefix;
+        int committed = 0;
+        if (L < 0 || L > N) {
+            flag |= 2;
+        } else if (P < 0 || (long)P + L + 1 > cap) {
+            flag |= 16;
+        } else {
+            committed = 1;
+            for (int i = 0; i <= L; i++) {
+                const int v = accept_path[(int64_t)s * (N + 1) + i];
+                if (v < 0 || v >= B) {
+                    flag |= 1;
+                    continue;
+                }
+                const long j = (long)P + i;
+                int64_t slot;  /* (position or pool row) whose Hkv rows are written */
+                if (block_table) {
+                    const int blk = block_table[(int64_t)s * max_blocks + j / block_size];
+                    if (blk < 0 || blk >= num_blocks) {
+                        flag |= 4;
+                        continue;
+                    }
+                    slot = (int64_t)blk * block_size + j % block_size;
+                } else {
+                    slot = (int64_t)s * max_prefix + j;
+                }
+                for (int g = 0; g < Hkv; g++) {
+                    const int64_t src = (((int64_t)s * B + v) * Hkv + g) * (int64_t)row;
+                    const int64_t dst = (slot * Hkv + g) * (int64_t)row;
+                    memcpy((char *)k_cache + dst, (const char *)k_tree + src, row);
+                    memcpy((char *)v_cache + dst, (const char *)v_tree + src, row);
+                }
+            }
+        }
+        if (new_prefix_len)
+            new_prefix_len[s] = (committed && !flag) ? P + L + 1 : P;
+        if (err)
+            err[s] = flag;
+    }
+    return 0;
+}
