@@ -53,11 +53,13 @@ KERNELS = {
     "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
     "step": ["step_phase1", "step_scan_kernel", "step_phase2"],
     "tree": ["tree_build_kernel"],
+    "commit": ["commit_kv_kernel"],
 }
 # the kernel whose dispatches count the launches of each entry point
 MARKER = {"topw": "topw_partial_kernel", "mask": "build_mask_kernel",
           "attention": ("attn_bf16_kernel", "attn_simple_kernel"),
-          "verify": "argmax_partial_kernel", "step": "step_phase2", "tree": "tree_build_kernel"}
+          "verify": "argmax_partial_kernel", "step": "step_phase2", "tree": "tree_build_kernel",
+          "commit": "commit_kv_kernel"}
 
 
 def algorithmic(w):
@@ -221,8 +223,9 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
     # ---- each entry point alone: one graph of nsets launches (one per cold input set)
     per_call_us = {}
     calls_here = CALLS + (("step",) if hasattr(st, "step_ws") else ()) + \
-        (("tree",) if hasattr(st, "tree_parent") else ())
-    st.topw()  # the tree call reads the top-W lists
+        (("tree",) if hasattr(st, "tree_parent") else ()) + \
+        (("commit",) if hasattr(st, "commit_k") else ())
+    st.run()  # the tree call reads the top-W lists, the commit the accepted paths
     for c in calls_here:
         g = _capture([getattr(s, "run_fused" if c == "step" else c) for s in rot.steps])
         per_call_us[c], _ = _time_graph(g, nsets, steps, warmup)
@@ -230,6 +233,11 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
     log(f"[bench] {name}: per call " + " ".join(f"{c}={per_call_us[c]:.2f}us" for c in calls_here))
 
     bytes_, flops = algorithmic(w)
+    if "commit" in calls_here:
+        # the accepted paths' K and V rows, read and written, plus lengths and paths
+        rows = int((st.accept_len.cpu().numpy().astype(np.int64) + 1).sum())
+        e = 4 if w.cfg.dtype == "f32" else 2
+        bytes_["commit"] = rows * w.cfg.Hkv * w.cfg.d * e * 4 + w.cfg.S * (w.cfg.N + 1 + 4) * 4
     calls = {}
     for c in calls_here:
         us = per_call_us[c]
@@ -305,7 +313,7 @@ def _kernel_hash(call):
     files = {"topw": ["topw.hip"], "mask": ["mask.hip"], "attention": ["attn.hip"],
              "verify": ["verify.hip"],
              "step": ["mask.hip", "topw.hip", "verify.hip", "attn.hip", "step.hip"],
-             "tree": ["tree.hip"]}[call]
+             "tree": ["tree.hip"], "commit": ["commit.hip"]}[call]
     import re
     h = hashlib.sha256()
     for f in files + ["jt_internal.h"]:
@@ -353,7 +361,8 @@ def traffic_run(name, seed, reps=3, log=print):
     st = DeviceStep(w, "cuda:0")
     nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(footprint(st), 1))))
     rot = Rotation(st, nsets)
-    for c in CALLS + (("run_fused",) if hasattr(st, "step_ws") else ()) + ("tree",):
+    extra = ("tree",) + (("commit",) if hasattr(st, "commit_k") else ())
+    for c in CALLS + (("run_fused",) if hasattr(st, "step_ws") else ()) + extra:
         for i in range(reps * nsets):
             getattr(rot.steps[i % nsets], c)()
         torch.cuda.synchronize()
@@ -388,7 +397,7 @@ def traffic_summarize(name, fetch_dir, write_dir):
     calibration copy moved) / (what the counter read for it).  The traffic run launches the
     entry points one after the other (top-W, mask, attention, verify, then the fused step,
     whose 8-wave shapes also run attn_bf16_kernel), so dispatches are assigned in order."""
-    order = list(CALLS) + ["step", "tree"]
+    order = list(CALLS) + ["step", "tree", "commit"]
     def hits(kname, call):
         return any(k in kname for k in KERNELS[call])
     def is_marker(kname, call):

@@ -58,10 +58,11 @@ typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
 /* device-side per-sequence flags written to err[s] */
 enum {
     JT_DEV_BAD_PARENT = 1,  /* parent[s,0] != -1 or parent[s,i] not in [0, i) */
-    JT_DEV_DEPTH_GT_N = 2,  /* some node is deeper than N */
+    JT_DEV_DEPTH_GT_N = 2,  /* some node is deeper than N (commit: accept_len not in [0, N]) */
     JT_DEV_BAD_BLOCK = 4,   /* a block-table entry needed by the prefix is outside the pool */
     JT_DEV_NAN = 8,         /* a target logit row holds a NaN */
-    JT_DEV_BAD_PREFIX = 16  /* prefix_len[s] outside [0, max_prefix] (it is clamped) */
+    JT_DEV_BAD_PREFIX = 16  /* prefix_len[s] outside [0, max_prefix] (it is clamped; commit:
+                               the path would not fit the cache) */
 };
 
 #define JT_MAX_NODES 256 /* B limit: one 256-bit ancestor row per node */
@@ -266,6 +267,40 @@ jt_status jt_build_tree_best_first(const int32_t *ids, const float *logprob,
                                    const int32_t *root_token, int32_t S, int32_t N, int32_t W,
                                    int32_t B, int32_t *parent, int32_t *tokens, float *score,
                                    int32_t *n_nodes, void *stream);
+
+/*
+ * Accepted-path commit: the K/V of the accepted root path join the prefix cache.  The
+ * verifier commits the longest accepted root path (paperlayer.ai JetSpec summary,
+ * section 2; JetSpec++ summary, section 3), whose K/V this pass computed in k_tree /
+ * v_tree.  Node 0 is the root (the last committed token), so for sequence s with
+ * L = accept_len[s] and P = prefix_len[s], node accept_path[s][i] is written to prefix
+ * position P + i for i = 0..L, every KV head, and new_prefix_len[s] = P + L + 1.  A node
+ * at depth i has rotary position P + i, which is its slot; nothing is re-rotated.
+ *
+ *   accept_len [S], accept_path [S, N+1]   as jt_verify_greedy writes them
+ *   k_tree, v_tree   [S, B, Hkv, d] dtype
+ *   k_cache, v_cache contiguous [S, max_prefix, Hkv, d] when block_table is NULL; else
+ *                    paged [num_blocks, block_size, Hkv, d], position j of sequence s in
+ *                    block block_table[s * max_blocks_per_seq + j / block_size]
+ *   prefix_len [S] in, new_prefix_len [S] out (may be the same array: the update is then
+ *                    in place)
+ *   err [S] (optional) out: JT_DEV_DEPTH_GT_N when accept_len is outside [0, N] and
+ *                    JT_DEV_BAD_PREFIX when P < 0 or P + L + 1 exceeds the capacity
+ *                    (max_prefix, or max_blocks_per_seq * block_size) -- nothing is
+ *                    written then; JT_DEV_BAD_PARENT for a path entry outside [0, B) and
+ *                    JT_DEV_BAD_BLOCK for a block id outside [0, num_blocks) -- that row
+ *                    is skipped.  A flagged sequence keeps new_prefix_len = P.
+ * Supported: d in {64, 128}; dtype JT_BF16 or JT_F32; 0 <= N <= 255; 1 <= B <= 256;
+ * the four K/V pointers 16-byte aligned.  No workspace; one workgroup per sequence.
+ */
+jt_status jt_commit_accepted_kv(const int32_t *accept_len, const int32_t *accept_path, int32_t N,
+                                const void *k_tree, const void *v_tree, int32_t S, int32_t B,
+                                int32_t Hkv, int32_t d, jt_dtype dtype, void *k_cache,
+                                void *v_cache, const int32_t *block_table,
+                                int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t num_blocks, const int32_t *prefix_len,
+                                int32_t max_prefix, int32_t *new_prefix_len, int32_t *err,
+                                void *stream);
 
 #ifdef __cplusplus
 }

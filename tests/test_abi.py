@@ -79,6 +79,14 @@ def test_host_validation_returns_before_launch():
     assert tree(N=-1) == 2 and tree(N=256) == 2
     assert tree() == 1
     assert tree(S=0) == 0
+    # accepted-path commit: d, dtype, N, NULLs
+    def commit(S=1, N=4, B=16, d=128, dt=1, table=None):
+        return L.jt_commit_accepted_kv(nul, nul, N, nul, nul, S, B, 8, d, dt, nul, nul, table,
+                                       4, 16, 8, nul, 64, nul, nul, nul)
+    assert commit(d=96) == 2 and commit(N=256) == 2 and commit(B=0) == 2
+    assert commit(dt=5) == 3
+    assert commit() == 1
+    assert commit(S=0) == 0
 
 
 def test_workspace_queries_are_pure():

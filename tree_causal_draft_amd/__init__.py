@@ -23,7 +23,8 @@ DEV_BAD_PARENT, DEV_DEPTH_GT_N, DEV_BAD_BLOCK, DEV_NAN, DEV_BAD_PREFIX = 1, 2, 4
 EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
            "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
            "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy",
-           "jt_step_workspace_size", "jt_draft_verify_step", "jt_build_tree_best_first")
+           "jt_step_workspace_size", "jt_draft_verify_step", "jt_build_tree_best_first",
+           "jt_commit_accepted_kv")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -69,8 +70,12 @@ def lib() -> ctypes.CDLL:
             [_sz, _vp])
         L.jt_build_tree_best_first.argtypes = ([_vp] * 3 + [ctypes.c_float] * 2 + [_vp] +
                                                [_i32] * 4 + [_vp] * 5)
+        L.jt_commit_accepted_kv.argtypes = ([_vp, _vp, _i32, _vp, _vp] + [_i32] * 4 +
+                                            [ctypes.c_int, _vp, _vp, _vp] + [_i32] * 3 +
+                                            [_vp, _i32, _vp, _vp, _vp])
         for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
-                   "jt_verify_greedy", "jt_draft_verify_step", "jt_build_tree_best_first"):
+                   "jt_verify_greedy", "jt_draft_verify_step", "jt_build_tree_best_first",
+                   "jt_commit_accepted_kv"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -323,3 +328,39 @@ def build_tree_best_first(ids, logprob, N, B, *, entropy=None, w_lp=1.0, w_ent=0
                                           _ptr(n_nodes), _stream(stream)),
            "jt_build_tree_best_first")
     return parent, tokens, score, n_nodes
+
+
+def commit_accepted_kv(accept_len, accept_path, k_tree, v_tree, k_cache, v_cache, prefix_len,
+                       *, block_table=None, block_size=16, num_blocks=None, new_prefix_len=None,
+                       err=None, stream=None):
+    """Write the accepted root path's K/V rows into the prefix cache (in place).
+
+    accept_len [S], accept_path [S,N+1] int32; k_tree/v_tree [S,B,Hkv,d]; caches
+    contiguous [S,Pmax,Hkv,d], or paged [num_blocks,block_size,Hkv,d] with block_table
+    [S,max_blocks].  new_prefix_len may be prefix_len itself.  Returns (new_prefix_len, err).
+    """
+    for t, n in ((accept_len, "accept_len"), (accept_path, "accept_path"), (k_tree, "k_tree"),
+                 (v_tree, "v_tree"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (prefix_len, "prefix_len")):
+        _need(t, n)
+    S, B, Hkv, d = k_tree.shape
+    N = accept_path.shape[1] - 1
+    dt = _dt(k_tree)
+    if block_table is None:
+        maxblk, nblk, Pmax = 0, 0, k_cache.shape[1]
+    else:
+        _need(block_table, "block_table")
+        maxblk, Pmax = block_table.shape[1], 0
+        nblk = k_cache.shape[0] if num_blocks is None else num_blocks
+    dev = k_tree.device
+    new_prefix_len = (torch.empty(S, dtype=torch.int32, device=dev) if new_prefix_len is None
+                      else new_prefix_len)
+    err = torch.empty(S, dtype=torch.int32, device=dev) if err is None else err
+    _check(lib().jt_commit_accepted_kv(_ptr(accept_len), _ptr(accept_path), N, _ptr(k_tree),
+                                       _ptr(v_tree), S, B, Hkv, d, dt, _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(block_table), maxblk, block_size,
+                                       nblk, _ptr(prefix_len), Pmax, _ptr(new_prefix_len),
+                                       _ptr(err), _stream(stream)),
+           "jt_commit_accepted_kv")
+    return new_prefix_len, err
+

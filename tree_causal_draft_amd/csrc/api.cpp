@@ -352,4 +352,34 @@ jt_status jt_build_tree_best_first(const int32_t *ids, const float *logprob,
                              tokens, score, n_nodes, as_stream(stream));
 }
 
+jt_status jt_commit_accepted_kv(const int32_t *accept_len, const int32_t *accept_path, int32_t N,
+                                const void *k_tree, const void *v_tree, int32_t S, int32_t B,
+                                int32_t Hkv, int32_t d, jt_dtype dtype, void *k_cache,
+                                void *v_cache, const int32_t *block_table,
+                                int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t num_blocks, const int32_t *prefix_len,
+                                int32_t max_prefix, int32_t *new_prefix_len, int32_t *err,
+                                void *stream)
+{
+    if (dtype != JT_BF16 && dtype != JT_F32)
+        return JT_ERR_DTYPE;
+    if (S < 0 || N < 0 || N > 255 || B < 1 || B > JT_MAX_NODES || Hkv < 1 ||
+        (d != 64 && d != 128))
+        return JT_ERR_SHAPE;
+    if (block_table ? (max_blocks_per_seq < 1 || block_size < 1 || num_blocks < 1)
+                    : max_prefix < 0)
+        return JT_ERR_SHAPE;
+    if (S == 0)
+        return JT_OK;
+    if (!accept_len || !accept_path || !k_tree || !v_tree || !k_cache || !v_cache ||
+        !prefix_len || !new_prefix_len)
+        return JT_ERR_NULL;
+    if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(k_cache) || !aligned16(v_cache))
+        return JT_ERR_ALIGN;
+    return launch_commit_kv(accept_len, accept_path, N, k_tree, v_tree, S, B, Hkv, d,
+                            dtype == JT_BF16 ? 2 : 4, k_cache, v_cache, block_table,
+                            max_blocks_per_seq, block_size, num_blocks, prefix_len, max_prefix,
+                            new_prefix_len, err, as_stream(stream));
+}
+
 } // extern "C"

@@ -149,6 +149,13 @@ jt_status launch_build_tree(const int32_t *ids, const float *logprob, const floa
                             int W, int B, int32_t *parent, int32_t *tokens, float *score,
                             int32_t *n_nodes, hipStream_t st);
 
+jt_status launch_commit_kv(const int32_t *accept_len, const int32_t *accept_path, int N,
+                           const void *k_tree, const void *v_tree, int S, int B, int Hkv, int d,
+                           int elem_bytes, void *k_cache, void *v_cache,
+                           const int32_t *block_table, int max_blocks, int block_size,
+                           int num_blocks, const int32_t *prefix_len, int max_prefix,
+                           int32_t *new_prefix_len, int32_t *err, hipStream_t st);
+
 size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d, int max_prefix,
                       int block_size);
 jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st);

@@ -7,3 +7,4 @@
 #include "attn.hip"
 #include "step.hip"
 #include "tree.hip"
+#include "commit.hip"

@@ -13,8 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (build_tree_best_first, build_tree_mask, draft_verify_step, step_workspace_size,
-               topw_per_depth,
+from . import (build_tree_best_first, build_tree_mask, commit_accepted_kv, draft_verify_step,
+               step_workspace_size, topw_per_depth,
                tree_attention, tree_attention_workspace_size, topw_workspace_size, verify_greedy,
                verify_workspace_size, JT_BF16, JT_F32)
 from .workload import Workload
@@ -57,6 +57,14 @@ class DeviceStep:
                 S, B, cfg.Hq, cfg.Hkv, cfg.d, w.max_prefix, dt,
                 cfg.block_size if w.block_table is not None else 0)
             self.attn_ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev) if nb else None
+            if w.block_table is None:
+                # a prefix cache with room for an accepted path, written by commit()
+                cap = w.max_prefix + N + 1
+                self.commit_k = torch.zeros((S, cap) + tuple(self.k_prefix.shape[2:]),
+                                            dtype=self.k_prefix.dtype, device=dev)
+                self.commit_v = torch.zeros_like(self.commit_k)
+                self.commit_len = torch.empty(S, dtype=torch.int32, device=dev)
+                self.err_commit = torch.empty(S, dtype=torch.int32, device=dev)
         if "topw" in parts:
             self.draft = to_device(w.draft_logits, dev)
             self.ids = torch.empty((S * N, W), dtype=torch.int32, device=dev)
@@ -95,6 +103,13 @@ class DeviceStep:
         build_tree_best_first(self.ids, self.logprob, self.cfg.N, self.cfg.B,
                               parent=self.tree_parent, tokens=self.tree_tokens,
                               score=self.tree_score, n_nodes=self.tree_n)
+
+    def commit(self):
+        """The accepted paths of the last verification into the commit cache (not part of
+        run())."""
+        commit_accepted_kv(self.accept_len, self.accept_path, self.k_tree, self.v_tree,
+                           self.commit_k, self.commit_v, self.prefix_len,
+                           new_prefix_len=self.commit_len, err=self.err_commit)
 
     def mask(self):
         build_tree_mask(self.parent, self.anc, self.depth, self.err_mask)
