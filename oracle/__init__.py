@@ -264,3 +264,35 @@ def commit_kv(accept_len, accept_path, N: int, k_tree, v_tree, k_cache, v_cache,
     if rc:
         raise ValueError(f"jto_commit_kv rc={rc}")
     return kc, vc, newp, err
+
+
+def verify_sampled(target_logits, parent, tokens, N: int, temperature: float, uniform, V=None):
+    """Stochastic verification with one inverse-CDF draw per node from softmax(logits / T).
+
+    ``uniform`` [S,B] in [0, 1) (float32 values, widened exactly).  Returns the dict of
+    verify_greedy with "sample" [S,B] in place of "argmax", plus "margin" [S,B] (each
+    draw's distance from its interval's nearer end, as a fraction of the row's weight).
+    """
+    parent = _c(parent, np.int32)
+    tokens = _c(tokens, np.int32)
+    S, B = parent.shape
+    dt = _dtype_code(target_logits)
+    tl = np.ascontiguousarray(target_logits).reshape(S * B, -1)
+    row_stride = tl.shape[1]
+    V = row_stride if V is None else V
+    u = np.ascontiguousarray(np.asarray(uniform, np.float32).astype(np.float64).reshape(S, B))
+    out = dict(accept_len=np.zeros(S, np.int32), accept_path=np.zeros((S, N + 1), np.int32),
+               bonus=np.zeros(S, np.int32), sample=np.zeros((S, B), np.int32),
+               margin=np.zeros((S, B), np.float64), err=np.zeros(S, np.int32))
+    lib = _load()
+    lib.jto_verify_sampled.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6
+    rc = lib.jto_verify_sampled(_p(tl), row_stride, V, dt, float(temperature), _p(u), _p(parent),
+                                _p(tokens), S, B, N, _p(out["accept_len"]),
+                                _p(out["accept_path"]), _p(out["bonus"]), _p(out["sample"]),
+                                _p(out["margin"]), _p(out["err"]))
+    if rc:
+        raise ValueError(f"jto_verify_sampled rc={rc}")
+    return out

@@ -373,18 +373,62 @@ static int32_t row_argmax(const void *logits, int64_t base, int V, int dtype, in
 }
 
 /*
- * Greedy tree verification.
- *   am[s,v]   = argmax_t target_logits[s,v,t] (lowest id on ties);
+ * The verification walk shared by the greedy and sampled rules, given the
+ * target's token am[v] at every node (its argmax, or its draw):
  *   v accepted iff every node u != root on the root path of v has
- *              tokens[s,u] == am[s,parent[u]];
+ *              tokens[u] == am[parent[u]];
  *   v*        = deepest accepted node, lowest index on ties (root is always
  *              accepted);
- *   accept_len[s] = depth(v*), accept_path[s,0..N] = root..v* padded with -1,
- *   bonus[s]  = am[s,v*].
- * Row (s, v) of the logits starts at (s*B + v)*row_stride elements.
- * err[s]: ORA_BAD_PARENT, ORA_DEPTH_GT_N (some node deeper than N), ORA_NAN.
- * A sequence with a bad parent array or a node deeper than N gets
- * accept_len 0, path [0, -1, ...] and bonus am[s,0].
+ *   accept_len = depth(v*), path[0..N] = root..v* padded with -1, bonus =
+ *   am[v*].  Returns the flags ORA_BAD_PARENT / ORA_DEPTH_GT_N; such a
+ *   sequence gets accept_len 0, path [0, -1, ...] and bonus am[0].
+ */
+static int tree_walk(const int32_t *par, const int32_t *tok, const int32_t *am, int B, int N,
+                     int32_t *accept_len, int32_t *path, int32_t *bonus)
+{
+    for (int k = 0; k <= N; k++)
+        path[k] = -1;
+    path[0] = 0;
+    *accept_len = 0;
+    *bonus = am[0];
+    if (!parents_valid(par, B))
+        return ORA_BAD_PARENT;
+    for (int v = 0; v < B; v++) {
+        int dv = 0;
+        for (int u = v; par[u] != -1; u = par[u])
+            dv++;
+        if (dv > N)
+            return ORA_DEPTH_GT_N;
+    }
+    int best_v = 0, best_d = 0;
+    for (int v = 0; v < B; v++) {
+        int ok = 1, dv = 0;
+        for (int u = v; par[u] != -1; u = par[u]) {
+            if (tok[u] != am[par[u]])
+                ok = 0;
+            dv++;
+        }
+        if (ok && dv > best_d) {
+            best_d = dv;
+            best_v = v;
+        }
+    }
+    *accept_len = best_d;
+    for (int u = best_v; u != -1; u = par[u]) {
+        int du = 0;
+        for (int w = u; par[w] != -1; w = par[w])
+            du++;
+        path[du] = u;
+    }
+    *bonus = am[best_v];
+    return 0;
+}
+
+/*
+ * Greedy tree verification: am[s,v] = argmax_t target_logits[s,v,t] (lowest id
+ * on ties), then tree_walk.  Row (s, v) of the logits starts at
+ * (s*B + v)*row_stride elements.  err[s]: ORA_BAD_PARENT, ORA_DEPTH_GT_N (some
+ * node deeper than N), ORA_NAN.
  */
 int jto_verify_greedy(const void *target_logits, int64_t row_stride, int V, int dtype,
                       const int32_t *parent, const int32_t *tokens, int S, int B, int N,
@@ -394,58 +438,100 @@ int jto_verify_greedy(const void *target_logits, int64_t row_stride, int V, int 
     if (S < 0 || B < 1 || V < 1 || N < 0 || row_stride < V)
         return 2;
     for (int s = 0; s < S; s++) {
-        const int32_t *par = parent + (int64_t)s * B;
-        const int32_t *tok = tokens + (int64_t)s * B;
         int32_t *am = argmax + (int64_t)s * B;
-        int32_t *path = accept_path + (int64_t)s * (N + 1);
-        int flags = 0, saw_nan = 0;
+        int saw_nan = 0;
         for (int v = 0; v < B; v++)
             am[v] = row_argmax(target_logits, ((int64_t)s * B + v) * row_stride, V, dtype, &saw_nan);
-        if (saw_nan)
-            flags |= ORA_NAN;
-        for (int k = 0; k <= N; k++)
-            path[k] = -1;
-        path[0] = 0;
-        accept_len[s] = 0;
-        bonus[s] = am[0];
-        if (!parents_valid(par, B)) {
-            err[s] = flags | ORA_BAD_PARENT;
+        const int flags = tree_walk(parent + (int64_t)s * B, tokens + (int64_t)s * B, am, B, N,
+                                    &accept_len[s], accept_path + (int64_t)s * (N + 1), &bonus[s]);
+        err[s] = flags | (saw_nan ? ORA_NAN : 0);
+    }
+    return 0;
+}
+
+/*
+ * One draw from softmax(x / T) by the inverse of its cumulative distribution
+ * in token-id order: the first t whose cumulative weight exceeds r * Z, with
+ * weights e_t = exp((x_t - m) / T) (m = row maximum, Z = their sum).  NaN
+ * entries weigh 0 and set *saw_nan (the greedy rule skips them too).  A row
+ * with no finite maximum gives token 0, like the argmax of such a row.
+ * *margin = the distance of r * Z from the nearer end of the drawn token's
+ * interval, divided by Z (how far the draw is from going to a neighbour).
+ */
+static int32_t row_sample(const void *logits, int64_t base, int V, int dtype, double T, double r,
+                          int *saw_nan, double *margin)
+{
+    double m = -INFINITY;
+    for (int t = 0; t < V; t++) {
+        double x = elem(logits, base + t, dtype);
+        if (isnan(x)) { *saw_nan = 1; continue; }
+        if (x > m) m = x;
+    }
+    if (m == -INFINITY) {
+        *margin = INFINITY;
+        return 0;
+    }
+    double Z = 0.0;
+    for (int t = 0; t < V; t++) {
+        double x = elem(logits, base + t, dtype);
+        if (!isnan(x))
+            Z += exp((x - m) / T);
+    }
+    const double target = r * Z;
+    double cum = 0.0;
+    int32_t last = 0;
+    for (int t = 0; t < V; t++) {
+        double x = elem(logits, base + t, dtype);
+        if (isnan(x))
             continue;
+        const double e = exp((x - m) / T);
+        if (e > 0.0)
+            last = t;
+        const double prev = cum;
+        cum += e;
+        if (cum > target) {
+            *margin = fmin(target - prev, cum - target) / Z;
+            return t;
         }
-        int too_deep = 0;
+    }
+    *margin = 0.0;
+    return last;
+}
+
+/*
+ * Stochastic tree verification at temperature T > 0.  The target's own draw
+ * decides every position: with a fixed draft every proposal is a point mass at
+ * the draft token, accepted with the target probability, and after a
+ * rejection the next token comes from the residual (JetSpec review, inference,
+ * acceptance equation; JetSpec++ summary, appendices F.1 and F.3).  Sibling
+ * tokens are distinct, so trying the children of a node one by one that way
+ * is the same in distribution as drawing one token x ~ softmax(logits / T) at
+ * the node and descending to the child carrying x, or stopping with bonus x.
+ * This function does the latter: am[s,v] = row_sample(row (s,v), uniform[s,v])
+ * for every node, then tree_walk.  margin (optional) [S,B] receives each
+ * draw's margin.  err[s]: as for jto_verify_greedy.
+ */
+int jto_verify_sampled(const void *target_logits, int64_t row_stride, int V, int dtype,
+                       double T, const double *uniform, const int32_t *parent,
+                       const int32_t *tokens, int S, int B, int N, int32_t *accept_len,
+                       int32_t *accept_path, int32_t *bonus, int32_t *sample, double *margin,
+                       int32_t *err)
+{
+    if (S < 0 || B < 1 || V < 1 || N < 0 || row_stride < V || !(T > 0.0))
+        return 2;
+    for (int s = 0; s < S; s++) {
+        int32_t *am = sample + (int64_t)s * B;
+        int saw_nan = 0;
         for (int v = 0; v < B; v++) {
-            int dv = 0;
-            for (int u = v; par[u] != -1; u = par[u])
-                dv++;
-            if (dv > N)
-                too_deep = 1;
+            double mg;
+            am[v] = row_sample(target_logits, ((int64_t)s * B + v) * row_stride, V, dtype, T,
+                               uniform[(int64_t)s * B + v], &saw_nan, &mg);
+            if (margin)
+                margin[(int64_t)s * B + v] = mg;
         }
-        if (too_deep) {
-            err[s] = flags | ORA_DEPTH_GT_N;
-            continue;
-        }
-        int best_v = 0, best_d = 0;
-        for (int v = 0; v < B; v++) {
-            int ok = 1, dv = 0;
-            for (int u = v; par[u] != -1; u = par[u]) {
-                if (tok[u] != am[par[u]])
-                    ok = 0;
-                dv++;
-            }
-            if (ok && dv > best_d) {
-                best_d = dv;
-                best_v = v;
-            }
-        }
-        accept_len[s] = best_d;
-        for (int u = best_v; u != -1; u = par[u]) {
-            int du = 0;
-            for (int w = u; par[w] != -1; w = par[w])
-                du++;
-            path[du] = u;
-        }
-        bonus[s] = am[best_v];
-        err[s] = flags;
+        const int flags = tree_walk(parent + (int64_t)s * B, tokens + (int64_t)s * B, am, B, N,
+                                    &accept_len[s], accept_path + (int64_t)s * (N + 1), &bonus[s]);
+        err[s] = flags | (saw_nan ? ORA_NAN : 0);
     }
     return 0;
 }
