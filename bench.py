@@ -54,12 +54,13 @@ KERNELS = {
     "step": ["step_phase1", "step_scan_kernel", "step_phase2"],
     "tree": ["tree_build_kernel"],
     "commit": ["commit_kv_kernel"],
+    "sampled": ["sample_partial_kernel", "sample_select_kernel", "verify_walk_kernel"],
 }
 # the kernel whose dispatches count the launches of each entry point
 MARKER = {"topw": "topw_partial_kernel", "mask": "build_mask_kernel",
           "attention": ("attn_bf16_kernel", "attn_simple_kernel"),
           "verify": "argmax_partial_kernel", "step": "step_phase2", "tree": "tree_build_kernel",
-          "commit": "commit_kv_kernel"}
+          "commit": "commit_kv_kernel", "sampled": "sample_select_kernel"}
 
 
 def algorithmic(w):
@@ -81,6 +82,9 @@ def algorithmic(w):
     # best-first tree from the top-W lists: ids + log-probs read; parent, tokens, score
     # and the node count written
     b["tree"] = S * N * W * 8 + S * B * 12 + S * 4
+    # stochastic verification: the target rows once (the rescan of one 8192-logit piece
+    # per row is not counted), the uniforms, and the outputs of greedy verification
+    b["sampled"] = b["verify"] + S * B * 4
     return b, flops
 
 
@@ -224,7 +228,8 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
     per_call_us = {}
     calls_here = CALLS + (("step",) if hasattr(st, "step_ws") else ()) + \
         (("tree",) if hasattr(st, "tree_parent") else ()) + \
-        (("commit",) if hasattr(st, "commit_k") else ())
+        (("commit",) if hasattr(st, "commit_k") else ()) + \
+        (("sampled",) if hasattr(st, "smp_ws") else ())
     st.run()  # the tree call reads the top-W lists, the commit the accepted paths
     for c in calls_here:
         g = _capture([getattr(s, "run_fused" if c == "step" else c) for s in rot.steps])
@@ -313,7 +318,8 @@ def _kernel_hash(call):
     files = {"topw": ["topw.hip"], "mask": ["mask.hip"], "attention": ["attn.hip"],
              "verify": ["verify.hip"],
              "step": ["mask.hip", "topw.hip", "verify.hip", "attn.hip", "step.hip"],
-             "tree": ["tree.hip"], "commit": ["commit.hip"]}[call]
+             "tree": ["tree.hip"], "commit": ["commit.hip"],
+             "sampled": ["verify.hip", "sample.hip"]}[call]
     import re
     h = hashlib.sha256()
     for f in files + ["jt_internal.h"]:
@@ -361,7 +367,8 @@ def traffic_run(name, seed, reps=3, log=print):
     st = DeviceStep(w, "cuda:0")
     nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(footprint(st), 1))))
     rot = Rotation(st, nsets)
-    extra = ("tree",) + (("commit",) if hasattr(st, "commit_k") else ())
+    extra = ("tree",) + (("commit",) if hasattr(st, "commit_k") else ()) + \
+        (("sampled",) if hasattr(st, "smp_ws") else ())
     for c in CALLS + (("run_fused",) if hasattr(st, "step_ws") else ()) + extra:
         for i in range(reps * nsets):
             getattr(rot.steps[i % nsets], c)()
@@ -397,7 +404,7 @@ def traffic_summarize(name, fetch_dir, write_dir):
     calibration copy moved) / (what the counter read for it).  The traffic run launches the
     entry points one after the other (top-W, mask, attention, verify, then the fused step,
     whose 8-wave shapes also run attn_bf16_kernel), so dispatches are assigned in order."""
-    order = list(CALLS) + ["step", "tree", "commit"]
+    order = list(CALLS) + ["step", "tree", "commit", "sampled"]
     def hits(kname, call):
         return any(k in kname for k in KERNELS[call])
     def is_marker(kname, call):

@@ -237,6 +237,35 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
                                void *stream);
 
 /*
+ * Stochastic tree verification at temperature T > 0.  With a fixed draft every proposal
+ * is a point mass at the draft token, accepted with the target probability, and after a
+ * rejection the next token comes from the residual, so every committed token is the
+ * target's own draw (JetSpec review, inference, acceptance equation; JetSpec++ summary,
+ * appendices F.1 and F.3).  Sibling tokens being distinct, this is done as one draw per
+ * node, x[s,v] ~ softmax(target_logits[s,v,:] / T): the first token t, in id order, whose
+ * cumulative weight exceeds uniform[s,v] times the row's total weight.  Then the walk of
+ * jt_verify_greedy with x in place of the arg-max: v is accepted iff every edge of its
+ * root path carries the draw of its parent, v* is the deepest accepted node (lowest index
+ * on ties), accept_len = depth(v*), bonus = x[s,v*].  NaN entries weigh 0 and flag the
+ * sequence (JT_DEV_NAN); a row of -inf draws token 0.
+ *
+ *   target_logits [S*B, row_stride] dtype    uniform float [S,B], values in [0, 1)
+ *   parent, tokens, anc, depth, N, outputs and err as for jt_verify_greedy
+ *   sample_out    int32 [S,B] (optional) out: the draw at every node
+ * A draw whose uniform lies within about 1e-5 of its token's interval end (as a fraction of
+ * the row's weight) may go to the neighbouring token under a different summation order.
+ * Supported: temperature > 0 and finite; otherwise as jt_verify_greedy.
+ */
+size_t jt_verify_sampled_workspace_size(int32_t S, int32_t B, int32_t V, jt_dtype dtype);
+jt_status jt_verify_sampled(const void *target_logits, int64_t row_stride, int32_t V,
+                            jt_dtype dtype, float temperature, const float *uniform,
+                            const int32_t *parent, const int32_t *tokens, const uint64_t *anc,
+                            const int32_t *depth, int32_t S, int32_t B, int32_t N,
+                            int32_t *accept_len, int32_t *accept_path, int32_t *bonus,
+                            int32_t *sample_out, int32_t *err, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
  * Best-first construction of the draft tree from the per-depth candidate lists that
  * jt_topw_per_depth produces (paperlayer.ai JetSpec summary, appendix B "Tree-Drafting
  * Algorithm Details", section 2 and appendix E "Drafting"; JetSpec review, inference,

@@ -87,6 +87,13 @@ def test_host_validation_returns_before_launch():
     assert commit(dt=5) == 3
     assert commit() == 1
     assert commit(S=0) == 0
+    # sampled verification: temperature <= 0 or inf, N > 255, NULLs
+    def smp(T=1.0, N=8):
+        return L.jt_verify_sampled(nul, 1000, 1000, 1, ctypes.c_float(T), nul, nul, nul, nul,
+                                   nul, 1, 16, N, nul, nul, nul, nul, nul, nul, 0, nul)
+    assert smp(T=0.0) == 2 and smp(T=-1.0) == 2 and smp(T=float("inf")) == 2
+    assert smp(N=256) == 2
+    assert smp() == 1
 
 
 def test_workspace_queries_are_pure():

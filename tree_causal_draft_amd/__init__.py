@@ -24,7 +24,7 @@ EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
            "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
            "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy",
            "jt_step_workspace_size", "jt_draft_verify_step", "jt_build_tree_best_first",
-           "jt_commit_accepted_kv")
+           "jt_commit_accepted_kv", "jt_verify_sampled_workspace_size", "jt_verify_sampled")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -73,9 +73,13 @@ def lib() -> ctypes.CDLL:
         L.jt_commit_accepted_kv.argtypes = ([_vp, _vp, _i32, _vp, _vp] + [_i32] * 4 +
                                             [ctypes.c_int, _vp, _vp, _vp] + [_i32] * 3 +
                                             [_vp, _i32, _vp, _vp, _vp])
+        L.jt_verify_sampled_workspace_size.restype = _sz
+        L.jt_verify_sampled_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
+        L.jt_verify_sampled.argtypes = ([_vp, _i64, _i32, ctypes.c_int, ctypes.c_float] +
+                                        [_vp] * 5 + [_i32] * 3 + [_vp] * 6 + [_sz, _vp])
         for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
                    "jt_verify_greedy", "jt_draft_verify_step", "jt_build_tree_best_first",
-                   "jt_commit_accepted_kv"):
+                   "jt_commit_accepted_kv", "jt_verify_sampled"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -363,4 +367,39 @@ def commit_accepted_kv(accept_len, accept_path, k_tree, v_tree, k_cache, v_cache
                                        _ptr(err), _stream(stream)),
            "jt_commit_accepted_kv")
     return new_prefix_len, err
+
+
+def verify_sampled_workspace_size(S, B, V, dtype) -> int:
+    return int(lib().jt_verify_sampled_workspace_size(S, B, V, dtype))
+
+
+def verify_sampled(target_logits, parent, tokens, anc, depth, N, temperature, uniform, *, V=None,
+                   accept_len=None, accept_path=None, bonus=None, sample_out=None, err=None,
+                   workspace=None, stream=None):
+    """Stochastic verification: one draw per node from softmax(logits / T) at the given
+    uniforms [S,B], then the greedy walk.  Returns (accept_len, accept_path, bonus,
+    sample [S,B], err)."""
+    for t, n in ((target_logits, "target_logits"), (parent, "parent"), (tokens, "tokens"),
+                 (anc, "anc"), (depth, "depth"), (uniform, "uniform")):
+        _need(t, n)
+    if uniform.dtype != torch.float32:
+        raise JTError("uniform must be float32")
+    S, B = parent.shape
+    stride = target_logits.shape[-1]
+    V = stride if V is None else V
+    dt = _dt(target_logits)
+    dev = target_logits.device
+    e = lambda shape: torch.empty(shape, dtype=torch.int32, device=dev)
+    accept_len = e(S) if accept_len is None else accept_len
+    accept_path = e((S, N + 1)) if accept_path is None else accept_path
+    bonus = e(S) if bonus is None else bonus
+    sample_out = e((S, B)) if sample_out is None else sample_out
+    err = e(S) if err is None else err
+    ws, wsb = _workspace(verify_sampled_workspace_size(S, B, V, dt), dev, workspace)
+    _check(lib().jt_verify_sampled(_ptr(target_logits), stride, V, dt, float(temperature),
+                                   _ptr(uniform), _ptr(parent), _ptr(tokens), _ptr(anc),
+                                   _ptr(depth), S, B, N, _ptr(accept_len), _ptr(accept_path),
+                                   _ptr(bonus), _ptr(sample_out), _ptr(err), _ptr(ws), wsb,
+                                   _stream(stream)), "jt_verify_sampled")
+    return accept_len, accept_path, bonus, sample_out, err
 

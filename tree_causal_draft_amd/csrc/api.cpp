@@ -220,6 +220,41 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
                          as_stream(stream));
 }
 
+size_t jt_verify_sampled_workspace_size(int32_t S, int32_t B, int32_t V, jt_dtype dtype)
+{
+    if (verify_shape(S, B, V, 0, dtype) != JT_OK || S == 0)
+        return 0;
+    return sample_workspace(S, B, V);
+}
+
+jt_status jt_verify_sampled(const void *target_logits, int64_t row_stride, int32_t V,
+                            jt_dtype dtype, float temperature, const float *uniform,
+                            const int32_t *parent, const int32_t *tokens, const uint64_t *anc,
+                            const int32_t *depth, int32_t S, int32_t B, int32_t N,
+                            int32_t *accept_len, int32_t *accept_path, int32_t *bonus,
+                            int32_t *sample_out, int32_t *err, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    jt_status st = verify_shape(S, B, V, N, dtype);
+    if (st != JT_OK)
+        return st;
+    if (row_stride < V || !(temperature > 0.f) || !(temperature < INFINITY))
+        return JT_ERR_SHAPE;
+    if (S == 0)
+        return JT_OK;
+    if (!target_logits || !uniform || !parent || !tokens || !anc || !depth || !accept_len ||
+        !accept_path || !bonus)
+        return JT_ERR_NULL;
+    const size_t need = sample_workspace(S, B, V);
+    if (!workspace || workspace_bytes < need)
+        return JT_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return JT_ERR_ALIGN;
+    return launch_verify_sampled(target_logits, row_stride, V, dtype, temperature, uniform,
+                                 parent, tokens, anc, depth, S, B, N, accept_len, accept_path,
+                                 bonus, sample_out, err, workspace, as_stream(stream));
+}
+
 size_t jt_step_workspace_size(int32_t S, int32_t B, int32_t N, int32_t W, int32_t V, int32_t Hq,
                               int32_t Hkv, int32_t d, int32_t max_prefix, int32_t block_size,
                               jt_dtype dtype)

@@ -144,6 +144,21 @@ struct StepLaunch {
     int32_t *depth;
     int32_t *accept_len, *accept_path, *bonus, *argmax_out, *err;
 };
+// the walk of verify.hip over per-row arg-max keys (nchunk keys per row)
+jt_status launch_verify_walk(const int32_t *parent, const int32_t *tokens, const uint64_t *anc,
+                             const int32_t *depth, int S, int B, int N, int nchunk,
+                             const uint64_t *keys, const uint32_t *nan, int32_t *accept_len,
+                             int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                             int32_t *err, hipStream_t st);
+
+size_t sample_workspace(int S, int B, int V);
+jt_status launch_verify_sampled(const void *logits, int64_t row_stride, int V, int dtype,
+                                float temperature, const float *uniform, const int32_t *parent,
+                                const int32_t *tokens, const uint64_t *anc, const int32_t *depth,
+                                int S, int B, int N, int32_t *accept_len, int32_t *accept_path,
+                                int32_t *bonus, int32_t *sample_out, int32_t *err, void *ws,
+                                hipStream_t st);
+
 jt_status launch_build_tree(const int32_t *ids, const float *logprob, const float *entropy,
                             float w_lp, float w_ent, const int32_t *root_token, int S, int N,
                             int W, int B, int32_t *parent, int32_t *tokens, float *score,

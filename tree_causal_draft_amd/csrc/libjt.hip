@@ -4,6 +4,7 @@
 #include "mask.hip"
 #include "topw.hip"
 #include "verify.hip"
+#include "sample.hip"
 #include "attn.hip"
 #include "step.hip"
 #include "tree.hip"

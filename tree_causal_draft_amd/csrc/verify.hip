@@ -439,4 +439,16 @@ jt_status launch_verify(const void *logits, int64_t row_stride, int V, int dtype
     return launch_status(hipGetLastError());
 }
 
+jt_status launch_verify_walk(const int32_t *parent, const int32_t *tokens, const uint64_t *anc,
+                             const int32_t *depth, int S, int B, int N, int nchunk,
+                             const uint64_t *keys, const uint32_t *nan, int32_t *accept_len,
+                             int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                             int32_t *err, hipStream_t st)
+{
+    hipLaunchKernelGGL(verify_walk_kernel, dim3(S), dim3(256), 0, st, B, N, nchunk, keys, nan,
+                       parent, tokens, anc, depth, accept_len, accept_path, bonus, argmax_out,
+                       err);
+    return launch_status(hipGetLastError());
+}
+
 } // namespace jt

@@ -14,7 +14,8 @@ import numpy as np
 import torch
 
 from . import (build_tree_best_first, build_tree_mask, commit_accepted_kv, draft_verify_step,
-               step_workspace_size, topw_per_depth,
+               step_workspace_size, topw_per_depth, verify_sampled,
+               verify_sampled_workspace_size,
                tree_attention, tree_attention_workspace_size, topw_workspace_size, verify_greedy,
                verify_workspace_size, JT_BF16, JT_F32)
 from .workload import Workload
@@ -86,6 +87,16 @@ class DeviceStep:
             self.err_verify = torch.empty(S, dtype=torch.int32, device=dev)
             nb = verify_workspace_size(S, B, cfg.V, dt)
             self.verify_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+            # stochastic verification (temperature 1) at seeded uniforms, into its own outputs
+            rng = np.random.default_rng(12345)
+            self.uniform = to_device(rng.random((S, B)).astype(np.float32), dev)
+            self.smp_accept_len = torch.empty(S, dtype=torch.int32, device=dev)
+            self.smp_accept_path = torch.empty((S, N + 1), dtype=torch.int32, device=dev)
+            self.smp_bonus = torch.empty(S, dtype=torch.int32, device=dev)
+            self.smp_sample = torch.empty((S, B), dtype=torch.int32, device=dev)
+            self.err_smp = torch.empty(S, dtype=torch.int32, device=dev)
+            nb = verify_sampled_workspace_size(S, B, cfg.V, dt)
+            self.smp_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
 
         if parts == ("topw", "mask", "attn", "verify") and dt == JT_BF16:
             self.err_step = torch.empty(S, dtype=torch.int32, device=dev)
@@ -126,6 +137,13 @@ class DeviceStep:
         verify_greedy(self.target, self.parent, self.tokens, self.anc, self.depth, self.cfg.N,
                       accept_len=self.accept_len, accept_path=self.accept_path, bonus=self.bonus,
                       argmax_out=self.argmax, err=self.err_verify, workspace=self.verify_ws)
+
+    def sampled(self, temperature=1.0):
+        """Stochastic verification of the same tree (reads anc / depth of the last mask)."""
+        verify_sampled(self.target, self.parent, self.tokens, self.anc, self.depth, self.cfg.N,
+                       temperature, self.uniform, accept_len=self.smp_accept_len,
+                       accept_path=self.smp_accept_path, bonus=self.smp_bonus,
+                       sample_out=self.smp_sample, err=self.err_smp, workspace=self.smp_ws)
 
     def run(self):
         """The four calls in order on the current stream."""
