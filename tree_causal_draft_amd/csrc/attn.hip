@@ -251,7 +251,7 @@ constexpr int kBtCap = 1024;  // block-table entries of one chunk staged in LDS
 
 // Work decomposition shared by the host launcher and the kernels.
 struct AttnPlan {
-    int nwr;       // waves per workgroup, one 32-row block each (2, 4 or 8)
+    int nwr;       // waves per workgroup, one 32-row block each (4 or 8)
     int rt;        // rows per workgroup = 32 * nwr
     int n_rtiles;  // row tiles per (s, g)
     int units;     // S * Hkv * n_rtiles
@@ -273,7 +273,11 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
 {
     AttnPlan p;
     const int rows = (Hq / Hkv) * B;
-    p.nwr = rows <= 64 ? 2 : (rows <= 128 ? 4 : 8);
+    // At least 4 waves: a 2-wave workgroup leaves the compiler a 512-register budget (its
+    // LDS allows one wave per SIMD), and it then keeps the O accumulators in AGPRs and
+    // copies all 64 to VGPRs and back around every tile (measured 15.9 us against 15.0 us
+    // with 4 waves, two of them idle, on the 16-node, 1024-key shape).
+    p.nwr = rows <= 128 ? 4 : 8;
     p.rt = 32 * p.nwr;
     p.n_rtiles = (rows + p.rt - 1) / p.rt;
     p.units = S * Hkv * p.n_rtiles;
@@ -1080,7 +1084,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
         if (grp == 1 && wave_has_rows)  // B's PV of the last tile
             pv(stage((ntiles - 1) & 3) + TILEB, pf);
     } else {
-        // ---- 2 or 4 waves (few rows), double buffering: after barrier j, tile j + 1 goes
+        // ---- 4 waves (few rows), double buffering: after barrier j, tile j + 1 goes
         // to the stage tile j - 1 used, which every wave has finished.
         if (0 < ntiles && !have_pro[0])
             issue_tile(kbeg, stage(0));
@@ -1154,7 +1158,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
 }
 
 template <int D, int NWR>
-__global__ void __launch_bounds__(64 * NWR)
+__global__ void __launch_bounds__(64 * NWR, 8 / NWR)  // 2 waves per SIMD: no AGPR round trips
 attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[AttnLds<D, NWR>::BYTES];
@@ -1196,9 +1200,7 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
 {
     const AttnPlan p = attn_plan(a.S, a.B, a.Hq, a.Hkv, a.max_prefix, a.block_table ? a.block_size : 0);
     const AttnWs w = attn_ws_split(p, ws);
-    if (p.nwr == 2)
-        launch_main<D, 2>(a, p, w, st);
-    else if (p.nwr == 4)
+    if (p.nwr == 4)
         launch_main<D, 4>(a, p, w, st);
     else
         launch_main<D, 8>(a, p, w, st);

@@ -164,10 +164,6 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
 {
     StepPlan sp;
     sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size);
-    if (sp.ap.nwr < 4) {
-        sp.ap.nwr = 4;  // same rows, chunks and results; the other two waves idle
-        sp.ap.rt = 128;
-    }
     const bool split = sp.ap.nwr == 8;  // scans in a launch of their own
     const int nw = split ? 4 : sp.ap.nwr;  // waves per scan workgroup
     const int rows_d = S * N, rows_t = S * B;
