@@ -484,10 +484,10 @@ __device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPla
         const int v = r / G, h = g * G + r % G;
         const int64_t row_g = ((int64_t)s * B + v) * a.Hq + h;
         uint4 pk;
-        pk.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
-        pk.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
-        pk.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
+        pk.x = f32x2_to_bf16x2(acc[0] * inv, acc[1] * inv);
+        pk.y = f32x2_to_bf16x2(acc[2] * inv, acc[3] * inv);
+        pk.z = f32x2_to_bf16x2(acc[4] * inv, acc[5] * inv);
+        pk.w = f32x2_to_bf16x2(acc[6] * inv, acc[7] * inv);
         *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + row_g * D + sgm * 8) = pk;
         if (a.lse && sgm == 0)
             a.lse[row_g] = l > 0.f ? (M + __log2f(l)) * kLn2 : -INFINITY;
@@ -727,7 +727,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     // as prefix keys right away (valid addresses for any key below max_prefix) and kept
     // if, once the length is known, every key of the tile is an in-range prefix key --
     // the same copy the exact path would have made.
-    constexpr int NPRO = NST == 4 ? 2 : 1;  // tiles fetched before the loop
+    constexpr int NPRO = 2;  // tiles fetched before the loop (every stage of a double buffer)
     bool spec[NPRO];
 #pragma unroll
     for (int k = 0; k < NPRO; ++k) {
@@ -768,14 +768,21 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     // the wave's 32 ancestor rows, later parked in LDS (lane hh holds words 2hh, 2hh+1)
     uint64_t anc_a, anc_b;
     if constexpr (kTreeRows) {
-        // built in the stage that the speculative copies leave free; the loop's first
-        // copy into it is issued after the first barrier, when every wave has read it
-        const uint32_t tr_base = lds_off(stage(NPRO));
+        // built in a stage the speculative copies leave free (the loop's first copy into
+        // it is issued after the first barrier, when every wave has read it), or, when
+        // they fill every stage, in the block-table and row areas, which are written only
+        // after a barrier that follows the last read here
+        static_assert(AttnLds<D, NWR>::BYTES - AttnLds<D, NWR>::BT_OFF >= JT_MAX_NODES * 36,
+                      "room for the tree rows");
+        const uint32_t tr_base = NPRO < NST ? lds_off(stage(NPRO))
+                                            : lds_off(lds + AttnLds<D, NWR>::BT_OFF);
         tree_rows_lds(par_v, B, tr_base);
         uint64_t rw[4];
         lds_read_row(tr_base + (uint32_t)vrow * 32u, rw);
         anc_a = hh ? rw[2] : rw[0];
         anc_b = hh ? rw[3] : rw[1];
+        if constexpr (NPRO == NST)
+            barrier_keep_dma();
     } else {
         const uint64_t *anc_src = a.anc + ((int64_t)s * B + vrow) * 4 + 2 * hh;
         anc_a = anc_src[0];
@@ -1084,16 +1091,24 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
         if (grp == 1 && wave_has_rows)  // B's PV of the last tile
             pv(stage((ntiles - 1) & 3) + TILEB, pf);
     } else {
-        // ---- 4 waves (few rows), double buffering: after barrier j, tile j + 1 goes
-        // to the stage tile j - 1 used, which every wave has finished.
+        // ---- 4 waves (few rows), double buffering: tiles 0 and 1 are fetched before the
+        // loop (into the two stages); after barrier j (j >= 1), tile j + 1 goes to the
+        // stage tile j - 1 used, which every wave has finished.  Before barrier 0 a wave
+        // waits for its share of tile 0 only (tile 1's copies, issued after it, may still
+        // run); later only tile j can be in flight.
         if (0 < ntiles && !have_pro[0])
             issue_tile(kbeg, stage(0));
+        if (1 < ntiles && !have_pro[1])
+            issue_tile(kbeg + TILE, stage(1));
         for (int j = 0; j < ntiles; ++j) {
             const int k = j & 1;
             const int kt = kbeg + j * TILE;
-            wait_vm<0>();
+            if (j == 0 && 1 < ntiles)
+                wait_vm<NOPS>();
+            else
+                wait_vm<0>();
             barrier_keep_dma();
-            if (j + 1 < ntiles)
+            if (j >= 1 && j + 1 < ntiles)
                 issue_tile(kt + TILE, stage(k ^ 1));
             if (wave_has_rows)
                 compute_tile(stage(k), stage(k) + TILEB, vis_window(kt));
@@ -1104,6 +1119,15 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     const float l = l_i + __shfl_xor(l_i, 32, kWave);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t slot0 = ((int64_t)unit * pl.n_chunks + chunk) * pl.rt + wr * 32;
+    // The accumulator spreads one row over the registers of 16 lanes.  A row-major copy of
+    // the wave's 32 rows in LDS (row pitch D*2 + 16 bytes, which staggers the banks) lets
+    // every lane store 16 contiguous bytes of a row instead of 8-byte pieces of 32 rows.
+    constexpr int OPITCH = D * 2 + 16;
+    static_assert(NWR * 32 * OPITCH <= NST * BUFB, "epilogue staging fits the tile stages");
+    wait_dma();       // no tile copy may still be landing in the stages
+    __syncthreads();  // every wave has finished reading the tiles
+    // stored only now: vmcnt counts stores too, so a store before wait_dma() would make it
+    // wait for the store's completion (measured: about 2 us per workgroup)
     if (wave_has_rows && row_ok && hh == 0) {
         if (pl.n_chunks == 1) {
             if (a.lse)
@@ -1112,13 +1136,6 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
             ws.ml[slot0 + col] = make_float2(m_i, l);
         }
     }
-    // The accumulator spreads one row over the registers of 16 lanes.  A row-major copy of
-    // the wave's 32 rows in LDS (row pitch D*2 + 16 bytes, which staggers the banks) lets
-    // every lane store 16 contiguous bytes of a row instead of 8-byte pieces of 32 rows.
-    constexpr int OPITCH = D * 2 + 16;
-    static_assert(NWR * 32 * OPITCH <= NST * BUFB, "epilogue staging fits the tile stages");
-    wait_dma();       // no tile copy may still be landing in the stages
-    __syncthreads();  // every wave has finished reading the tiles
     if (wave_has_rows) {
         uint8_t *ob = L0 + wid * 32 * OPITCH;
 #pragma unroll
@@ -1127,10 +1144,8 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
             for (int q = 0; q < 4; ++q) {
                 const int d0 = db * 32 + 8 * q + 4 * hh;
                 uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(o_acc[db][4 * q] * inv) |
-                       ((uint32_t)f32_to_bf16(o_acc[db][4 * q + 1] * inv) << 16);
-                pk.y = (uint32_t)f32_to_bf16(o_acc[db][4 * q + 2] * inv) |
-                       ((uint32_t)f32_to_bf16(o_acc[db][4 * q + 3] * inv) << 16);
+                pk.x = f32x2_to_bf16x2(o_acc[db][4 * q] * inv, o_acc[db][4 * q + 1] * inv);
+                pk.y = f32x2_to_bf16x2(o_acc[db][4 * q + 2] * inv, o_acc[db][4 * q + 3] * inv);
                 *reinterpret_cast<uint2 *>(ob + col * OPITCH + d0 * 2) = pk;
             }
         // the rows written by other lanes of this wave are read back below

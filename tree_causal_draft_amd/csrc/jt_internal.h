@@ -14,14 +14,20 @@ __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_flo
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bf16, round to nearest even (finite inputs; NaN stays NaN)
+// float -> bf16, round to nearest even (NaN stays NaN): the hardware conversion
+// (v_cvt_pk_bf16_f32).  A bit-twiddling version compiled to a branch per value around the
+// NaN test, about 20 instructions each -- 3 us per workgroup in the attention epilogue.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two floats -> packed bf16 pair (lo in bits 0..15), one conversion instruction
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Monotone map of a float to uint32 for "value descending" comparisons.
