@@ -52,6 +52,7 @@ struct StepPlan {
 };
 
 constexpr int kStepRowsPerBlock = 4;  // phase 2: top-W rows merged per workgroup (one per wave)
+constexpr int kPhase1Slots = 2 * 256;  // phase-1 workgroups resident at once: 2 per CU, 256 CUs
 
 template <int D, int NWR> struct StepLds {
     static constexpr int TOPW = NWR * (kWaveCap + 2 * JT_MAX_W) * 8;
@@ -157,8 +158,7 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Work decomposition of the fused step.  For few rows the phase-1 grid should fit the
-// chip in one round (two 4-wave workgroups per CU), so the logit scans take two pieces
-// (top-W) per wave and up to four 8192-logit sub-chunks (arg-max) per workgroup.
+// chip in one round (two 4-wave workgroups per CU); see the scan plan below.
 static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, int max_prefix,
                           int block_size)
 {
@@ -171,21 +171,40 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
         sp.tp = topw_plan(rows_d, V);
         sp.gp = arg_plan(rows_t, V);
     } else {
-        sp.tp.npiece = (V + kPiece - 1) / kPiece;
-        sp.tp.ppw = (sp.tp.npiece + kMaxLists - 1) / kMaxLists;
-        if (sp.tp.ppw < 2 && rows_d * sp.tp.npiece > 4 * 256)
-            sp.tp.ppw = 2;
-        sp.tp.nlist = (sp.tp.npiece + sp.tp.ppw - 1) / sp.tp.ppw;
-        sp.gp.nsub = (V + kArgSub - 1) / kArgSub;
-        int want = rows_t > 0 ? (256 + rows_t - 1) / rows_t : 1;  // chunks per row
-        want = max(want, (sp.gp.nsub + 3) / 4);                     // at most ~4 sub-chunks each
-        int spw = (sp.gp.nsub + want - 1) / want;
-        if (spw < 1)
-            spw = 1;
-        while ((sp.gp.nsub + spw - 1) / spw > kArgMaxChunks)
-            ++spw;
+        // Phase 1 should run in one round of two 4-wave workgroups per CU.  Top-W pieces
+        // per wave cost most (the top-W role is the longest scan: 9.1 us with one piece per
+        // wave against 10.4 us with two, for 16 rows of 151,936), so take the fewest pieces
+        // per wave, then the fewest arg-max sub-chunks per workgroup, that fit; if nothing
+        // fits, two pieces per wave and about four sub-chunks per workgroup.
+        const int npiece = (V + kPiece - 1) / kPiece;
+        const int nsub = (V + kArgSub - 1) / kArgSub;
+        const int ppw0 = (npiece + kMaxLists - 1) / kMaxLists;
+        const int nA = sp.ap.units * sp.ap.n_chunks;
+        int ppw = -1, spw = -1;
+        for (int pw = ppw0; pw <= ppw0 + 1 && ppw < 0; ++pw)
+            for (int sw = 1; sw <= 8 && ppw < 0; ++sw) {
+                const int nch = (nsub + sw - 1) / sw;
+                if (nch > kArgMaxChunks)
+                    continue;
+                const long nT = ((long)rows_d * ((npiece + pw - 1) / pw) + nw - 1) / nw;
+                if (nA + nT + (long)rows_t * nch + S <= kPhase1Slots) {
+                    ppw = pw;
+                    spw = sw;
+                }
+            }
+        if (ppw < 0) {
+            ppw = max(2, ppw0);
+            int want = max(rows_t > 0 ? (256 + rows_t - 1) / rows_t : 1, (nsub + 3) / 4);
+            spw = max(1, (nsub + want - 1) / want);
+            while ((nsub + spw - 1) / spw > kArgMaxChunks)
+                ++spw;
+        }
+        sp.tp.npiece = npiece;
+        sp.tp.ppw = ppw;
+        sp.tp.nlist = (npiece + ppw - 1) / ppw;
+        sp.gp.nsub = nsub;
         sp.gp.sub_per_wg = spw;
-        sp.gp.nchunk = (sp.gp.nsub + spw - 1) / spw;
+        sp.gp.nchunk = (nsub + spw - 1) / spw;
     }
     sp.nA = sp.ap.units * sp.ap.n_chunks;
     sp.nT = (rows_d * sp.tp.nlist + nw - 1) / nw;
