@@ -10,64 +10,38 @@
 // whose cumulative weight exceeds r * Z.
 //
 // Three launches:
-//   sample_partial_kernel  streams every row once (HBM-bound, like the arg-max scan): per
-//                          8192-logit sub-chunk, its maximum m and weight sum
-//                          S = sum exp((x - m) / T); NaN entries weigh 0 and are flagged;
-//   sample_select_kernel   one workgroup per row: Z from the sub-chunk sums, the sub-chunk
-//                          whose cumulative weight passes r * Z, then a rescan of that one
-//                          sub-chunk (an L2 / Infinity Cache hit) with block scans for the
-//                          exact token; the draw goes out as a one-entry arg-max key;
+//   sample_partial_kernel  streams every row once (HBM-bound, like the arg-max scan): each
+//                          wave owns 2048-logit pieces of a row and writes every piece's
+//                          maximum m and weight sum S = sum exp((x - m) / T) with wave
+//                          reductions only; NaN entries weigh 0 and are flagged;
+//   sample_select_kernel   one workgroup per row: Z and the piece whose cumulative weight
+//                          passes r * Z from one block scan over the piece sums, then a
+//                          rescan of that one piece (an L2 / Infinity Cache hit) with one
+//                          block scan in token order for the exact token; the draw goes
+//                          out as a one-entry arg-max key;
 //   verify_walk_kernel     the greedy walk, reading the draws as its arg-max.
 #include "jt_internal.h"
 
 namespace jt {
 
 constexpr int kSmpThreads = 256;
+constexpr int kSmpPiece = 2048;       // logits per wave piece (32 per lane)
+constexpr int kSmpMaxWaves = 16384;   // partial waves to aim for at most
 
 struct SmpPlan {
-    int nsub, sub_per_wg, nrun;  // sub-chunks per row, per workgroup, workgroups per row
+    int npiece;  // pieces per row
+    int ppw;     // pieces per wave
+    int nwave;   // waves per row
 };
 
 static SmpPlan smp_plan(int rows, int V)
 {
     SmpPlan p;
-    p.nsub = (V + kArgSub - 1) / kArgSub;
-    const int want = rows > 0 ? (2048 + rows - 1) / rows : 1;  // workgroups per row
-    int spw = (p.nsub + want - 1) / want;
-    if (spw < 1)
-        spw = 1;
-    p.sub_per_wg = spw;
-    p.nrun = (p.nsub + spw - 1) / spw;
+    p.npiece = (V + kSmpPiece - 1) / kSmpPiece;
+    const long total = (long)rows * p.npiece;
+    p.ppw = (int)max(1L, (total + kSmpMaxWaves - 1) / kSmpMaxWaves);
+    p.nwave = (p.npiece + p.ppw - 1) / p.ppw;
     return p;
-}
-
-// Words of a thread's share of sub-chunk sc: element k of load i is element
-// (tid + NT*i)*E + k of the sub-chunk (entries at or past V are left 0 and masked later).
-template <typename T, int NT, int L>
-__device__ __forceinline__ void smp_load(const T *row, int64_t base, int V, int tid, bool aligned,
-                                         uint4 (&u)[L])
-{
-    constexpr int E = AVec<T>::kElems;
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
-        if (aligned && e0 + E <= V) {
-            u[i] = *reinterpret_cast<const uint4 *>(row + e0);
-        } else {
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                const int64_t e = e0 + k;
-                if (e < V) {
-                    if constexpr (sizeof(T) == 2)
-                        w[k >> 1] |= (uint32_t)row[e] << (16 * (k & 1));
-                    else
-                        w[k] = __float_as_uint(row[e]);
-                }
-            }
-            u[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
 }
 
 template <typename T>
@@ -82,6 +56,27 @@ __device__ __forceinline__ void smp_unpack(const uint4 &u, float (&x)[AVec<T>::k
     }
 }
 
+// 16 bytes of a row starting at element e0 (entries at or past V read as 0 bits)
+template <typename T>
+__device__ __forceinline__ uint4 smp_load16(const T *row, int64_t e0, int V, bool aligned)
+{
+    constexpr int E = AVec<T>::kElems;
+    if (aligned && e0 + E <= V)
+        return *reinterpret_cast<const uint4 *>(row + e0);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int64_t e = e0 + k;
+        if (e < V) {
+            if constexpr (sizeof(T) == 2)
+                w[k >> 1] |= (uint32_t)row[e] << (16 * (k & 1));
+            else
+                w[k] = __float_as_uint(row[e]);
+        }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // weight of one logit against reference m: exp((x - m) / T) as exp2((x - m) * c), c =
 // log2(e) / T; a NaN, -inf or padding entry weighs 0
 __device__ __forceinline__ float smp_weight(float x, float m, float c, bool in_range)
@@ -90,20 +85,12 @@ __device__ __forceinline__ float smp_weight(float x, float m, float c, bool in_r
     return (in_range && x == x && x != -INFINITY) ? e : 0.f;
 }
 
-__device__ __forceinline__ float block_sum_f32(float v, float *red)
+__device__ __forceinline__ float wave_sum_f32(float v)
 {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         v += __shfl_xor(v, o, kWave);
-    __syncthreads();
-    if (lane == 0)
-        red[wid] = v;
-    __syncthreads();
-    float t = 0.f;
-    for (int w = 0; w < nw; ++w)
-        t += red[w];
-    return t;
+    return v;
 }
 __device__ __forceinline__ float block_max_f32(float v, float *red)
 {
@@ -143,63 +130,72 @@ __device__ __forceinline__ float block_excl_scan_f32(float v, float *red, float 
     return before + inc - v;
 }
 
-// Per (row, run of sub-chunks): each sub-chunk's (max, weight sum), and the run's NaN bit.
+// Each wave owns ppw consecutive 2048-logit pieces of one row (lane l holds elements
+// (l + 64 i) * E .. + E - 1 of a piece) and writes each piece's (max, weight sum) and NaN
+// bit; no workgroup barrier.  The next piece's loads are issued before the current one is
+// reduced.
 template <typename T>
 __global__ void __launch_bounds__(kSmpThreads)
 sample_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, float c,
-                      SmpPlan p, float2 *__restrict__ ws_ms, uint32_t *__restrict__ ws_nan,
-                      bool aligned)
+                      SmpPlan p, int rows, float2 *__restrict__ ws_ms,
+                      uint32_t *__restrict__ ws_nan, bool aligned)
 {
     constexpr int E = AVec<T>::kElems;
-    constexpr int NT = kSmpThreads;
-    constexpr int L = kArgSub / (E * NT);
-    __shared__ float red[NT / 64];
-    const int tid = threadIdx.x;
-    const int row_idx = blockIdx.x / p.nrun, run = blockIdx.x % p.nrun;
-    const T *row = logits + (int64_t)row_idx * row_stride;
-    const int sc0 = run * p.sub_per_wg, sc1 = min(p.nsub, sc0 + p.sub_per_wg);
-    bool nan = false;
-    uint4 u[L];
-    if (sc0 < sc1)
-        smp_load<T, NT, L>(row, (int64_t)sc0 * kArgSub, V, tid, aligned, u);
-    for (int sc = sc0; sc < sc1; ++sc) {
-        const int64_t base = (int64_t)sc * kArgSub;
+    constexpr int L = kSmpPiece / (kWave * E);  // 16-byte loads per lane per piece
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (kSmpThreads / kWave) + (threadIdx.x >> 6);
+    if (gw >= rows * p.nwave)
+        return;
+    const int r = gw / p.nwave, wv = gw % p.nwave;
+    const T *row = logits + (int64_t)r * row_stride;
+    const int pc0 = wv * p.ppw, pc1 = min(p.npiece, pc0 + p.ppw);
+    uint4 nxt[L];
+    auto load = [&](int pc, uint4 (&u)[L]) {
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            u[i] = smp_load16<T>(row, (int64_t)pc * kSmpPiece + (int64_t)(lane + kWave * i) * E, V,
+                                 aligned);
+    };
+    if (pc0 < pc1)
+        load(pc0, nxt);
+    for (int pc = pc0; pc < pc1; ++pc) {
         float x[L][E];
 #pragma unroll
         for (int i = 0; i < L; ++i)
-            smp_unpack<T>(u[i], x[i]);
-        if (sc + 1 < sc1)  // the next sub-chunk's loads overlap this one's reductions
-            smp_load<T, NT, L>(row, base + kArgSub, V, tid, aligned, u);
+            smp_unpack<T>(nxt[i], x[i]);
+        if (pc + 1 < pc1)
+            load(pc + 1, nxt);
+        const int64_t base = (int64_t)pc * kSmpPiece;
         float m = -INFINITY;
+        bool nan = false;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
+            const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
 #pragma unroll
-            for (int k = 0; k < E; ++k) {
+            for (int k = 0; k < E; ++k)
                 if (e0 + k < V) {
                     nan |= x[i][k] != x[i][k];
                     m = fmaxf(m, x[i][k]);
                 }
-            }
         }
-        const float M = block_max_f32(m, red);
+        const float M = wave_max_f32(m);
         float s = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int i = 0; i < L; ++i) {
-                const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
+                const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
 #pragma unroll
                 for (int k = 0; k < E; ++k)
                     s += smp_weight(x[i][k], M, c, e0 + k < V);
             }
         }
-        const float S = block_sum_f32(s, red);
-        if (tid == 0)
-            ws_ms[(int64_t)row_idx * p.nsub + sc] = make_float2(M, S);
+        const float S = wave_sum_f32(s);
+        const bool any_nan = __ballot(nan) != 0ull;
+        if (lane == 0) {
+            ws_ms[(int64_t)r * p.npiece + pc] = make_float2(M, S);
+            ws_nan[(int64_t)r * p.npiece + pc] = any_nan ? 1u : 0u;
+        }
     }
-    const bool any = __syncthreads_or(nan);
-    if (tid == 0)
-        ws_nan[blockIdx.x] = any ? 1u : 0u;
 }
 
 // One workgroup per row: the draw.  Writes a one-entry arg-max key (any nonzero order
@@ -214,130 +210,130 @@ sample_select_kernel(const T *__restrict__ logits, int64_t row_stride, int V, fl
 {
     constexpr int E = AVec<T>::kElems;
     constexpr int NT = kSmpThreads;
-    constexpr int L = kArgSub / (E * NT);
+    constexpr int PER = kSmpPiece / NT;  // logits of the rescanned piece per thread (8)
+    static_assert(PER % E == 0, "whole 16-byte loads per thread");
     __shared__ float red[NT / 64];
-    __shared__ int pick;
+    __shared__ int pick, lo_pos, hi_pos;
+    __shared__ float pick_before;
     const int tid = threadIdx.x;
     const int r = blockIdx.x;
-    const float2 *ms = ws_ms + (int64_t)r * p.nsub;
+    const float2 *ms = ws_ms + (int64_t)r * p.npiece;
     const T *row = logits + (int64_t)r * row_stride;
 
     // row maximum and NaN bit
     float m = -INFINITY;
-    for (int i = tid; i < p.nsub; i += NT)
-        m = fmaxf(m, ms[i].x);
-    const float M = block_max_f32(m, red);
     uint32_t nb = 0u;
-    for (int i = tid; i < p.nrun; i += NT)
-        nb |= ws_nan[(int64_t)r * p.nrun + i];
+    for (int i = tid; i < p.npiece; i += NT) {
+        m = fmaxf(m, ms[i].x);
+        nb |= ws_nan[(int64_t)r * p.npiece + i];
+    }
+    const float M = block_max_f32(m, red);
     const bool nan = __syncthreads_or(nb != 0u);
     int draw = 0;  // a row with no finite maximum draws token 0, like its arg-max
     if (M != -INFINITY) {
-        // sub-chunk weights against M, Z, and the sub-chunk where the cumulative weight
-        // passes r * Z (blocks of NT sub-chunks, scanned in order)
+        auto piece_w = [&](int i) {
+            const float2 q = ms[i];
+            return q.x == -INFINITY ? 0.f : q.y * __builtin_amdgcn_exp2f((q.x - M) * c);
+        };
+        // Z, then the piece where the cumulative weight passes r * Z: one block scan per
+        // NT pieces (one in all for rows up to 524,288 logits)
         float Z = 0.f;
-        for (int i0 = 0; i0 < p.nsub; i0 += NT) {
+        for (int i0 = 0; i0 < p.npiece; i0 += NT) {
             const int i = i0 + tid;
-            const float2 q = i < p.nsub ? ms[i] : make_float2(-INFINITY, 0.f);
-            const float w = q.x == -INFINITY ? 0.f : q.y * __builtin_amdgcn_exp2f((q.x - M) * c);
-            Z += block_sum_f32(w, red);
+            float tot;
+            block_excl_scan_f32(i < p.npiece ? piece_w(i) : 0.f, red, &tot);
+            Z += tot;
         }
         const float target = uniform[r] * Z;
+        if (tid == 0) {
+            pick = INT_MAX;
+            pick_before = 0.f;
+        }
         float carry = 0.f;
-        int sc = -1;
-        for (int i0 = 0; i0 < p.nsub && sc < 0; i0 += NT) {
+        int pc = -1;
+        float before_pc = 0.f;
+        for (int i0 = 0; i0 < p.npiece && pc < 0; i0 += NT) {
             const int i = i0 + tid;
-            const float2 q = i < p.nsub ? ms[i] : make_float2(-INFINITY, 0.f);
-            const float w = q.x == -INFINITY ? 0.f : q.y * __builtin_amdgcn_exp2f((q.x - M) * c);
+            const float w = i < p.npiece ? piece_w(i) : 0.f;
             float tot;
             const float before = carry + block_excl_scan_f32(w, red, &tot);
-            __syncthreads();
-            if (tid == 0)
-                pick = INT_MAX;
-            __syncthreads();
-            if (i < p.nsub && w > 0.f && before + w > target && before <= target)
+            if (w > 0.f && before <= target && before + w > target)
                 atomicMin(&pick, i);
             __syncthreads();
-            if (pick != INT_MAX)
-                sc = pick;
-            carry += tot;
+            if (pick != INT_MAX && i == pick)
+                pick_before = before;
             __syncthreads();
+            if (pick != INT_MAX) {
+                pc = pick;
+                before_pc = pick_before;
+            }
+            carry += tot;
         }
-        // rounding can leave r * Z past the last sub-chunk: take the last with weight
-        __shared__ int last_sc;
-        if (sc < 0) {
+        if (pc < 0) {
+            // rounding left r * Z past the last piece: the last piece with weight, entered
+            // at its end (its last weighted logit is drawn below)
             if (tid == 0) {
-                last_sc = 0;
-                for (int i = p.nsub - 1; i >= 0; --i)
-                    if (ms[i].x != -INFINITY && ms[i].y > 0.f) {
-                        last_sc = i;
+                int last = 0;
+                for (int i = p.npiece - 1; i >= 0; --i)
+                    if (piece_w(i) > 0.f) {
+                        last = i;
                         break;
                     }
+                pick = last;
             }
             __syncthreads();
-            sc = last_sc;
+            pc = pick;
+            before_pc = -INFINITY;  // the crossing search below then fails, past the end
         }
-        // cumulative weight before sub-chunk sc, in the same order as above
-        float before_sc = 0.f;
-        for (int i0 = 0; i0 < sc; i0 += NT) {
-            const int i = i0 + tid;
-            const float2 q = i < sc ? ms[i] : make_float2(-INFINITY, 0.f);
-            const float w = q.x == -INFINITY ? 0.f : q.y * __builtin_amdgcn_exp2f((q.x - M) * c);
-            before_sc += block_sum_f32(w, red);
+        // rescan piece pc in token order: thread tid holds logits PER*tid .. PER*tid+PER-1
+        const int64_t base = (int64_t)pc * kSmpPiece + (int64_t)tid * PER;
+        float x[PER];
+#pragma unroll
+        for (int q = 0; q < PER / E; ++q) {
+            const uint4 u = smp_load16<T>(row, base + q * E, V, aligned);
+            float xe[E];
+            smp_unpack<T>(u, xe);
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                x[q * E + k] = xe[k];
         }
-        // rescan sub-chunk sc in token order: load i covers elements [2048 i, 2048 i + 2048)
-        // of the sub-chunk, thread tid the E of them at 2048 i + E tid
-        uint4 u[L];
-        const int64_t base = (int64_t)sc * kArgSub;
-        smp_load<T, NT, L>(row, base, V, tid, aligned, u);
-        __syncthreads();
-        if (tid == 0)
-            pick = INT_MAX;
-        int first_pos = INT_MAX, last_pos = -1;  // weighted elements of this thread
-        float run = before_sc;
+        float w[PER], s = 0.f;
+        int first_pos = INT_MAX, last_pos = -1;
 #pragma unroll
-        for (int i = 0; i < L; ++i) {
-            float x[E];
-            smp_unpack<T>(u[i], x);
-            const int64_t e0 = base + (int64_t)(tid + NT * i) * E;
-            float w[E], s = 0.f;
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                w[k] = smp_weight(x[k], M, c, e0 + k < V);
-                s += w[k];
-                if (w[k] > 0.f) {
-                    first_pos = min(first_pos, (int)(e0 + k));
-                    last_pos = max(last_pos, (int)(e0 + k));
-                }
+        for (int k = 0; k < PER; ++k) {
+            w[k] = smp_weight(x[k], M, c, base + k < V);
+            s += w[k];
+            if (w[k] > 0.f) {
+                first_pos = min(first_pos, (int)(base + k));
+                last_pos = max(last_pos, (int)(base + k));
             }
-            float tot;
-            float cum = run + block_excl_scan_f32(s, red, &tot);
-#pragma unroll
-            for (int k = 0; k < E; ++k) {
-                const float nxt = cum + w[k];
-                if (w[k] > 0.f && cum <= target && nxt > target)
-                    atomicMin(&pick, (int)(e0 + k));
-                cum = nxt;
-            }
-            run += tot;
         }
-        // no crossing inside (rounding near an end of the sub-chunk): its first or last
-        // weighted element, whichever end the target lies past
-        __shared__ int lo_pos, hi_pos;
+        float tot;
+        float cum = before_pc + block_excl_scan_f32(s, red, &tot);
         if (tid == 0) {
+            pick = INT_MAX;
             lo_pos = INT_MAX;
             hi_pos = -1;
         }
         __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const float nx = cum + w[k];
+            if (w[k] > 0.f && cum <= target && nx > target)
+                atomicMin(&pick, (int)(base + k));
+            cum = nx;
+        }
         if (first_pos != INT_MAX)
             atomicMin(&lo_pos, first_pos);
         if (last_pos >= 0)
             atomicMax(&hi_pos, last_pos);
         __syncthreads();
+        // no crossing inside (rounding near an end of the piece): its first or last
+        // weighted logit, whichever end the target lies past (-inf start: past the end)
         if (pick != INT_MAX)
             draw = pick;
         else
-            draw = target < before_sc ? lo_pos : hi_pos;
+            draw = (before_pc != -INFINITY && target < before_pc) ? lo_pos : hi_pos;
         if (draw < 0 || draw == INT_MAX)
             draw = 0;
     }
@@ -353,7 +349,7 @@ size_t sample_workspace(int S, int B, int V)
 {
     const int rows = S * B;
     const SmpPlan p = smp_plan(rows, V);
-    return (size_t)rows * p.nsub * sizeof(float2) + (size_t)rows * p.nrun * sizeof(uint32_t) +
+    return (size_t)rows * p.npiece * (sizeof(float2) + sizeof(uint32_t)) +
            (size_t)rows * (sizeof(uint64_t) + sizeof(uint32_t)) + 1024;
 }
 
@@ -374,24 +370,25 @@ jt_status launch_verify_sampled(const void *logits, int64_t row_stride, int V, i
         w += (bytes + 255) & ~(size_t)255;
         return q;
     };
-    float2 *ms = reinterpret_cast<float2 *>(take((size_t)rows * p.nsub * sizeof(float2)));
-    uint32_t *nanr = reinterpret_cast<uint32_t *>(take((size_t)rows * p.nrun * sizeof(uint32_t)));
+    float2 *ms = reinterpret_cast<float2 *>(take((size_t)rows * p.npiece * sizeof(float2)));
+    uint32_t *nanr = reinterpret_cast<uint32_t *>(take((size_t)rows * p.npiece * sizeof(uint32_t)));
     uint64_t *keys = reinterpret_cast<uint64_t *>(take((size_t)rows * sizeof(uint64_t)));
     uint32_t *nanw = reinterpret_cast<uint32_t *>(take((size_t)rows * sizeof(uint32_t)));
     const float c = 1.4426950408889634f / temperature;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
-    const dim3 g1((unsigned)(rows * p.nrun)), g2((unsigned)rows), blk(kSmpThreads);
+    const long waves = (long)rows * p.nwave;
+    const dim3 g1((unsigned)((waves + 3) / 4)), g2((unsigned)rows), blk(kSmpThreads);
     if (dtype == JT_BF16) {
         const bool al = addr % 16 == 0 && row_stride % 8 == 0;
         hipLaunchKernelGGL(sample_partial_kernel<uint16_t>, g1, blk, 0, st,
-                           (const uint16_t *)logits, row_stride, V, c, p, ms, nanr, al);
+                           (const uint16_t *)logits, row_stride, V, c, p, rows, ms, nanr, al);
         hipLaunchKernelGGL(sample_select_kernel<uint16_t>, g2, blk, 0, st,
                            (const uint16_t *)logits, row_stride, V, c, p, uniform, ms, nanr,
                            keys, nanw, sample_out, al);
     } else {
         const bool al = addr % 16 == 0 && row_stride % 4 == 0;
         hipLaunchKernelGGL(sample_partial_kernel<float>, g1, blk, 0, st, (const float *)logits,
-                           row_stride, V, c, p, ms, nanr, al);
+                           row_stride, V, c, p, rows, ms, nanr, al);
         hipLaunchKernelGGL(sample_select_kernel<float>, g2, blk, 0, st, (const float *)logits,
                            row_stride, V, c, p, uniform, ms, nanr, keys, nanw, sample_out, al);
     }
