@@ -402,8 +402,11 @@ def traffic_summarize(name, fetch_dir, write_dir):
     """Per entry point, HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE) KiB over the entry
     point's dispatches, divided by its launch count, each counter scaled by (bytes the
     calibration copy moved) / (what the counter read for it).  The traffic run launches the
-    entry points one after the other (top-W, mask, attention, verify, then the fused step,
-    whose 8-wave shapes also run attn_bf16_kernel), so dispatches are assigned in order."""
+    entry points one after the other (top-W, mask, attention, verify, the fused step, the
+    tree builder, the commit, the stochastic verifier), so dispatches are assigned in order:
+    a dispatch stays with the current entry point while its kernel is one of that entry
+    point's (the step's 8-wave shapes run attn_bf16_kernel, the stochastic verifier runs
+    verify_walk_kernel) and moves to the next entry point it matches otherwise."""
     order = list(CALLS) + ["step", "tree", "commit", "sampled"]
     def hits(kname, call):
         return any(k in kname for k in KERNELS[call])
@@ -426,10 +429,11 @@ def traffic_summarize(name, fetch_dir, write_dir):
         tot = {c: 0.0 for c in order}
         cnt = {c: 0 for c in order}
         for did, kname, val in ours:
-            for k in range(cur + 1, len(order)):
-                if hits(kname, order[k]):
-                    cur = k
-                    break
+            if not hits(kname, order[cur]):  # a kernel of a later entry point: move on
+                for k in range(cur + 1, len(order)):
+                    if hits(kname, order[k]):
+                        cur = k
+                        break
             call = order[cur]
             tot[call] += val
             cnt[call] += 1 if is_marker(kname, call) else 0
