@@ -501,6 +501,14 @@ template <int N> __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The same wait as inline asm with a memory clobber: no load may move across it, so the
+// loads it counts stay issued before it.
+template <int N> __device__ __forceinline__ void wait_vm_asm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // Workgroup barrier that does not drain the DMA pipeline: __syncthreads() carries a
 // workgroup fence, which the compiler implements with s_waitcnt vmcnt(0) and would wait
 // for the copies of later tiles too.  Each wave has already waited for its share of
@@ -714,12 +722,16 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
         }
     };
 
-    // node tid's parent, loaded before any tile copy so that waiting for it does not wait
-    // for the copies (memory operations complete in issue order)
+    // node tid's parent (clamped to a real node, so that every wave issues the load),
+    // loaded before any tile copy.  The load is inline asm: the compiler does not track
+    // it, and the wait before the tree rows counts the copies and query loads issued after
+    // it, so the pointer doubling overlaps their flight instead of waiting for all of them
+    // (the compiler's own wait there would be vmcnt(0): the masked loads in between defeat
+    // its counting).
     int par_v = -1;
     if constexpr (kTreeRows) {
-        if (tid < B)
-            par_v = a.parent[(int64_t)s * B + tid];
+        const int32_t *pp = a.parent + (int64_t)s * B + min(tid, B - 1);
+        asm volatile("global_load_dword %0, %1, off" : "=v"(par_v) : "v"(pp) : "memory");
     }
 
     // ---- speculative copies.  The prefix length is a device value: rather than wait
@@ -756,12 +768,14 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     const int row_g = (s * B + vrow) * a.Hq + g * G + (row_ok ? rr % G : 0);
     bf16x8_t qf[KS];
     {
+        // every lane loads (a row past the end reads a real row and is zeroed): exactly KS
+        // loads per wave, which the wait below counts
         const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)row_g * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (row_ok)
-                u = *reinterpret_cast<const uint4 *>(qrow + ks * 16 + hh * 8);
+            uint4 u = *reinterpret_cast<const uint4 *>(qrow + ks * 16 + hh * 8);
+            if (!row_ok)
+                u = make_uint4(0, 0, 0, 0);
             qf[ks] = __builtin_bit_cast(bf16x8_t, u);
         }
     }
@@ -776,6 +790,15 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
                       "room for the tree rows");
         const uint32_t tr_base = NPRO < NST ? lds_off(stage(NPRO))
                                             : lds_off(lds + AttnLds<D, NWR>::BT_OFF);
+        // the parent has landed once at most the later copies (NOPS per speculative tile)
+        // and the KS query loads are outstanding
+        static_assert(NPRO == 2, "one wait per count of speculative tiles");
+        if (spec[0] && spec[1])
+            wait_vm_asm<2 * NOPS + KS>();
+        else if (spec[0] || spec[1])
+            wait_vm_asm<NOPS + KS>();
+        else
+            wait_vm_asm<KS>();
         tree_rows_lds(par_v, B, tr_base);
         uint64_t rw[4];
         lds_read_row(tr_base + (uint32_t)vrow * 32u, rw);

@@ -64,11 +64,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
 // Wave-wide maximum of a 64-bit key through DPP moves (no LDS round trips): pairs,
 // quads, half rows, rows, then the row broadcasts; lane 63 ends with the maximum, which
 // is returned to every lane.
+// One 64-bit compare and two selects: a short-circuit form of the compare compiles to
+// exec-mask branches, several times slower.
 __device__ __forceinline__ uint64_t dpp_max_step(uint64_t v, uint32_t ohi, uint32_t olo)
 {
-    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-    const bool take = ohi > hi || (ohi == hi && olo > lo);
-    return take ? (((uint64_t)ohi << 32) | olo) : v;
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
 }
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint64_t dpp_max_u64_stage(uint64_t v)
