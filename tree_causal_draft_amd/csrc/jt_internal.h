@@ -93,12 +93,37 @@ __device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v)
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) { return wave_max_u64_dpp(v); }
 
+// Float wave reductions through the same DPP pattern (no LDS round trips, which a
+// shuffle butterfly pays at every step).  Lanes of rows a broadcast stage leaves out keep
+// `old`: the value itself for the maximum, 0 for the sum, so every element is counted
+// once.  The sum's order is fixed: pairs, quads, half rows, rows, then rows 0+1 and 2+3,
+// then both halves.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v, float old)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, false));
+}
 __device__ __forceinline__ float wave_max_f32(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+    v = fmaxf(v, dpp_f32<0xB1, 0xF>(v, v));
+    v = fmaxf(v, dpp_f32<0x4E, 0xF>(v, v));
+    v = fmaxf(v, dpp_f32<0x141, 0xF>(v, v));
+    v = fmaxf(v, dpp_f32<0x140, 0xF>(v, v));
+    v = fmaxf(v, dpp_f32<0x142, 0xA>(v, v));
+    v = fmaxf(v, dpp_f32<0x143, 0xC>(v, v));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_sum_f32(float v)
+{
+    v += dpp_f32<0xB1, 0xF>(v, 0.f);
+    v += dpp_f32<0x4E, 0xF>(v, 0.f);
+    v += dpp_f32<0x141, 0xF>(v, 0.f);
+    v += dpp_f32<0x140, 0xF>(v, 0.f);
+    v += dpp_f32<0x142, 0xA>(v, 0.f);
+    v += dpp_f32<0x143, 0xC>(v, 0.f);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 inline jt_status launch_status(hipError_t e) { return e == hipSuccess ? JT_OK : JT_ERR_LAUNCH; }

@@ -85,13 +85,6 @@ __device__ __forceinline__ float smp_weight(float x, float m, float c, bool in_r
     return (in_range && x == x && x != -INFINITY) ? e : 0.f;
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, kWave);
-    return v;
-}
 __device__ __forceinline__ float block_max_f32(float v, float *red)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;

@@ -189,6 +189,26 @@ __device__ __forceinline__ uint32_t wave_wth_code(uint32_t code, int W)
     return t;
 }
 
+// For each of a lane's K keys, the number of entries of keys[0..n) greater than it.  n is a
+// multiple of 8 (the caller pads with zero keys) and keys is 16-byte aligned.  Every lane
+// reads the same entries, so each read is an LDS broadcast.  (Issuing the next reads
+// before comparing the current ones measured slower: more registers and copies.)
+template <int K>
+__device__ __forceinline__ void count_greater(const uint64_t *keys, int n, const uint64_t (&mine)[K],
+                                              int (&cnt)[K])
+{
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        cnt[k] = 0;
+#pragma unroll 4
+    for (int i = 0; i < n; i += 2) {
+        const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(keys + i);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            cnt[k] += (p.x > mine[k] ? 1 : 0) + (p.y > mine[k] ? 1 : 0);
+    }
+}
+
 // Each wave owns `ppw` consecutive pieces of 2048 logits of one row and works alone (no
 // workgroup barrier).  Per piece:
 //   * the lane's (max, sum of exp(x - max)), merged into a running pair;
@@ -302,29 +322,35 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
             const uint32_t id = (uint32_t)(base + (int64_t)lane * E) + (uint32_t)(kWave * E * (j / E) + j % E);
             return ((uint64_t)order_code(x[j]) << 32) | (uint64_t)(~id);
         };
-        // tau == 0: fewer than W real lane maxima; every valid element is a candidate
-        uint32_t msk = valid;
-        if (tau != 0u) {
-            const float tf = order_decode(tau);  // x >= tf <=> code(x) >= tau, for non-NaN x
-            uint32_t mk = 0u;
-#pragma unroll
-            for (int j = 0; j < 32; ++j)
-                mk |= (x[j] >= tf ? 1u : 0u) << j;
-            msk &= mk;
-        }
-        const uint32_t jmask = wave_or_u32(msk);
+        // candidates: the valid elements at or above the threshold (x >= tf <=> code(x) >=
+        // tau for non-NaN x), or every valid element when tau == 0 (fewer than W real lane
+        // maxima).  Each slot j is tested with one ballot; slots no lane needs are skipped.
+        const bool all = tau == 0u;
+        const float tf = all ? 0.f : order_decode(tau);
+        auto is_cand = [&](int j) -> bool {
+            const bool in = (valid >> j) & 1u;
+            return all ? in : (in && x[j] >= tf);
+        };
         int n = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            if (jmask & (1u << j)) {
-                const bool pred = (msk >> j) & 1u;
-                const uint64_t b = __ballot(pred);
+        auto take = [&](int j, bool pred) {
+            const uint64_t b = __ballot(pred);
+            if (b != 0ull) {
                 const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
                 if (pred && slot < kWaveCap)
                     cand[slot] = key_of(j);
                 n += __popcll(b);
             }
+        };
+        if (!all && __ballot(valid != 0xffffffffu) == 0ull) {
+            // no padding in the piece (every piece but a row's last): one compare per slot
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                take(j, x[j] >= tf);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                take(j, is_cand(j));
         }
         if (n > kWaveCap) {
             // rare overflow (huge ties): W rounds of exact arg-max over the registers
@@ -333,7 +359,7 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
                 uint64_t mine = 0ull;
 #pragma unroll
                 for (int j = 0; j < 32; ++j) {
-                    if (!((msk >> j) & 1u))
+                    if (!is_cand(j))
                         continue;
                     const uint64_t k = key_of(j);
                     if (k < prev && k > mine)
@@ -348,19 +374,23 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
         }
         if (lane < W)
             cand[n + lane] = run;
-        wave_sync();
         const int tot = n + W;
+        const int tot8 = (tot + 7) & ~7;
+        if (tot <= kWave && lane < tot8 - tot)
+            cand[tot + lane] = 0ull;  // zero keys up to a multiple of 8 for the counting reads
+        wave_sync();
         if (tot <= kWave) {
-            uint64_t v = lane < tot ? cand[lane] : 0ull;
-            uint64_t nrun = 0ull;
-            for (int r = 0; r < W; ++r) {
-                const uint64_t K = wave_max_u64_dpp(v);
-                if (lane == r)
-                    nrun = K;
-                if (v == K)
-                    v = 0ull;
-            }
-            run = nrun;
+            // rank by count: a key's place in the new list is the number of keys above it
+            // (nonzero keys are unique: distinct ids), for all keys at once instead of W
+            // dependent wave-wide maxima
+            uint64_t mine[1] = {lane < tot ? cand[lane] : 0ull};
+            int cnt[1];
+            count_greater<1>(cand, tot8, mine, cnt);
+            const int nz = __popcll(__ballot(mine[0] != 0ull));
+            if (mine[0] != 0ull && cnt[0] < W)
+                best[cnt[0]] = mine[0];
+            wave_sync();
+            run = lane < min(W, nz) ? best[lane] : 0ull;
         } else {
             wave_select_topw(cand, tot, W, best);
             run = lane < W ? best[lane] : 0ull;
@@ -379,14 +409,9 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
         if (want_t)
             tw = c * (run_t + (run_m - m) * run_s);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        sw += __shfl_xor(sw, o, kWave);
-    if (want_t) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            tw += __shfl_xor(tw, o, kWave);
-    }
+    sw = wave_sum_f32(sw);
+    if (want_t)
+        tw = wave_sum_f32(tw);
     if (lane == 0) {
         ws_ms[gl] = make_float2(m, sw);
         if (want_t)
@@ -402,7 +427,7 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
                     int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
                     float2 *__restrict__ ws_ms, float *__restrict__ ws_t)
 {
-    __shared__ uint64_t cand_all[4][kWaveCap + JT_MAX_W];
+    __shared__ __attribute__((aligned(16))) uint64_t cand_all[4][kWaveCap + JT_MAX_W];
     __shared__ uint64_t best_all[4][JT_MAX_W];
     const int wid = threadIdx.x >> 6;
     topw_partial_wave<T, kAligned>(logits, row_stride, rows, V, W, npiece, ppw, nlist, ws_keys,
@@ -413,25 +438,6 @@ topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, 
 constexpr int kMergeCand = JT_MAX_W * JT_MAX_W;  // candidate keys a row merge can keep
 constexpr int kMergeLds = kMergeCand + 8;          // LDS keys per merging wave (8 of padding)
 
-// For each of a lane's K keys, the number of entries of keys[0..n) greater than it.  n is a
-// multiple of 8 (the caller pads with zero keys) and keys is 16-byte aligned.  Every lane
-// reads the same entries, so each read is an LDS broadcast.  (Issuing the next reads
-// before comparing the current ones measured slower: more registers and copies.)
-template <int K>
-__device__ __forceinline__ void count_greater(const uint64_t *keys, int n, const uint64_t (&mine)[K],
-                                              int (&cnt)[K])
-{
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        cnt[k] = 0;
-#pragma unroll 4
-    for (int i = 0; i < n; i += 2) {
-        const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(keys + i);
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            cnt[k] += (p.x > mine[k] ? 1 : 0) + (p.y > mine[k] ? 1 : 0);
-    }
-}
 
 // One wave per row: merge the partial lists and (max, sum) pairs of row r.  Every list is
 // sorted descending and nonzero keys are unique, so the W-th largest list head bounds the
@@ -497,9 +503,7 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
             t += c * (ts[j] + (p.x - m) * p.y);
         }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        s += __shfl_xor(s, o, kWave);
+    s = wave_sum_f32(s);
     float lse;
     if (s != s)
         lse = s;
@@ -508,9 +512,7 @@ __device__ __forceinline__ void topw_merge_row(int r, int W, int nchunk, const u
     else
         lse = m + logf(s);
     if (row_entropy) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1)
-            t += __shfl_xor(t, o, kWave);
+        t = wave_sum_f32(t);
         // H = log S - T / S; a NaN row gives NaN, a row of -inf (no distribution) 0
         const float h = (s != s) ? s : (m == -INFINITY ? 0.f : logf(s) - t / s);
         if (lane == 0)
