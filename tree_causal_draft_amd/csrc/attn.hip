@@ -494,6 +494,18 @@ __device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPla
     }
 }
 
+// max(v, v of lane i ^ 32) through v_permlane32_swap (gfx950), which exchanges the upper
+// half of one register with the lower half of another: applied to two copies of v, the
+// pair holds both halves' values in every lane.  Inline asm on two distinct registers:
+// the builtin, given one value for both operands, has its two results folded into one.
+// The s_nop covers the wait states after the copies are written.
+__device__ __forceinline__ float half_swap_max(float v)
+{
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return fmaxf(a, b);
+}
+
 // s_waitcnt vmcnt(N), N < 64 (expcnt and lgkmcnt left unconstrained)
 template <int N> __device__ __forceinline__ void wait_vm()
 {
@@ -984,13 +996,24 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
         // when the tile maximum exceeds it by more than kRescale (log2 units), so the
         // rescale of O (64 multiplies) is rare.  Probabilities are then at most 2^kRescale,
         // which fp32 and bf16 hold exactly in range; numerator and denominator share m_i.
-        float mx = -INFINITY;
+        // the row maximum as a tree (short dependency chains), then across the two
+        // half-waves that hold the row's two key halves
+        // (each chain starts from -inf, which the compiler folds into three-input maxima of
+        // the raw accumulators without canonicalising them first)
+        float t8m[8];
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
+        for (int q = 0; q < 8; ++q) {
+            const f32x16_t &a4 = sacc[q >> 2];
+            const int j0 = 4 * (q & 3);
+            float t = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                mx = fmaxf(mx, sacc[kbk][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+            for (int i = 0; i < 4; ++i)
+                t = fmaxf(t, a4[j0 + i]);
+            t8m[q] = t;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(t8m[0], t8m[1]), fmaxf(t8m[2], t8m[3])),
+                         fmaxf(fmaxf(t8m[4], t8m[5]), fmaxf(t8m[6], t8m[7])));
+        mx = half_swap_max(mx) * c;
         const bool move = mx > m_i + kRescale;
         if (__ballot(move)) {
             const float m_new = move ? mx : m_i;
@@ -1002,7 +1025,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
                 o_acc[db] *= alpha;
         }
         const float m_use = m_i == -INFINITY ? 0.f : m_i;
-        float psum = 0.f;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short add chains
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -1014,12 +1037,12 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
                 for (int i = 0; i < 8; ++i) {
                     const float p = __builtin_amdgcn_exp2f(
                         __builtin_fmaf(sacc[kbk][8 * m2 + i], c, -m_use));
-                    psum += p;
+                    ps[i & 3] += p;
                     t8[i] = (__bf16)p;
                 }
                 pf[kbk][m2] = t8;
             }
-        l_i += psum;
+        l_i += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     };
     auto pv = [&](const uint8_t *vb, const bf16x8_t (&pf)[2][2]) {
         // O^T += V^T . P^T; V^T fragments by transposing reads of row-major V.  The key
