@@ -95,6 +95,23 @@ def test_bf16_paged(bs):
     _check(w, f"paged bs={bs}")
 
 
+@pytest.mark.parametrize("S,B,G,prefix,paged", [
+    (6, 48, 4, (0, 700), False),    # empty to long prefixes
+    (5, 64, 4, (0, 1000), True),    # paged, two row tiles per KV head
+    (4, 80, 2, (200, 200), False),  # equal lengths: shares may still straddle units
+    (3, 136, 1, (0, 5), False),     # fewer tiles than workgroups: one-tile shares
+    (40, 72, 2, (0, 300), True),    # many short sequences, shares of one or two tiles
+])
+def test_bf16_balanced_schedule(S, B, G, prefix, paged):
+    """Several sequences with more than 128 rows per KV head: workgroups take equal shares
+    of all units' key tiles, so a unit is split at arbitrary tiles and merged from the
+    pieces of the workgroups it spans."""
+    w = wl.make("ragged", 455 + S, parts=("attn",), qk_std=1.0,
+                **_small(S=S, B=B, Hq=2 * G, Hkv=2, prefix=prefix, paged=paged,
+                         N=min(10, B - 1) if B > 1 else 0, W=4))
+    _check(w, f"balanced S={S} B={B} G={G} paged={paged}")
+
+
 def test_fp32_paged_and_gqa():
     w = wl.make("ragged", 450, parts=("attn",), **_small(S=2, dtype="f32", d=64, Hq=8, Hkv=1,
                                                            prefix=(33, 97), paged=True, B=20))

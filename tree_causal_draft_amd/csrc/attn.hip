@@ -256,8 +256,10 @@ struct AttnPlan {
     int n_rtiles;  // row tiles per (s, g)
     int units;     // S * Hkv * n_rtiles
     int ch;        // keys per chunk (multiple of 64)
-    int n_chunks;  // chunks per unit (1 = no split-KV)
+    int n_chunks;  // chunks per unit (1 = no split-KV); 0 with the balanced schedule
     int remap;     // 1: place consecutive work items on one XCD
+    int bal;       // 1: balanced schedule (equal shares of all units' key tiles)
+    int nwg;       // workgroups of the balanced schedule
 };
 
 // Split-KV workspace: (m, l) per partial row, then the partial rows themselves
@@ -267,11 +269,29 @@ struct AttnPlan {
 struct AttnWs {
     float2 *ml;
     uint16_t *o;
+    int32_t *sched;  // balanced schedule: S + 1 tile offsets of the sequences (last: total)
+    int2 *wstart;    // balanced schedule: per workgroup, its first unit and tile (-1: idle)
 };
 
-static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int block_size)
+// Sequences the balanced schedule handles (its schedule kernel keeps them in LDS).
+constexpr int kBalMaxS = 4096;
+
+// Key tiles of row tile rt of a sequence with prefix length P: the keys its rows can see.
+__host__ __device__ inline int attn_unit_tiles(int P, int rt, int rtrows, int B, int G)
+{
+    const int v_hi = min(B - 1, (rt * rtrows + rtrows - 1) / G);
+    return (P + v_hi + 1 + 63) / 64;
+}
+
+// allow_bal: several sequences with 8-wave workgroups take the balanced schedule, whose
+// key ranges follow the prefix lengths on the device.  (The fused step's 4-wave phase-1
+// attention keeps chunks; both entry points plan alike, so their outputs stay bit-equal.)
+static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int block_size,
+                          bool allow_bal = false)
 {
     AttnPlan p;
+    p.bal = 0;
+    p.nwg = 0;
     const int rows = (Hq / Hkv) * B;
     // At least 4 waves: a 2-wave workgroup leaves the compiler a 512-register budget (its
     // LDS allows one wave per SIMD), and it then keeps the O accumulators in AGPRs and
@@ -281,6 +301,30 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     p.rt = 32 * p.nwr;
     p.n_rtiles = (rows + p.rt - 1) / p.rt;
     p.units = S * Hkv * p.n_rtiles;
+    if (allow_bal && p.nwr == 8 && S > 1 && S <= kBalMaxS) {
+        // Prefix lengths differ per sequence and are known on the device only: chunks sized
+        // for max_prefix leave the long sequences' workgroups running alone.  The balanced
+        // schedule gives each workgroup an equal share of all units' tiles instead.
+        long tmax = 0;  // tiles if every prefix held max_prefix keys
+        for (int rt = 0; rt < p.n_rtiles; ++rt)
+            tmax += attn_unit_tiles(max_prefix, rt, p.rt, B, Hq / Hkv);
+        tmax *= (long)S * Hkv;
+        if (tmax < (1L << 30)) {
+            long nwg = p.nwr == 8 ? 256 : 512;
+            if (block_size > 0) {
+                // a share's block-table entries must fit the LDS staging area
+                const long cap = max(1L, (long)(kBtCap - 2) * block_size / 64);
+                nwg = max(nwg, (tmax + cap - 1) / cap);
+            }
+            nwg = min(nwg, tmax);
+            p.bal = 1;
+            p.nwg = (int)max(1L, nwg);
+            p.ch = 0;
+            p.n_chunks = 0;
+            p.remap = 0;
+            return p;
+        }
+    }
     const int gran = 64;
     const int keys = max_prefix + B;
     const int maxc = (keys + gran - 1) / gran;
@@ -310,21 +354,41 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     return p;
 }
 
-static size_t attn_ws_bytes(const AttnPlan &p, int d)
+static size_t attn_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partial slots: (unit, chunk) in the chunked schedule; in the balanced one, unit u's
+// piece from workgroup w sits in slot u + w (unique: along the tiles, each step to the
+// next piece moves to the next unit, the next workgroup, or both).
+static size_t attn_ws_slots(const AttnPlan &p)
 {
-    if (p.n_chunks <= 1)
-        return 0;
-    const size_t slots = (size_t)p.units * p.n_chunks * p.rt;
-    return slots * sizeof(float2) + slots * (size_t)d * 2;
+    if (p.bal)
+        return ((size_t)p.units + p.nwg) * p.rt;
+    return p.n_chunks <= 1 ? 0 : (size_t)p.units * p.n_chunks * p.rt;
 }
 
-static AttnWs attn_ws_split(const AttnPlan &p, void *ws)
+static size_t attn_ws_bytes(const AttnPlan &p, int S, int d)
 {
-    AttnWs w{nullptr, nullptr};
-    if (p.n_chunks <= 1 || !ws)
+    const size_t slots = attn_ws_slots(p);
+    size_t head = 0;
+    if (p.bal)
+        head = attn_align256(((size_t)S + 1) * sizeof(int32_t)) +
+               attn_align256((size_t)p.nwg * sizeof(int2));
+    return head + slots * sizeof(float2) + slots * (size_t)d * 2;
+}
+
+static AttnWs attn_ws_split(const AttnPlan &p, int S, void *ws)
+{
+    AttnWs w{nullptr, nullptr, nullptr, nullptr};
+    const size_t slots = attn_ws_slots(p);
+    if (slots == 0 || !ws)
         return w;
-    const size_t slots = (size_t)p.units * p.n_chunks * p.rt;
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
+    if (p.bal) {
+        w.sched = reinterpret_cast<int32_t *>(b);
+        b += attn_align256(((size_t)S + 1) * sizeof(int32_t));
+        w.wstart = reinterpret_cast<int2 *>(b);
+        b += attn_align256((size_t)p.nwg * sizeof(int2));
+    }
     w.ml = reinterpret_cast<float2 *>(b);
     w.o = reinterpret_cast<uint16_t *>(b + slots * sizeof(float2));
     return w;
@@ -436,7 +500,28 @@ __device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPla
     const int G = a.G, B = a.B;
     const int P = clamp_prefix(a, s);
     const int v_hi = min(B - 1, (rt * pl.rt + pl.rt - 1) / G);
-    const int nact = (P + v_hi + 1 + pl.ch - 1) / pl.ch;
+    // pieces: nk slots from `first`, one slot apart per piece, of which nact hold keys
+    int nk = pl.n_chunks, nact = 0;
+    int64_t first = (int64_t)unit * pl.n_chunks;
+    if (pl.bal) {
+        // the unit's tiles start at A (sequences' offsets, then KV heads, then row tiles)
+        // and go to workgroups wf .. wl of the equal shares of T tiles
+        const int64_t T = w.sched[a.S];
+        const int64_t nw = min((int64_t)pl.nwg, T);
+        const int ts = (w.sched[s + 1] - w.sched[s]) / a.Hkv;  // tiles of one KV head
+        int64_t A = w.sched[s] + (int64_t)g * ts;
+        for (int r2 = 0; r2 < rt; ++r2)
+            A += attn_unit_tiles(P, r2, pl.rt, B, G);
+        const int tu = attn_unit_tiles(P, rt, pl.rt, B, G);
+        auto wg_of = [&](int64_t x) { return (int)(((x + 1) * nw + T - 1) / T - 1); };
+        const int wf = wg_of(A), wl = wg_of(A + tu - 1);
+        if (wf == wl)
+            return;  // one workgroup held the whole unit and wrote its output
+        nk = nact = wl - wf + 1;
+        first = (int64_t)unit + wf;
+    } else {
+        nact = (P + v_hi + 1 + pl.ch - 1) / pl.ch;
+    }
     for (; it < pl.rt * SPR; it += stride) {
         const int rl = it / SPR, sgm = it % SPR;
         const int r = rt * pl.rt + rl;
@@ -446,22 +531,22 @@ __device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPla
         // and folded with an online max (one pass).  The reads do not wait for the prefix
         // length (inactive chunks' slots lie inside the workspace); a chunk k >= nact is
         // dropped by selection, never multiplied in, since its bytes are stale.
-        const int64_t base = (int64_t)unit * pl.n_chunks * pl.rt + rl;
+        const int64_t base = first * pl.rt + rl;
         float M = -INFINITY, l = 0.f;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < pl.n_chunks; k0 += NB) {
+        for (int k0 = 0; k0 < nk; k0 += NB) {
             float2 ml[NB];
             uint4 u[NB];
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
-                const int k = min(k0 + q, pl.n_chunks - 1);
+                const int k = min(k0 + q, nk - 1);
                 const int64_t slot = base + (int64_t)k * pl.rt;
                 ml[q] = w.ml[slot];
                 u[q] = *reinterpret_cast<const uint4 *>(w.o + slot * D + sgm * 8);
             }
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
-                const bool use = k0 + q < nact && k0 + q < pl.n_chunks;
+                const bool use = k0 + q < nact && k0 + q < nk;
                 const float mk = use ? ml[q].x : -INFINITY;
                 if (mk == -INFINITY)
                     continue;  // inactive chunk, or no visible key in it
@@ -626,13 +711,19 @@ template <int D, int NWR> struct AttnLds {
     static constexpr int BYTES = ANC_OFF + NWR * 32 * 5 * 8;
 };
 
-// The bf16 MFMA pass over one work item.  `blk` / `nblk`: this workgroup's index among
-// the workgroups running the pass and their number; `lds`: AttnLds<D, NWR>::BYTES of
-// LDS, 16-byte aligned.  kTreeRows: build the ancestor rows from the parent array here
+// The bf16 MFMA pass over one work item: the rows of row tile `rt` of (sequence s, KV
+// head g) against keys kbeg .. min(klim, the rows' last visible key) - 1.  `slot_tile`:
+// the item's partial slot (normalised bf16 rows plus (m, l)), unless `final`, when the
+// item covers the unit's keys alone and writes the output (and LSE) itself.  `validate`:
+// this item checks the sequence's prefix and blocks.  `speculate`: copy the first tiles
+// of a contiguous prefix before the prefix length is known.  `lds`: AttnLds<D, NWR>::BYTES
+// of LDS, 16-byte aligned.  kTreeRows: build the ancestor rows from the parent array here
 // (needs 64 * NWR >= B) instead of reading the mask step's rows.
 template <int D, int NWR, bool kTreeRows>
-__device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl, const AttnWs &ws,
-                                          int blk, int nblk, uint8_t *lds)
+__device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl, const AttnWs &ws,
+                                          int s, int g, int rt, int kbeg, int klim,
+                                          int64_t slot_tile, bool final, bool validate,
+                                          bool speculate, uint8_t *lds)
 {
     constexpr int NST = AttnLds<D, NWR>::NST;
     constexpr int SEGS = D / 8;                  // 16-byte segments per K/V row
@@ -661,21 +752,8 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     const int wr = wid;  // the wave's 32-row block
     const int col = lane & 31, hh = lane >> 5;
 
-    // ---- work item
-    int item = blk;
-    if (pl.remap) {
-        const int per = nblk >> 3;
-        item = (blk & 7) * per + (blk >> 3);
-    }
-    const int rt = item % pl.n_rtiles;
-    const int chunk = (item / pl.n_rtiles) % pl.n_chunks;
-    const int sg = item / (pl.n_rtiles * pl.n_chunks);
-    const int s = sg / a.Hkv, g = sg % a.Hkv;
-    const int unit = sg * pl.n_rtiles + rt;
     const int G = a.G, B = a.B, R = G * B;
     const int r0 = rt * pl.rt;
-
-    const int kbeg = chunk * pl.ch;
     const int v_hi = min(B - 1, (r0 + pl.rt - 1) / G);
 
     const uintptr_t kpre_a = reinterpret_cast<uintptr_t>(a.k_prefix);
@@ -756,7 +834,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
 #pragma unroll
     for (int k = 0; k < NPRO; ++k) {
         const int kt = kbeg + k * TILE;
-        spec[k] = !paged && kt + TILE <= a.max_prefix;
+        spec[k] = speculate && !paged && kt + TILE <= a.max_prefix;
         if (spec[k]) {
             if (fast_ok) {
                 dma_prefix(kt, stage(k));
@@ -824,11 +902,11 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
         anc_b = anc_src[1];
     }
 
-    if (a.err && rt == 0 && chunk == 0 && g == 0)
+    if (a.err && validate)
         attn_validate(a, s);
     const int P = clamp_prefix(a, s);
     const int kend_u = P + v_hi + 1;
-    const int kend = min(kend_u, kbeg + pl.ch);
+    const int kend = min(kend_u, klim);
     if (kbeg >= kend) {
         wait_vm<0>();  // speculative copies land before the workgroup's LDS is released
         return;        // nothing to do: the combine pass skips this chunk
@@ -1164,7 +1242,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     // ---- epilogue: final output (one chunk), or a normalised bf16 partial plus (m, l)
     const float l = l_i + __shfl_xor(l_i, 32, kWave);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t slot0 = ((int64_t)unit * pl.n_chunks + chunk) * pl.rt + wr * 32;
+    const int64_t slot0 = slot_tile * pl.rt + wr * 32;
     // The accumulator spreads one row over the registers of 16 lanes.  A row-major copy of
     // the wave's 32 rows in LDS (row pitch D*2 + 16 bytes, which staggers the banks) lets
     // every lane store 16 contiguous bytes of a row instead of 8-byte pieces of 32 rows.
@@ -1175,7 +1253,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     // stored only now: vmcnt counts stores too, so a store before wait_dma() would make it
     // wait for the store's completion (measured: about 2 us per workgroup)
     if (wave_has_rows && row_ok && hh == 0) {
-        if (pl.n_chunks == 1) {
+        if (final) {
             if (a.lse)
                 a.lse[row_g] = l > 0.f ? (m_i + __log2f(l)) * kLn2 : -INFINITY;
         } else {
@@ -1206,7 +1284,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
             const uint4 val = *reinterpret_cast<const uint4 *>(ob + row * OPITCH + sgm * 16);
             if (rr2 < R) {
                 uint16_t *dst;
-                if (pl.n_chunks == 1) {
+                if (final) {
                     const int v2 = rr2 / G, h2 = g * G + rr2 % G;
                     dst = reinterpret_cast<uint16_t *>(a.out) + (((int64_t)s * B + v2) * a.Hq + h2) * D;
                 } else {
@@ -1218,12 +1296,155 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
     }
 }
 
+// Chunked schedule: work item `blk` of `nblk` is (unit, chunk), chunks of pl.ch keys; with
+// pl.remap the chunks of one unit run on one XCD and share its L2.
+template <int D, int NWR, bool kTreeRows>
+__device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl, const AttnWs &ws,
+                                          int blk, int nblk, uint8_t *lds)
+{
+    int item = blk;
+    if (pl.remap) {
+        const int per = nblk >> 3;
+        item = (blk & 7) * per + (blk >> 3);
+    }
+    const int rt = item % pl.n_rtiles;
+    const int chunk = (item / pl.n_rtiles) % pl.n_chunks;
+    const int sg = item / (pl.n_rtiles * pl.n_chunks);
+    const int g = sg % a.Hkv;
+    const int kbeg = chunk * pl.ch;
+    attn_item<D, NWR, kTreeRows>(a, pl, ws, sg / a.Hkv, g, rt, kbeg, kbeg + pl.ch,
+                                 ((int64_t)sg * pl.n_rtiles + rt) * pl.n_chunks + chunk,
+                                 pl.n_chunks == 1, rt == 0 && chunk == 0 && g == 0, true, lds);
+}
+
+// Balanced schedule: the units' key tiles, in unit order, form one sequence of T tiles;
+// workgroup w < n = min(nwg, T) takes tiles floor(w T / n) .. floor((w + 1) T / n) - 1, one
+// piece per unit it meets, starting from the unit and tile the schedule kernel found.
+template <int D, int NWR>
+__device__ __forceinline__ void attn_main_bal(const AttnArgs &a, const AttnPlan &pl, const AttnWs &ws,
+                                              int w, uint8_t *lds)
+{
+    const int2 st = ws.wstart[w];
+    if (st.x < 0)
+        return;  // an empty share
+    const int64_t T = ws.sched[a.S];
+    const int64_t nw = min((int64_t)pl.nwg, T);  // every share nonempty
+    int64_t left = (int64_t)(w + 1) * T / nw - (int64_t)w * T / nw;
+    const int per_seq = a.Hkv * pl.n_rtiles;
+    int u = st.x, off = st.y;
+    int s = u / per_seq;
+    int P = clamp_prefix(a, s);
+    bool first = true;
+    while (left > 0) {
+        const int rt = u % pl.n_rtiles, g = (u / pl.n_rtiles) % a.Hkv;
+        const int tu = attn_unit_tiles(P, rt, pl.rt, a.B, a.G);
+        const int n = (int)min((int64_t)(tu - off), left);
+        if (!first)
+            __syncthreads();  // the previous piece's epilogue has read back its LDS staging
+        first = false;
+        attn_item<D, NWR, false>(a, pl, ws, s, g, rt, off * 64, (off + n) * 64, (int64_t)u + w,
+                                 off == 0 && n == tu, off == 0 && g == 0 && rt == 0, false, lds);
+        left -= n;
+        off = 0;
+        ++u;
+        if (left > 0 && u / per_seq != s) {
+            s = u / per_seq;
+            P = clamp_prefix(a, s);
+        }
+    }
+}
+
 template <int D, int NWR>
 __global__ void __launch_bounds__(64 * NWR, 8 / NWR)  // 2 waves per SIMD: no AGPR round trips
 attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[AttnLds<D, NWR>::BYTES];
-    attn_main<D, NWR, false>(a, pl, ws, blockIdx.x, gridDim.x, lds);
+    if (pl.bal)
+        attn_main_bal<D, NWR>(a, pl, ws, blockIdx.x, lds);
+    else
+        attn_main<D, NWR, false>(a, pl, ws, blockIdx.x, gridDim.x, lds);
+}
+
+// The balanced schedule, one workgroup of 256 threads: per sequence its tile offset (each
+// thread sums a run of sequences, the runs' offsets come from a scan of the 256 sums),
+// then per workgroup of the main pass the unit and tile its share starts at (a binary
+// search over the offsets, then the KV head and row tile within the sequence).
+__global__ void __launch_bounds__(256) attn_sched_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
+{
+    __shared__ int32_t tab[kBalMaxS + 1];
+    __shared__ int32_t pre[kBalMaxS];
+    __shared__ int32_t part[256];
+    const int tid = threadIdx.x, S = a.S;
+    const int per = (S + 255) / 256;
+    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+    int sum = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int P = clamp_prefix(a, s);
+        pre[s] = P;
+        int r = 0;
+        for (int rt = 0; rt < pl.n_rtiles; ++rt)
+            r += attn_unit_tiles(P, rt, pl.rt, a.B, a.G);
+        tab[s] = a.Hkv * r;
+        sum += a.Hkv * r;
+    }
+    // exclusive scan of the 256 run sums: inclusive within each wave, then the wave totals
+    const int lane = tid & 63, wid = tid >> 6;
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, kWave);
+        if (lane >= o)
+            inc += v;
+    }
+    if (lane == 63)
+        part[wid] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int k = 0; k < wid; ++k)
+        base += part[k];
+    const int total = part[0] + part[1] + part[2] + part[3];
+    int c = base + inc - sum;
+    for (int s = s0; s < s1; ++s) {
+        const int v = tab[s];
+        tab[s] = c;
+        c += v;
+    }
+    if (tid == 0)
+        tab[S] = total;
+    __syncthreads();
+    for (int s = tid; s <= S; s += 256)
+        ws.sched[s] = tab[s];
+    // With fewer tiles than workgroups, only the first T take a share (of one tile each), so
+    // that no share is empty: the merge expects a piece from every workgroup it spans.
+    const int64_t T = total;
+    const int64_t nw = min((int64_t)pl.nwg, T);
+    for (int w = tid; w < pl.nwg; w += 256) {
+        int2 r = make_int2(-1, 0);
+        if (w < nw) {
+            const int64_t a0 = (int64_t)w * T / nw;
+            int lo = 0, hi = S - 1;  // the last sequence whose offset is <= a0
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (tab[mid] <= a0)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            int rel = (int)(a0 - tab[lo]);
+            const int ts = (tab[lo + 1] - tab[lo]) / a.Hkv;  // tiles of one KV head
+            const int g = rel / ts;
+            rel -= g * ts;
+            int rt = 0;
+            for (; rt < pl.n_rtiles - 1; ++rt) {
+                const int t = attn_unit_tiles(pre[lo], rt, pl.rt, a.B, a.G);
+                if (rel < t)
+                    break;
+                rel -= t;
+            }
+            r = make_int2((lo * a.Hkv + g) * pl.n_rtiles + rt, rel);
+        }
+        ws.wstart[w] = r;
+    }
 }
 
 // Separate merge pass for large units: one thread per (unit, row, 8 output columns).
@@ -1246,33 +1467,40 @@ size_t attention_workspace(int S, int B, int Hq, int Hkv, int d, int max_prefix,
 {
     if (dtype != JT_BF16)
         return 0;
-    return attn_ws_bytes(attn_plan(S, B, Hq, Hkv, max_prefix, block_size), d);
+    return attn_ws_bytes(attn_plan(S, B, Hq, Hkv, max_prefix, block_size, true), S, d);
 }
 
 template <int D, int NWR>
 static void launch_main(const AttnArgs &a, const AttnPlan &p, const AttnWs &w, hipStream_t st)
 {
-    const unsigned grid = (unsigned)((long)p.units * p.n_chunks);
+    const unsigned grid = p.bal ? (unsigned)p.nwg : (unsigned)((long)p.units * p.n_chunks);
     hipLaunchKernelGGL((attn_bf16_kernel<D, NWR>), dim3(grid), dim3(64 * NWR), 0, st, a, p, w);
 }
 
 template <int D>
 static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
 {
-    const AttnPlan p = attn_plan(a.S, a.B, a.Hq, a.Hkv, a.max_prefix, a.block_table ? a.block_size : 0);
-    const AttnWs w = attn_ws_split(p, ws);
+    const AttnPlan p = attn_plan(a.S, a.B, a.Hq, a.Hkv, a.max_prefix,
+                                 a.block_table ? a.block_size : 0, true);
+    const AttnWs w = attn_ws_split(p, a.S, ws);
+    if (p.bal) {
+        hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, a, p, w);
+        jt_status e = launch_status(hipGetLastError());
+        if (e != JT_OK)
+            return e;
+    }
     if (p.nwr == 4)
         launch_main<D, 4>(a, p, w, st);
     else
         launch_main<D, 8>(a, p, w, st);
     jt_status e = launch_status(hipGetLastError());
-    if (e != JT_OK || p.n_chunks == 1)
+    if (e != JT_OK || (!p.bal && p.n_chunks == 1))
         return e;
     const long threads = (long)p.units * p.rt * (D / 8);
     const dim3 cgrid((unsigned)((threads + 255) / 256)), cblock(256);
     // 16 chunks per round trip only where that makes it a single trip; wider batches cost
     // more in registers (occupancy) and padded loads than the trips they save
-    if (p.n_chunks > 8 && p.n_chunks <= 16)
+    if (!p.bal && p.n_chunks > 8 && p.n_chunks <= 16)
         hipLaunchKernelGGL((attn_combine_kernel<D, 16>), cgrid, cblock, 0, st, a, p, w);
     else
         hipLaunchKernelGGL((attn_combine_kernel<D, 8>), cgrid, cblock, 0, st, a, p, w);

@@ -163,7 +163,7 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
                           int block_size)
 {
     StepPlan sp;
-    sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size);
+    sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size, true);
     const bool split = sp.ap.nwr == 8;  // scans in a launch of their own
     const int nw = split ? 4 : sp.ap.nwr;  // waves per scan workgroup
     const int rows_d = S * N, rows_t = S * B;
@@ -206,11 +206,11 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
         sp.gp.sub_per_wg = spw;
         sp.gp.nchunk = (nsub + spw - 1) / spw;
     }
-    sp.nA = sp.ap.units * sp.ap.n_chunks;
+    sp.nA = sp.ap.bal ? sp.ap.nwg : sp.ap.units * sp.ap.n_chunks;
     sp.nT = (rows_d * sp.tp.nlist + nw - 1) / nw;
     sp.nG = rows_t * sp.gp.nchunk;
     sp.nM = S;
-    sp.nC = sp.ap.n_chunks > 1
+    sp.nC = sp.ap.bal || sp.ap.n_chunks > 1
                 ? (int)(((long)sp.ap.units * sp.ap.rt * (d / 8) + 255) / 256)
                 : 0;
     sp.nR = (rows_d + kStepRowsPerBlock - 1) / kStepRowsPerBlock;
@@ -227,7 +227,7 @@ static StepWs step_ws_layout(const StepPlan &sp, int S, int N, int B, int W, int
     StepWs L;
     size_t off = 0;
     L.attn = off;
-    off += align256(attn_ws_bytes(sp.ap, d));
+    off += align256(attn_ws_bytes(sp.ap, S, d));
     const size_t tparts = (size_t)S * N * sp.tp.nlist;
     L.tkeys = off;
     off += align256(tparts * W * sizeof(uint64_t));
@@ -257,6 +257,8 @@ template <int D>
 static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st)
 {
     if (sp.ap.nwr == 8) {
+        if (sp.ap.bal)  // the attention pass's balanced schedule
+            hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, sa.attn, sp.ap, sa.aws);
         const unsigned gs = (unsigned)(sp.nT + sp.nG + sp.nM);
         hipLaunchKernelGGL(step_scan_kernel, dim3(gs), dim3(256), 0, st, sa, sp);
         AttnArgs a = sa.attn;
@@ -291,7 +293,7 @@ jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st)
     sa.err_mask = reinterpret_cast<int32_t *>(w + L.flags);
     sa.err_attn = sa.err_mask + aa.S;
     sa.attn.err = sa.err_attn;
-    sa.aws = attn_ws_split(sp.ap, w + L.attn);
+    sa.aws = attn_ws_split(sp.ap, aa.S, w + L.attn);
     sa.draft = in.draft;
     sa.draft_stride = in.draft_stride;
     sa.target = in.target;
