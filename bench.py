@@ -464,6 +464,49 @@ def traffic_summarize(name, fetch_dir, write_dir):
     print(json.dumps({name: out}, indent=1, sort_keys=True))
 
 
+def attention_only(name, seed, reps=20, log=print):
+    """The attention call alone on one workload (graph replay over cold input sets, as the
+    per-call timing): for the parity configurations that are not bench lines."""
+    import torch
+    from tree_causal_draft_amd import workload as wl
+    from tree_causal_draft_amd.step import DeviceStep
+    w = wl.make(name, seed, parts=("attn",))
+    st = DeviceStep(w, "cuda:0", parts=("mask", "attn"))
+    st.mask()
+    fp = sum(getattr(st, n).numel() * getattr(st, n).element_size()
+             for n in ("q", "k_tree", "v_tree", "k_prefix", "v_prefix"))
+    nsets = max(1, min(32, math.ceil(2 * LLC_BYTES / fp)))
+    rot = Rotation(st, nsets)
+    g = _capture([s.attention for s in rot.steps])
+    us, _ = _time_graph(g, nsets, reps * nsets, nsets)
+    b, fl = algorithmic(w)
+    tf = fl / us / 1e6
+    log(f"[bench] {name}: attention {us:.2f} us/call over {nsets} cold sets")
+    return {"workload": name, "attention_us": round(us, 2), "TFLOPs": round(tf, 1),
+            "mfma_frac": round(tf / 2500.0, 4), "GBps": round(b["attention"] / us / 1e3, 1)}
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=20):
+    """Device-to-device copy rate (bytes read + written per second, GB/s) of one GiB on
+    this GPU: the practical HBM ceiling that the 8 TB/s peak is quoted beside."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    t1.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / us / 1e3, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -475,6 +518,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calls-only", action="store_true")
     ap.add_argument("--traffic-run", metavar="NAME")
+    ap.add_argument("--attention-only", metavar="NAME[,NAME...]",
+                    help="time the attention call alone on these workloads")
     ap.add_argument("--traffic-summarize", nargs=3, metavar=("NAME", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -497,6 +542,10 @@ def main():
     if args.traffic_run:
         traffic_run(args.traffic_run, seed_of(args.traffic_run), log=log)
         return
+    if args.attention_only:
+        for n in args.attention_only.split(","):
+            print(json.dumps(attention_only(n, seed_of(n), log=log)), flush=True)
+        return
 
     names = [args.workload] + [n for n in args.secondary.split(",") if n]
     results = [time_workload(n, args.steps, args.warmup, seed_of(n), log=log,
@@ -504,6 +553,7 @@ def main():
     cpu = None
     if not args.no_cpu and not args.calls_only:
         cpu = cpu_baseline(args.workload, seed_of(args.workload), args.cpu_seconds, log=log)
+    copy_gbps = None if args.calls_only else copy_bandwidth()
 
     def summary(r):
         c = r["w"].cfg
@@ -549,6 +599,7 @@ def main():
         "roofline": roofline_line(prim, dom),
         "attention_roofline": roofline_line(prim, "attention"),
         "cpu_baseline": cpu,
+        "copy_bandwidth_GBps": copy_gbps,
     }
     if args.calls_only:
         line["mode"] = "calls-only (entry points timed alone; no whole-step figure)"
