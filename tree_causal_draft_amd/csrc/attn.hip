@@ -590,6 +590,13 @@ __device__ __forceinline__ float half_swap_max(float v)
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     return fmaxf(a, b);
 }
+// v + v of lane i ^ 32, the same way (the pair holds v and the other half's value)
+__device__ __forceinline__ float half_swap_add(float v)
+{
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return a + b;
+}
 
 // s_waitcnt vmcnt(N), N < 64 (expcnt and lgkmcnt left unconstrained)
 template <int N> __device__ __forceinline__ void wait_vm()
@@ -1240,7 +1247,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
     }
 
     // ---- epilogue: final output (one chunk), or a normalised bf16 partial plus (m, l)
-    const float l = l_i + __shfl_xor(l_i, 32, kWave);
+    const float l = half_swap_add(l_i);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t slot0 = slot_tile * pl.rt + wr * 32;
     // The accumulator spreads one row over the registers of 16 lanes.  A row-major copy of

@@ -13,8 +13,8 @@
 //     lane max, then sum of exp(x - max) (exact per-lane rescale);
 //   * only logits at or above a threshold (a lower bound on the piece's W-th largest)
 //     become 64-bit keys (order code << 32 | ~id): value descending, id ascending in one
-//     integer compare, so bf16 ties resolve exactly like a full sort; W rounds of a DPP
-//     wave max over them and the wave's running list give the new list;
+//     integer compare, so bf16 ties resolve exactly like a full sort; the new list is
+//     picked among them and the wave's running list by rank counts;
 //   * a merge kernel (one wave per row) combines the per-wave top-W lists and the
 //     (max, sum-exp) pairs into ids, log-probs and the row log-sum-exp, selecting by
 //     rank counts;
@@ -215,14 +215,13 @@ __device__ __forceinline__ void count_greater(const uint64_t *keys, int n, const
 //   * a threshold tau: the larger of the W-th largest lane maximum and the W-th entry of
 //     the wave's running list (a lower bound on the W-th largest key of the piece and the
 //     list together), so only logits >= tau can enter the list;
-//   * the lanes' candidate masks (one float compare per logit) and their wave-wide OR,
-//     which skips every slot j that no lane needs; the candidates of the remaining slots
-//     are compacted into the wave's LDS slice as 64-bit keys (order code << 32 | ~id:
-//     value descending, id ascending in one integer compare, so bf16 ties resolve like a
-//     full sort) by ballot + mbcnt;
-//   * the running list (lane r holds entry r) is appended and W rounds of a DPP wave max
-//     -- over registers when at most 64 keys compete, else over the LDS slice -- give the
-//     new list.
+//   * the candidates, one ballot per slot j (one float compare per logit; slots no lane
+//     needs are skipped), compacted into the wave's LDS slice as 64-bit keys (order code
+//     << 32 | ~id: value descending, id ascending in one integer compare, so bf16 ties
+//     resolve like a full sort) at offsets from mbcnt;
+//   * the running list (lane r holds entry r) is appended and the new list picked by
+//     rank: with at most 64 keys each key's place is the number of keys above it, counted
+//     over LDS broadcast reads, else W rounds of a wave maximum over the LDS slice.
 // Output per wave: its W best keys, descending, 0-padded, its (max, sum) pair and, when
 // ws_t is not null, the entropy sum T of its logits (relative to the same max).
 // `cand` holds kWaveCap + JT_MAX_W keys and `best` JT_MAX_W keys of this wave's LDS.

@@ -169,6 +169,7 @@ __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logit
                     first = (int)(e0 + k);
         }
     }
+    // (a shuffle butterfly: a DPP maximum of complements measured 0.5 us slower per step)
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         first = min(first, __shfl_xor(first, o, kWave));
@@ -296,10 +297,7 @@ __device__ __forceinline__ void verify_walk_block(int s, int B, int N, int nchun
             flags |= JT_DEV_NAN;
     }
     // OR of the flags over the block
-    int f = flags;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        f |= __shfl_xor(f, o, kWave);
+    int f = (int)wave_or_u32((uint32_t)flags);
     if (lane == 0)
         fl[wid] = f;
     __syncthreads();
@@ -336,9 +334,7 @@ __device__ __forceinline__ void verify_walk_block(int s, int B, int N, int nchun
         if (accepted)
             key = ((uint32_t)dv << 16) | (uint32_t)(65535 - v);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        key = max(key, (uint32_t)__shfl_xor((int)key, o, kWave));
+    key = wave_max_u32(key);
     if (lane == 0)
         wbest[wid] = key;
     __syncthreads();
