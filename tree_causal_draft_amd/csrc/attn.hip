@@ -394,18 +394,21 @@ static AttnWs attn_ws_split(const AttnPlan &p, int S, void *ws)
     return w;
 }
 
-// 16-byte segment swizzle of an LDS K/V row with SEGS segments.  Eight consecutive rows
-// get distinct values in the low three bits (a 16-byte read of one segment from rows
-// r..r+7 touches eight different 16-byte bank groups), and the four rows of a
-// transposing V read (rows 4a..4a+3, segment pair {2c, 2c+1}) map to eight distinct
-// segments; bit 3 separates rows r and r+8.
+// 16-byte segment swizzle of an LDS K/V row with SEGS segments.  With 16 segments (d =
+// 128) every 256-byte row starts at the same bank of the 64 four-byte banks, so only the
+// segment order separates rows.  Any 16 consecutive rows get 16 distinct values (a
+// 16-byte K read of one segment from 16 rows is free of conflicts), and in each group of
+// four rows 4a..4a+3 bit 1 is fixed while bits 2-3 take all four values: the lanes of a
+// transposing V read, rows 4a..4a+3 (and 4a+4..4a+7) by segments {4b..4b+3}, then touch
+// 16 distinct segments, all 64 banks.  (The order it replaced, bits 1-2 from row & 3,
+// gave those reads two-way conflicts: measured with SQ_LDS_BANK_CONFLICT.)  With 8
+// segments (d = 64), eight consecutive rows get distinct values.
 template <int SEGS> __device__ __forceinline__ int seg_swz(int row)
 {
-    const int lo = ((row & 3) << 1) | ((row >> 2) & 1);
     if constexpr (SEGS >= 16)
-        return lo | (((row >> 3) & 1) << 3);
+        return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
     else
-        return lo;
+        return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
 __device__ __forceinline__ void lds_dma16(const void *gsrc, void *ldst)
