@@ -94,9 +94,16 @@ __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logit
     u16x2_t mag = {0, 0};    // bf16: maximum of the magnitude bits (NaN iff > 0x7f80)
     uint32_t magf = 0u;      // fp32: the same on 32-bit words (NaN iff > 0x7f800000)
     uint4 u[L];  // after the scan: the words of the last sub-chunk
+    uint4 un[L];  // the next sub-chunk's words, loaded while this one is reduced
+    if (sc0 < sc1)
+        load_sub(sc0, un);
     for (int sc = sc0; sc < sc1; ++sc) {
         const int64_t base = (int64_t)sc * kArgSub;
-        load_sub(sc, u);
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            u[i] = un[i];
+        if (sc + 1 < sc1)
+            load_sub(sc + 1, un);
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
