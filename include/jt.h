@@ -121,7 +121,11 @@ jt_status jt_build_tree_mask(const int32_t *parent, int32_t S, int32_t B, uint64
  * block_size a power of two; dtype JT_BF16 or JT_F32; q/k/v/out 16-byte aligned.
  * bf16 runs on MFMA (fp32 accumulate, bf16 out); fp32 runs on the vector ALU.
  */
-/* block_size: the paged pool's block size, or 0 for a contiguous prefix. */
+/* block_size: the paged pool's block size, or 0 for a contiguous prefix.  The workspace
+ * holds split-KV partial rows (and, for several sequences with more than 128 query rows
+ * per KV head, the schedule that gives every workgroup an equal share of all sequences'
+ * key tiles); its contents need no initialisation.  Calls that overlap on one workspace
+ * race. */
 size_t jt_tree_attention_workspace_size(int32_t S, int32_t B, int32_t Hq, int32_t Hkv,
                                         int32_t d, int32_t max_prefix, int32_t block_size,
                                         jt_dtype dtype);
