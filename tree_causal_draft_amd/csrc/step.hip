@@ -65,7 +65,9 @@ template <int D, int NWR> struct StepLds {
 
 // The scan and mask roles, for workgroups of NW waves; `b` counts from the first scan
 // workgroup.
-template <int NW>
+// kArgPrefetch: the arg-max role loads its next sub-chunk early, worth it in the scan
+// launch (three waves per SIMD) and not in the attention-sharing phase 1.
+template <int NW, bool kArgPrefetch>
 __device__ __forceinline__ void step_scan_roles(const StepArgs &sa, const StepPlan &sp, int b,
                                                 uint8_t *pool)
 {
@@ -80,7 +82,7 @@ __device__ __forceinline__ void step_scan_roles(const StepArgs &sa, const StepPl
     }
     b -= sp.nT;
     if (b < sp.nG) {
-        argmax_partial_block<uint16_t, true, 64 * NW>(
+        argmax_partial_block<uint16_t, true, 64 * NW, kArgPrefetch>(
             static_cast<const uint16_t *>(sa.target), sa.target_stride, sa.V, sp.gp.nsub,
             sp.gp.sub_per_wg, sp.gp.nchunk, sa.gkeys, sa.gnan, b,
             reinterpret_cast<uint64_t *>(pool), reinterpret_cast<uint32_t *>(pool + NW * 8));
@@ -101,7 +103,7 @@ __device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepP
     if (b < sp.nA)
         attn_main<D, NWR, true>(sa.attn, sp.ap, sa.aws, b, sp.nA, pool);
     else
-        step_scan_roles<NWR>(sa, sp, b - sp.nA, pool);
+        step_scan_roles<NWR, false>(sa, sp, b - sp.nA, pool);
 }
 
 // 4 waves: two workgroups per CU (register budget 256 per lane, LDS 2 x 74 KB)
@@ -121,7 +123,7 @@ constexpr int kScanLds = 4 * (kWaveCap + 2 * JT_MAX_W) * 8 > JT_MAX_NODES * 40
 __global__ void __launch_bounds__(256) step_scan_kernel(StepArgs sa, StepPlan sp)
 {
     __shared__ __attribute__((aligned(16))) uint8_t pool[kScanLds];
-    step_scan_roles<4>(sa, sp, blockIdx.x, pool);
+    step_scan_roles<4, true>(sa, sp, blockIdx.x, pool);
 }
 
 template <int D, int NB>

@@ -37,7 +37,9 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 // threads holding M re-read that sub-chunk (an L2 hit; the last one is still in
 // registers) for their first index of M, and a block-wide minimum gives the lowest.  With no value above -inf the chunk's first
 // element stands (a row of -inf keeps its first id).
-template <typename T, bool kAligned, int NT>
+// kPrefetch: the next sub-chunk's loads are issued while one is reduced (for a role that
+// runs at few waves per SIMD; with many waves resident the copies already overlap).
+template <typename T, bool kAligned, int NT, bool kPrefetch = true>
 __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logits, int64_t row_stride, int V,
                                      int nsub, int sub_per_wg, int nchunk,
                                      uint64_t *__restrict__ ws_keys, uint32_t *__restrict__ ws_nan,
@@ -95,15 +97,19 @@ __device__ __forceinline__ void argmax_partial_block(const T *__restrict__ logit
     uint32_t magf = 0u;      // fp32: the same on 32-bit words (NaN iff > 0x7f800000)
     uint4 u[L];  // after the scan: the words of the last sub-chunk
     uint4 un[L];  // the next sub-chunk's words, loaded while this one is reduced
-    if (sc0 < sc1)
+    if (kPrefetch && sc0 < sc1)
         load_sub(sc0, un);
     for (int sc = sc0; sc < sc1; ++sc) {
         const int64_t base = (int64_t)sc * kArgSub;
+        if constexpr (kPrefetch) {
 #pragma unroll
-        for (int i = 0; i < L; ++i)
-            u[i] = un[i];
-        if (sc + 1 < sc1)
-            load_sub(sc + 1, un);
+            for (int i = 0; i < L; ++i)
+                u[i] = un[i];
+            if (sc + 1 < sc1)
+                load_sub(sc + 1, un);
+        } else {
+            load_sub(sc, u);
+        }
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
