@@ -1,5 +1,6 @@
 // The whole draft-and-verify step in two launches (jt_draft_verify_step); three for
-// shapes whose attention needs 8-wave workgroups (see step_scan_kernel).
+// shapes whose attention needs 8-wave workgroups (see step_scan_kernel), and then a
+// fourth, the attention's schedule kernel, when several sequences share the pass.
 //
 // Each launch runs several steps side by side, one role per range of workgroup ids:
 //   phase 1  attention   the split-KV MFMA pass; its workgroups build the tree's ancestor
