@@ -147,6 +147,44 @@ def test_nan_inf_rows_and_odd_vocab():
     _compare(bf, par, tok, 4, 1.3, u, "bf16")
 
 
+def test_special_pieces_in_aligned_rows():
+    """Rows whose length is a multiple of 8, so that whole 2048-logit pieces take the
+    unmasked pass: a NaN there, a piece of -inf only, a row whose weight sits in one
+    piece, a NaN in the ragged last piece, and plain rows beside them."""
+    rng = np.random.default_rng(957)
+    S, B, V = 2, 5, 8 * 2048 + 1000
+    tl = rng.normal(0, 3, (S, B, V)).astype(np.float32)
+    tl[0, 0, 3 * 2048 + 5] = np.nan
+    tl[0, 1, 2048:4096] = -np.inf
+    tl[0, 2, :] = -np.inf
+    tl[0, 2, 4 * 2048 + 17:4 * 2048 + 900] = rng.normal(0, 1, 883)
+    tl[0, 3, V - 3] = np.nan
+    tl[0, 4, :2048] = -np.inf
+    tl[0, 4, 5000] = 40.0
+    par = np.tile(np.array([-1, 0, 0, 1, 2], np.int32), (S, 1))
+    tok = rng.integers(0, V, (S, B)).astype(np.int32)
+    u = rng.random((S, B)).astype(np.float32)
+    for T in (1.0, 0.6):
+        g, o, _ = _compare(tl, par, tok, 4, T, u, f"aligned special pieces T={T}")
+        assert g["err"][0] & 8 and not g["err"][1] & 8
+        assert 4 * 2048 + 17 <= g["sample"][0, 2] < 4 * 2048 + 900
+        _compare(wl.to_dtype(tl, "bf16"), par, tok, 4, T, u, f"bf16 special pieces T={T}")
+
+
+def test_rows_longer_than_one_chunk_of_pieces():
+    """600,000-logit rows: 293 pieces, more than the 256 one pass of the piece search
+    holds, with uniforms that land in the second pass."""
+    rng = np.random.default_rng(958)
+    S, B, V = 1, 4, 600_000
+    tl = rng.normal(0, 1, (S, B, V)).astype(np.float32)
+    par = np.array([[-1, 0, 0, 1]], np.int32)
+    tok = rng.integers(0, V, (S, B)).astype(np.int32)
+    u = np.array([[0.1, 0.9, 0.97, 0.9999]], np.float32)
+    g, o, _ = _compare(tl, par, tok, 3, 1.0, u, "600k fp32")
+    assert (g["sample"][0, 1:] > 256 * 2048).all()
+    _compare(wl.to_dtype(tl, "bf16"), par, tok, 3, 1.0, u, "600k bf16")
+
+
 def test_low_temperature_equals_device_greedy():
     w = wl.make("low_budget", 955, parts=("tree", "target"))
     c = w.cfg

@@ -126,6 +126,30 @@ __device__ __forceinline__ float wave_sum_f32(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Inclusive prefix sum over the wave in lane order, through DPP moves that read 0 where
+// they have no source lane: each lane first adds its three predecessors in its 16-lane row
+// (a 4-lane window), then the window 4 lanes back (lanes 4-15 of each row) and the sum 8
+// lanes back (lanes 8-15), which completes every row; then lane 15's total goes into rows
+// 1 and 3 and lane 31's into rows 2 and 3.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ float dpp_f32_or0(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, BANK_MASK,
+                                                                 true));
+}
+__device__ __forceinline__ float wave_incl_scan_f32(float v)
+{
+    float s = v + dpp_f32_or0<0x111, 0xF, 0xF>(v);  // row_shr:1
+    s += dpp_f32_or0<0x112, 0xF, 0xF>(v);           // row_shr:2
+    s += dpp_f32_or0<0x113, 0xF, 0xF>(v);           // row_shr:3
+    s += dpp_f32_or0<0x114, 0xF, 0xE>(s);           // row_shr:4
+    s += dpp_f32_or0<0x118, 0xF, 0xC>(s);           // row_shr:8
+    s += dpp_f32_or0<0x142, 0xA, 0xF>(s);           // row_bcast:15
+    s += dpp_f32_or0<0x143, 0xC, 0xF>(s);           // row_bcast:31
+    return s;
+}
+
 inline jt_status launch_status(hipError_t e) { return e == hipSuccess ? JT_OK : JT_ERR_LAUNCH; }
 
 // ---- launchers (each .hip file implements its own) ----

@@ -15,10 +15,10 @@
 //                          maximum m and weight sum S = sum exp((x - m) / T) with wave
 //                          reductions only; NaN entries weigh 0 and are flagged;
 //   sample_select_kernel   one workgroup per row: Z and the piece whose cumulative weight
-//                          passes r * Z from one block scan over the piece sums, then a
-//                          rescan of that one piece (an L2 / Infinity Cache hit) with one
-//                          block scan in token order for the exact token; the draw goes
-//                          out as a one-entry arg-max key;
+//                          passes r * Z from a wave prefix sum over the piece sums, then a
+//                          rescan of that one piece (an L2 / Infinity Cache hit) in token
+//                          order for the exact token; the draw goes out as a one-entry
+//                          arg-max key;
 //   verify_walk_kernel     the greedy walk, reading the draws as its arg-max.
 #include "jt_internal.h"
 
@@ -85,48 +85,17 @@ __device__ __forceinline__ float smp_weight(float x, float m, float c, bool in_r
     return (in_range && x == x && x != -INFINITY) ? e : 0.f;
 }
 
-__device__ __forceinline__ float block_max_f32(float v, float *red)
-{
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    v = wave_max_f32(v);
-    __syncthreads();
-    if (lane == 0)
-        red[wid] = v;
-    __syncthreads();
-    float t = -INFINITY;
-    for (int w = 0; w < nw; ++w)
-        t = fmaxf(t, red[w]);
-    return t;
-}
-// exclusive prefix sum over the block in thread order; *total gets the block sum
-__device__ __forceinline__ float block_excl_scan_f32(float v, float *red, float *total)
-{
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    float inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(inc, o, kWave);
-        if (lane >= o)
-            inc += y;
-    }
-    __syncthreads();
-    if (lane == 63)
-        red[wid] = inc;
-    __syncthreads();
-    float before = 0.f, all = 0.f;
-    for (int w = 0; w < nw; ++w) {
-        if (w < wid)
-            before += red[w];
-        all += red[w];
-    }
-    *total = all;
-    return before + inc - v;
-}
-
 // Each wave owns ppw consecutive 2048-logit pieces of one row (lane l holds elements
 // (l + 64 i) * E .. + E - 1 of a piece) and writes each piece's (max, weight sum) and NaN
 // bit; no workgroup barrier.  The next piece's loads are issued before the current one is
 // reduced.
+//
+// A whole, aligned piece first takes an unmasked pass: the maximum with the 3-operand
+// NaN-propagating maximum and four unmasked partial sums.  A NaN logit makes its own weight,
+// and so the sum, NaN whatever the maximum came out as; a -inf logit weighs exp2(-inf) = 0
+// already; so a finite sum with a finite maximum is the masked pass's result up to the order
+// of the additions, and anything else (a NaN, +inf, a piece of -inf only, the row's ragged
+// last piece) is redone by the masked pass.
 template <typename T>
 __global__ void __launch_bounds__(kSmpThreads)
 sample_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, float c,
@@ -135,19 +104,30 @@ sample_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, f
 {
     constexpr int E = AVec<T>::kElems;
     constexpr int L = kSmpPiece / (kWave * E);  // 16-byte loads per lane per piece
+    constexpr int NX = L * E;                   // logits per lane per piece
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * (kSmpThreads / kWave) + (threadIdx.x >> 6);
+    // wave-uniform, so that the piece loop and its branches stay scalar
+    const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * (kSmpThreads / kWave) +
+                                                  (threadIdx.x >> 6));
     if (gw >= rows * p.nwave)
         return;
     const int r = gw / p.nwave, wv = gw % p.nwave;
     const T *row = logits + (int64_t)r * row_stride;
     const int pc0 = wv * p.ppw, pc1 = min(p.npiece, pc0 + p.ppw);
+    // pieces [0, nfull) lie wholly inside the row (and are 16-byte aligned when it is)
+    const int nfull = aligned ? V / kSmpPiece : 0;
     uint4 nxt[L];
     auto load = [&](int pc, uint4 (&u)[L]) {
+        const int64_t e0 = (int64_t)pc * kSmpPiece + (int64_t)lane * E;
+        if (pc < nfull) {
 #pragma unroll
-        for (int i = 0; i < L; ++i)
-            u[i] = smp_load16<T>(row, (int64_t)pc * kSmpPiece + (int64_t)(lane + kWave * i) * E, V,
-                                 aligned);
+            for (int i = 0; i < L; ++i)
+                u[i] = *reinterpret_cast<const uint4 *>(row + e0 + kWave * E * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i)
+                u[i] = smp_load16<T>(row, e0 + kWave * E * i, V, aligned);
+        }
     };
     if (pc0 < pc1)
         load(pc0, nxt);
@@ -158,32 +138,52 @@ sample_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, f
             smp_unpack<T>(nxt[i], x[i]);
         if (pc + 1 < pc1)
             load(pc + 1, nxt);
-        const int64_t base = (int64_t)pc * kSmpPiece;
-        float m = -INFINITY;
-        bool nan = false;
+        float M = -INFINITY, S = __builtin_nanf("");
+        if (pc < nfull) {
+            float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < L; ++i) {
-            const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
+            for (int j = 0; j < NX; j += 2) {
+                m0 = __builtin_elementwise_maximum(m0, x[j / E][j % E]);
+                m1 = __builtin_elementwise_maximum(m1, x[j / E][j % E + 1]);
+            }
+            M = wave_max_f32(__builtin_elementwise_maximum(m0, m1));
+            float s4[4];
 #pragma unroll
-            for (int k = 0; k < E; ++k)
-                if (e0 + k < V) {
-                    nan |= x[i][k] != x[i][k];
-                    m = fmaxf(m, x[i][k]);
-                }
+            for (int j = 0; j < NX; ++j) {
+                const float w = __builtin_amdgcn_exp2f((x[j / E][j % E] - M) * c);
+                s4[j & 3] = j < 4 ? w : s4[j & 3] + w;
+            }
+            S = wave_sum_f32((s4[0] + s4[1]) + (s4[2] + s4[3]));
         }
-        const float M = wave_max_f32(m);
-        float s = 0.f;
-        if (M != -INFINITY) {
+        bool any_nan = false;
+        if (!(M > -INFINITY && M < INFINITY && S == S)) {
+            const int64_t base = (int64_t)pc * kSmpPiece;
+            float m = -INFINITY;
+            bool nan = false;
 #pragma unroll
             for (int i = 0; i < L; ++i) {
                 const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
 #pragma unroll
                 for (int k = 0; k < E; ++k)
-                    s += smp_weight(x[i][k], M, c, e0 + k < V);
+                    if (e0 + k < V) {
+                        nan |= x[i][k] != x[i][k];
+                        m = fmaxf(m, x[i][k]);
+                    }
             }
+            M = wave_max_f32(m);
+            float s = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int i = 0; i < L; ++i) {
+                    const int64_t e0 = base + (int64_t)(lane + kWave * i) * E;
+#pragma unroll
+                    for (int k = 0; k < E; ++k)
+                        s += smp_weight(x[i][k], M, c, e0 + k < V);
+                }
+            }
+            S = wave_sum_f32(s);
+            any_nan = __ballot(nan) != 0ull;
         }
-        const float S = wave_sum_f32(s);
-        const bool any_nan = __ballot(nan) != 0ull;
         if (lane == 0) {
             ws_ms[(int64_t)r * p.npiece + pc] = make_float2(M, S);
             ws_nan[(int64_t)r * p.npiece + pc] = any_nan ? 1u : 0u;
@@ -193,6 +193,11 @@ sample_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int V, f
 
 // One workgroup per row: the draw.  Writes a one-entry arg-max key (any nonzero order
 // code, id = the draw) and NaN bit per row for the walk, and the draw to sample_out.
+//
+// Every wave finds the piece by itself from the piece sums (wave reductions and a DPP
+// prefix sum, no LDS): the same instructions on the same data, so the same piece in each.
+// The four waves then share the rescan of that piece in token order, with one exchange of
+// wave totals and one of per-wave results through LDS.
 template <typename T>
 __global__ void __launch_bounds__(kSmpThreads)
 sample_select_kernel(const T *__restrict__ logits, int64_t row_stride, int V, float c,
@@ -202,90 +207,98 @@ sample_select_kernel(const T *__restrict__ logits, int64_t row_stride, int V, fl
                      int32_t *__restrict__ sample_out, bool aligned)
 {
     constexpr int E = AVec<T>::kElems;
-    constexpr int NT = kSmpThreads;
-    constexpr int PER = kSmpPiece / NT;  // logits of the rescanned piece per thread (8)
+    constexpr int NWV = kSmpThreads / kWave;
+    constexpr int PER = kSmpPiece / kSmpThreads;  // logits of the rescanned piece per thread (8)
+    constexpr int KP = 4;                         // piece sums per lane per chunk
+    constexpr int CH = kWave * KP;                // pieces per chunk
     static_assert(PER % E == 0, "whole 16-byte loads per thread");
-    __shared__ float red[NT / 64];
-    __shared__ int pick, lo_pos, hi_pos;
-    __shared__ float pick_before;
-    const int tid = threadIdx.x;
+    __shared__ float wtot[NWV];
+    __shared__ int wpick[NWV], wlo[NWV], whi[NWV];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int r = blockIdx.x;
     const float2 *ms = ws_ms + (int64_t)r * p.npiece;
+    const uint32_t *nr = ws_nan + (int64_t)r * p.npiece;
     const T *row = logits + (int64_t)r * row_stride;
+    const float u = uniform[r];
 
     // row maximum and NaN bit
     float m = -INFINITY;
     uint32_t nb = 0u;
-    for (int i = tid; i < p.npiece; i += NT) {
+    for (int i = lane; i < p.npiece; i += kWave) {
         m = fmaxf(m, ms[i].x);
-        nb |= ws_nan[(int64_t)r * p.npiece + i];
+        nb |= nr[i];
     }
-    const float M = block_max_f32(m, red);
-    const bool nan = __syncthreads_or(nb != 0u);
+    const float M = wave_max_f32(m);
+    const bool nan = __ballot(nb != 0u) != 0ull;
     int draw = 0;  // a row with no finite maximum draws token 0, like its arg-max
     if (M != -INFINITY) {
         auto piece_w = [&](int i) {
+            if (i >= p.npiece)
+                return 0.f;
             const float2 q = ms[i];
             return q.x == -INFINITY ? 0.f : q.y * __builtin_amdgcn_exp2f((q.x - M) * c);
         };
-        // Z, then the piece where the cumulative weight passes r * Z: one block scan per
-        // NT pieces (one in all for rows up to 524,288 logits)
+        // Z over chunks of CH pieces, lane l holding pieces KP l .. KP l + KP - 1 of each
         float Z = 0.f;
-        for (int i0 = 0; i0 < p.npiece; i0 += NT) {
-            const int i = i0 + tid;
-            float tot;
-            block_excl_scan_f32(i < p.npiece ? piece_w(i) : 0.f, red, &tot);
-            Z += tot;
+        for (int i0 = 0; i0 < p.npiece; i0 += CH) {
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < KP; ++k)
+                s += piece_w(i0 + lane * KP + k);
+            Z += wave_sum_f32(s);
         }
-        const float target = uniform[r] * Z;
-        if (tid == 0) {
-            pick = INT_MAX;
-            pick_before = 0.f;
-        }
-        float carry = 0.f;
+        const float target = u * Z;
+        // the piece whose cumulative interval [before, before + w) holds the target
         int pc = -1;
-        float before_pc = 0.f;
-        for (int i0 = 0; i0 < p.npiece && pc < 0; i0 += NT) {
-            const int i = i0 + tid;
-            const float w = i < p.npiece ? piece_w(i) : 0.f;
-            float tot;
-            const float before = carry + block_excl_scan_f32(w, red, &tot);
-            if (w > 0.f && before <= target && before + w > target)
-                atomicMin(&pick, i);
-            __syncthreads();
-            if (pick != INT_MAX && i == pick)
-                pick_before = before;
-            __syncthreads();
-            if (pick != INT_MAX) {
-                pc = pick;
-                before_pc = pick_before;
+        float before_pc = 0.f, carry = 0.f;
+        for (int i0 = 0; i0 < p.npiece && pc < 0; i0 += CH) {
+            float w[KP], s = 0.f;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                w[k] = piece_w(i0 + lane * KP + k);
+                s += w[k];
             }
-            carry += tot;
+            const float incl = wave_incl_scan_f32(s);
+            float b = carry + (incl - s);
+            int hit = -1;
+            float hb = 0.f;
+#pragma unroll
+            for (int k = 0; k < KP; ++k) {
+                if (hit < 0 && w[k] > 0.f && b <= target && b + w[k] > target) {
+                    hit = i0 + lane * KP + k;
+                    hb = b;
+                }
+                b += w[k];
+            }
+            const uint64_t any = __ballot(hit >= 0);
+            if (any) {
+                const int at = __builtin_ctzll(any);
+                pc = __builtin_amdgcn_readlane(hit, at);
+                before_pc = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hb), at));
+            }
+            carry += __builtin_bit_cast(float,
+                                        __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
         }
         if (pc < 0) {
             // rounding left r * Z past the last piece: the last piece with weight, entered
             // at its end (its last weighted logit is drawn below)
-            if (tid == 0) {
-                int last = 0;
-                for (int i = p.npiece - 1; i >= 0; --i)
-                    if (piece_w(i) > 0.f) {
-                        last = i;
-                        break;
-                    }
-                pick = last;
-            }
-            __syncthreads();
-            pc = pick;
+            int last = -1;
+            for (int i = lane; i < p.npiece; i += kWave)
+                if (piece_w(i) > 0.f)
+                    last = i;
+            const uint64_t any = __ballot(last >= 0);
+            pc = any ? __builtin_amdgcn_readlane(last, 63 - __builtin_clzll(any)) : 0;
             before_pc = -INFINITY;  // the crossing search below then fails, past the end
         }
-        // rescan piece pc in token order: thread tid holds logits PER*tid .. PER*tid+PER-1
-        const int64_t base = (int64_t)pc * kSmpPiece + (int64_t)tid * PER;
+        // rescan piece pc in token order: thread t holds logits PER t .. PER t + PER - 1
+        const int64_t base = (int64_t)pc * kSmpPiece + (int64_t)threadIdx.x * PER;
         float x[PER];
 #pragma unroll
         for (int q = 0; q < PER / E; ++q) {
-            const uint4 u = smp_load16<T>(row, base + q * E, V, aligned);
+            const uint4 v = smp_load16<T>(row, base + q * E, V, aligned);
             float xe[E];
-            smp_unpack<T>(u, xe);
+            smp_unpack<T>(v, xe);
 #pragma unroll
             for (int k = 0; k < E; ++k)
                 x[q * E + k] = xe[k];
@@ -301,26 +314,37 @@ sample_select_kernel(const T *__restrict__ logits, int64_t row_stride, int V, fl
                 last_pos = max(last_pos, (int)(base + k));
             }
         }
-        float tot;
-        float cum = before_pc + block_excl_scan_f32(s, red, &tot);
-        if (tid == 0) {
-            pick = INT_MAX;
-            lo_pos = INT_MAX;
-            hi_pos = -1;
-        }
+        const float incl = wave_incl_scan_f32(s);
+        if (lane == 63)
+            wtot[wid] = incl;
         __syncthreads();
+        float off = 0.f;
+        for (int q = 0; q < wid; ++q)
+            off += wtot[q];
+        float cum = before_pc + (off + (incl - s));
+        int hit = INT_MAX;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const float nx = cum + w[k];
-            if (w[k] > 0.f && cum <= target && nx > target)
-                atomicMin(&pick, (int)(base + k));
+            if (hit == INT_MAX && w[k] > 0.f && cum <= target && nx > target)
+                hit = (int)(base + k);
             cum = nx;
         }
-        if (first_pos != INT_MAX)
-            atomicMin(&lo_pos, first_pos);
-        if (last_pos >= 0)
-            atomicMax(&hi_pos, last_pos);
+        const uint64_t bh = __ballot(hit != INT_MAX), bl = __ballot(first_pos != INT_MAX),
+                       bu = __ballot(last_pos >= 0);
+        if (lane == 0) {
+            wpick[wid] = bh ? __builtin_amdgcn_readlane(hit, __builtin_ctzll(bh)) : INT_MAX;
+            wlo[wid] = bl ? __builtin_amdgcn_readlane(first_pos, __builtin_ctzll(bl)) : INT_MAX;
+            whi[wid] = bu ? __builtin_amdgcn_readlane(last_pos, 63 - __builtin_clzll(bu)) : -1;
+        }
         __syncthreads();
+        int pick = INT_MAX, lo_pos = INT_MAX, hi_pos = -1;
+#pragma unroll
+        for (int q = 0; q < NWV; ++q) {
+            pick = min(pick, wpick[q]);
+            lo_pos = min(lo_pos, wlo[q]);
+            hi_pos = max(hi_pos, whi[q]);
+        }
         // no crossing inside (rounding near an end of the piece): its first or last
         // weighted logit, whichever end the target lies past (-inf start: past the end)
         if (pick != INT_MAX)
@@ -330,7 +354,7 @@ sample_select_kernel(const T *__restrict__ logits, int64_t row_stride, int V, fl
         if (draw < 0 || draw == INT_MAX)
             draw = 0;
     }
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         keys[r] = rank_key(0.f, (uint32_t)draw);
         nan_out[r] = nan ? 1u : 0u;
         if (sample_out)
