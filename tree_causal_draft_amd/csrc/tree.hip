@@ -16,7 +16,8 @@
 // table in LDS: a pop moves no data between lanes beyond the popped node's score and
 // depth.  Parent and token stay in registers until the end.  Pops are inherently
 // sequential (a child may outrank every queued node), so the kernel is bound by the
-// latency of one pop, about a hundred dependent instructions (0.3 us measured).
+// latency of one pop, about a hundred dependent instructions (0.3 us measured).  Nodes at
+// the depth limit are never queued: their pops would expand nothing.
 #include "jt_internal.h"
 
 namespace jt {
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
                     key[k] = 0u;
         }
         if (dv >= N)
-            continue;  // at the depth limit: popped, not expanded
+            continue;  // at the depth limit: popped, not expanded (only the root when N = 0)
         // children n .. n+cnt-1; cnt <= 16, so a lane receives at most one of them
         const int cnt = min(W, B - n);
         const int r = (lane - n) & (kWave - 1);
@@ -137,7 +138,9 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
             const float cs = tree_add(sv, inc[e]);
             const int ct = cid[e];
             const int k = (n + r) >> 6;
-            const uint32_t ck = tree_key(true, cs);
+            // a child at the depth limit is never expanded, so its pop would change nothing:
+            // it is not queued at all, and the pops that remain are the same, in order
+            const uint32_t ck = tree_key(dv + 1 < N, cs);
 #pragma unroll
             for (int q = 0; q < kTreeSlots; ++q)
                 if (q == k) {
