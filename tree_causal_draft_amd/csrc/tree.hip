@@ -100,16 +100,11 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
         if (M == 0u)
             break;  // queue empty
         // the lowest node index holding M: slot k first (lower k, lower index), then lane
-        int kk = kTreeSlots - 1;
-        uint64_t hit = 0ull;
-#pragma unroll
-        for (int k = 0; k < kTreeSlots; ++k) {
-            const uint64_t b = __ballot(key[k] == M);
-            if (hit == 0ull && b != 0ull) {
-                hit = b;
-                kk = k;
-            }
-        }
+        static_assert(kTreeSlots == 4, "four slots per lane");
+        const uint64_t b0 = __ballot(key[0] == M), b1 = __ballot(key[1] == M),
+                       b2 = __ballot(key[2] == M), b3 = __ballot(key[3] == M);
+        const int kk = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
+        const uint64_t hit = b0 ? b0 : b1 ? b1 : b2 ? b2 : b3;
         const int ln = (int)__builtin_ctzll(hit);
         const int v = ln + kWave * kk;
         float s_sel = sc[0];
@@ -142,14 +137,14 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
             // it is not queued at all, and the pops that remain are the same, in order
             const uint32_t ck = tree_key(dv + 1 < N, cs);
 #pragma unroll
-            for (int q = 0; q < kTreeSlots; ++q)
-                if (q == k) {
-                    sc[q] = cs;
-                    dp[q] = dv + 1;
-                    key[q] = ck;
-                    pa[q] = v;
-                    tk[q] = ct;
-                }
+            for (int q = 0; q < kTreeSlots; ++q) {
+                const bool at = q == k;  // selects, not a branch per slot
+                sc[q] = at ? cs : sc[q];
+                dp[q] = at ? dv + 1 : dp[q];
+                key[q] = at ? ck : key[q];
+                pa[q] = at ? v : pa[q];
+                tk[q] = at ? ct : tk[q];
+            }
         }
         n += cnt;
     }
