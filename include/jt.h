@@ -260,7 +260,9 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
  *   sample_out    int32 [S,B] (optional) out: the draw at every node
  * A draw whose uniform lies within about 1e-5 of its token's interval end (as a fraction of
  * the row's weight) may go to the neighbouring token under a different summation order.
- * Supported: temperature > 0 and finite; otherwise as jt_verify_greedy.
+ * Supported: temperature > 0 and finite, with log2(e) / temperature finite in fp32 (so
+ * temperature >= about 4.2e-39; smaller values return JT_ERR_SHAPE); otherwise as
+ * jt_verify_greedy.
  */
 size_t jt_verify_sampled_workspace_size(int32_t S, int32_t B, int32_t V, jt_dtype dtype);
 jt_status jt_verify_sampled(const void *target_logits, int64_t row_stride, int32_t V,
@@ -336,6 +338,18 @@ jt_status jt_commit_accepted_kv(const int32_t *accept_len, const int32_t *accept
                                 int32_t num_blocks, const int32_t *prefix_len,
                                 int32_t max_prefix, int32_t *new_prefix_len, int32_t *err,
                                 void *stream);
+
+/*
+ * Measurement helper, not a step of the method: the bf16 matrix-core rate the device
+ * sustains, reported beside the nominal dense peak.  Launches `blocks` workgroups of 4
+ * waves; every wave issues iters * 8 independent v_mfma_f32_32x32x16_bf16 (32x32x16
+ * products, 32,768 flops each), so the work is blocks * 4 * iters * 8 * 32768 flops; time
+ * it with events on `stream`.  4 workgroups per compute unit (1024 on MI355X) put 4 waves
+ * on every SIMD.
+ *   out   float [blocks * 256] device, overwritten with the accumulators' sums.
+ * Supported: iters >= 1, blocks >= 1.
+ */
+jt_status jt_probe_mfma_rate(int32_t iters, int32_t blocks, float *out, void *stream);
 
 #ifdef __cplusplus
 }

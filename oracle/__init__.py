@@ -45,9 +45,24 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile jt_oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer (any report
+    aborts) into ``path``; a process loads it through JT_ORACLE_LIB with the sanitizer
+    runtimes preloaded (the sanitized-pins test does exactly that)."""
+    subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-Wall",
+                    "-Wextra", "-o", path, _SRC, "-lm"], check=True)
+    return path
+
+
 def _load():
     global _lib
     if _lib is None:
+        alt = os.environ.get("JT_ORACLE_LIB")
+        if alt:
+            _lib = ctypes.CDLL(alt)
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = ctypes.CDLL(_LIB)

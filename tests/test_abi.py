@@ -92,8 +92,13 @@ def test_host_validation_returns_before_launch():
         return L.jt_verify_sampled(nul, 1000, 1000, 1, ctypes.c_float(T), nul, nul, nul, nul,
                                    nul, 1, 16, N, nul, nul, nul, nul, nul, nul, 0, nul)
     assert smp(T=0.0) == 2 and smp(T=-1.0) == 2 and smp(T=float("inf")) == 2
+    # log2(e)/T overflows fp32 below about 4.2e-39 (a subnormal T): refused, not NaN weights
+    assert smp(T=1e-39) == 2 and smp(T=1e-38) != 2
     assert smp(N=256) == 2
     assert smp() == 1
+    # the matrix-core rate probe
+    assert L.jt_probe_mfma_rate(0, 4, nul, nul) == 2 and L.jt_probe_mfma_rate(4, 0, nul, nul) == 2
+    assert L.jt_probe_mfma_rate(4, 4, nul, nul) == 1
 
 
 def test_workspace_queries_are_pure():

@@ -12,7 +12,8 @@ import torch
 import oracle
 import tree_causal_draft_amd as jt
 from tree_causal_draft_amd import workload as wl
-from gpu_util import assert_attention_close, dev, host, need_gpu
+from gpu_util import (assert_attention_close, assert_lse_close, block_rows, dev, host,
+                      need_gpu, oracle_attention)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +48,7 @@ def _check(w, what, sel=None, scale=0.0):
         glse = lse[sel[:, 0], sel[:, 1], sel[:, 2]]
     assert np.array_equal(err, rerr)
     assert_attention_close(got, ref, cfg.dtype, what)
-    tol = 1e-5 if cfg.dtype == "f32" else 2e-3
-    assert np.abs(glse - rlse).max() <= tol * max(1.0, np.abs(rlse).max()), what
+    assert_lse_close(glse, rlse, cfg.dtype, what)
     return out
 
 
@@ -161,6 +161,24 @@ def _sample(w, n, seed):
 def test_config_full_size_sampled(name):
     w = wl.make(name, 480, parts=("attn",))
     _check(w, name, sel=_sample(w, 96, 1))
+
+
+@pytest.mark.parametrize("name", ["ragged", "moe_verify"])
+@pytest.mark.parametrize("sharp", [False, True])
+def test_config_full_size_whole_blocks(name, sharp):
+    """ragged (paged, shuffled table, balanced schedule) and moe_verify at full size: every
+    row of one whole 256-row block of query rows per sequence (a different KV head and
+    block from one sequence to the next), and the sharp variant (q, k ~ N(0, 1))."""
+    w = wl.make(name, 482, parts=("attn",), qk_std=1.0 if sharp else None)
+    cfg = w.cfg
+    print(f"[attn] {name} sharp={sharp} whole blocks", flush=True)
+    out, lse, err = _run_gpu(w)
+    sel, ref, rlse, rerr = oracle_attention(w, block_rows(w))
+    assert np.array_equal(err, rerr)
+    got = out[sel[:, 0], sel[:, 1], sel[:, 2]]
+    glse = lse[sel[:, 0], sel[:, 1], sel[:, 2]]
+    assert_attention_close(got, ref, cfg.dtype, f"{name} sharp={sharp}")
+    assert_lse_close(glse, rlse, cfg.dtype, f"{name} sharp={sharp}")
 
 
 @pytest.mark.parametrize("name", ["low_budget", "high_budget"])

@@ -4,7 +4,8 @@ The fused call must reproduce, bit for bit, every integer and attention output o
 four separate calls on the same inputs (those are held to the oracle by the other GPU
 tests), and its err must be the OR of their flags.  Log-probs and row LSE agree to the
 log-prob tolerance: the step may cut a row into pieces differently, so its sums add in
-another order.  One case is also compared with the oracle directly.  Attention outputs of
+another order.  The benchmark's own inputs (every configuration at full size) are also compared with the
+oracle directly.  Attention outputs of
 a sequence with a bad parent array are unspecified and are not compared.
 """
 import numpy as np
@@ -14,7 +15,9 @@ import torch
 import oracle
 from tree_causal_draft_amd import workload as wl
 from tree_causal_draft_amd.step import DeviceStep
-from gpu_util import BF16_ATOL, BF16_RTOL, LP_ATOL, LP_RTOL, assert_lp_close, host, need_gpu
+from gpu_util import (BF16_ATOL, BF16_RTOL, LP_ATOL, LP_RTOL, assert_attention_close,
+                      assert_lp_close, assert_lse_close, block_rows, host, need_gpu,
+                      oracle_attention)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +60,69 @@ def _compare(w, what, tamper=None):
             a, b = a[keep], b[keep]
         assert torch.equal(a, b), (what, k)
     return st, err_sep
+
+
+def _small(name, **kw):
+    base = dict(V=8192)
+    base.update(kw)
+    return base
+
+
+# the benchmark's inputs: bench.py seeds workload k (in CONFIG_ORDER) with 1000 * (k + 1)
+BENCH_SEED = {n: 1000 * (k + 1) for k, n in enumerate(wl.CONFIG_ORDER)}
+
+
+def _against_oracle(w, st, sel=None):
+    """The fused step's outputs against the oracle on the same inputs: top-W ids and the
+    verification outputs bit for bit, log-probs and row LSE within the log-prob tolerance,
+    attention (every row, or the rows `sel`) and its LSE within the bf16 bounds."""
+    c = w.cfg
+    ids, lp, lse = oracle.topw(w.draft_logits, c.W)
+    assert np.array_equal(host(st.ids), ids), "top-W ids"
+    assert_lp_close(host(st.logprob), lp, "logprob")
+    assert_lp_close(host(st.row_lse), lse, "row_lse")
+    ref = oracle.verify_greedy(w.target_logits, w.parent, w.tokens, c.N)
+    for k, t in (("accept_len", st.accept_len), ("accept_path", st.accept_path),
+                 ("bonus", st.bonus), ("argmax", st.argmax)):
+        assert np.array_equal(host(t), ref[k]), k
+    sel, out, rlse, _ = oracle_attention(w, sel)
+    got, glse = host(st.attn_out), host(st.lse)
+    got = got[sel[:, 0], sel[:, 1], sel[:, 2]]
+    glse = glse[sel[:, 0], sel[:, 1], sel[:, 2]]
+    assert_attention_close(got, out, c.dtype, f"{c.name} attention ({len(sel)} rows)")
+    e = assert_lse_close(glse, rlse, c.dtype, f"{c.name} lse")
+    print(f"[step] {c.name}: oracle parity ok, {len(sel)} attention rows, "
+          f"max |lse err| {e:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "low_budget", "high_budget"])
+def test_bench_inputs_against_oracle(name):
+    """The benchmarked call on the benchmark's own inputs (its seed, full vocabulary): equal
+    to the four calls bit for bit, and to the oracle on every output and attention row.
+    tiny is fp32, which the fused call does not take: its step is the four calls."""
+    w = wl.make(name, BENCH_SEED[name])
+    if w.cfg.dtype == "f32":
+        need_gpu()
+        st = DeviceStep(w, "cuda:0")
+        st.run()
+        torch.cuda.synchronize()
+        err = st.err_mask | st.err_attn | st.err_verify
+    else:
+        st, err = _compare(w, name + " bench inputs")
+    assert int(err.abs().sum()) == 0
+    _against_oracle(w, st)
+
+
+@pytest.mark.parametrize("name", ["ragged", "moe_verify"])
+def test_full_vocab_balanced_schedule(name):
+    """ragged and moe_verify at full size (V = 151,936; moe_verify reads 622 MB of target
+    logits) through the four-launch balanced schedule, on the benchmark's inputs: equal to
+    the four calls bit for bit, and to the oracle on ids, acceptance and every row of one
+    whole 256-row block of query rows per sequence."""
+    w = wl.make(name, BENCH_SEED[name])
+    st, err = _compare(w, name + " full V")
+    assert int(err.abs().sum()) == 0
+    _against_oracle(w, st, sel=block_rows(w))
 
 
 def _small(name, **kw):

@@ -104,3 +104,22 @@ def test_entropy_nan_and_uniform_rows():
     x[1, 77] = np.nan                    # a NaN: NaN entropy
     x[2, :5] = 30.0                      # five equal maxima far above the rest: ~ln 5
     _check(wl.to_dtype(x, "bf16"), 4, what="nan / uniform / 5-way")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [700, 151936])
+def test_wth_entry_neg_inf(dtype, V):
+    """Rows with fewer than W finite logits: the list ends in -inf entries (lowest ids
+    first among them) whose log-probs must be exactly -inf; only -inf matches an infinite
+    reference in the comparison."""
+    W = 8
+    rng = np.random.default_rng(V + W)
+    x = np.full((4, V), -np.inf, np.float32)
+    x[0, [3, V - 1]] = [1.0, 2.0]                                   # two finite
+    x[1, rng.choice(V, W - 1, replace=False)] = rng.normal(0, 3, W - 1)  # the W-th is -inf
+    x[2, V // 2] = 0.0                                              # one finite
+    x[3] = rng.normal(0, 3, V)                                      # all finite (control)
+    x[3, :: 5] = -np.inf
+    r_ids, r_lp, _ = oracle.topw(wl.to_dtype(x, dtype), W)
+    assert np.isneginf(r_lp[:3]).sum() == (W - 2) + 1 + (W - 1)
+    _check(wl.to_dtype(x, dtype), W, what=f"W-th -inf {dtype} V={V}")

@@ -60,6 +60,19 @@ def test_hand_worked_cases():
         assert int(got["n_nodes"][0]) == c["n_nodes"], c["why"]
 
 
+def test_float32_score_order():
+    """The hand-worked case whose float32 path scores tie where the exact sums do not: the
+    device must pop in the float32 order, as the oracle does."""
+    with open(os.path.join(GOLD, "bestfirst_fp32.json")) as fh:
+        g = json.load(fh)
+    ids = np.array(g["ids"], np.int32)
+    lp = np.array([[int(x, 16) for x in row] for row in g["logprob_hex"]],
+                  np.uint32).view(np.float32)
+    got = _both(ids, lp, g["N"], g["B"], "float32 order", root_token=[g["root_token"]])
+    assert got["parent"][0].tolist() == g["expected"]["parent"]
+    assert got["tokens"][0].tolist() == g["expected"]["tokens"]
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_random_lists(seed):
     rng = np.random.default_rng(500 + seed)

@@ -9,6 +9,7 @@ import oracle
 import tree_causal_draft_amd as jt
 from tree_causal_draft_amd import workload as wl
 from gpu_util import dev, host, need_gpu
+from tree_util import enumerate_accept
 
 pytestmark = pytest.mark.gpu
 
@@ -47,22 +48,36 @@ def test_config_unplanted_ties(name):
     _check(w.target_logits, w.parent, w.tokens, w.cfg.N, what=name + " unplanted")
 
 
-def test_exhaustive_tiny_trees():
-    """All parent arrays with B <= 5 x all accept patterns (duplicates included)."""
-    for B in range(1, 6):
-        V = 2 * B + 2
-        pats = list(itertools.product([0, 1], repeat=B - 1))
-        pars, toks = [], []
-        for tail in itertools.product(*[range(i) for i in range(1, B)]):
-            parent = [-1] + list(tail)
-            for pat in pats:
-                tok = [0] + [2 * parent[u] + (0 if pat[u - 1] else 1) for u in range(1, B)]
-                pars.append(parent)
-                toks.append(tok)
-        S = len(pars)
-        x = np.zeros((S * B, V), np.float32)
-        x[np.arange(S * B), np.tile(2 * np.arange(B), S)] = 1.0
-        _check(x, np.array(pars), np.array(toks), B, what=f"exhaustive B={B}")
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7])
+def test_exhaustive_tiny_trees(B):
+    """Every parent array with B <= 7 nodes x every accept pattern (2^(B-1)), one batched
+    call per B (B = 7: 720 x 64 = 46,080 sequences).  GPU, oracle and the set-based
+    enumerator must agree bit for bit.  The target argmax at node v is token 2v; the edge
+    into u carries 2*parent[u] when its pattern bit is set (accepted), 2*parent[u] + 1
+    otherwise, so sibling tokens may repeat (several accepted paths, lowest leaf wins)."""
+    V = 2 * B + 2
+    pats = np.array(list(itertools.product([0, 1], repeat=B - 1)), np.int32).reshape(2 ** (B - 1), B - 1)
+    tails = list(itertools.product(*[range(i) for i in range(1, B)]))
+    P = len(pats)
+    par = np.empty((len(tails) * P, B), np.int32)
+    tok = np.zeros((len(tails) * P, B), np.int32)
+    for k, tail in enumerate(tails):
+        parent = np.array([-1] + list(tail), np.int32)
+        rows = slice(k * P, (k + 1) * P)
+        par[rows] = parent
+        if B > 1:
+            tok[rows, 1:] = 2 * parent[1:] + (1 - pats)
+    S = len(par)
+    am = 2 * np.arange(B)
+    x = np.zeros((S * B, V), np.float32)
+    x[np.arange(S * B), np.tile(am, S)] = 1.0
+    r, ref = _check(x, par, tok, B, what=f"exhaustive B={B}")
+    got_len, got_path, got_bonus = host(r["accept_len"]), host(r["accept_path"]), host(r["bonus"])
+    for s in range(S):
+        ok = (1,) + tuple(int(b) for b in tok[s, 1:] == am[par[s, 1:]]) if B > 1 else (1,)
+        L, path, bonus = enumerate_accept(par[s].tolist(), ok, am)
+        assert got_len[s] == L and got_bonus[s] == bonus, (B, s)
+        assert got_path[s, :L + 1].tolist() == path and (got_path[s, L + 1:] == -1).all(), (B, s)
 
 
 def test_ties_nan_and_flags():

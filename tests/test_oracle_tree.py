@@ -138,3 +138,30 @@ def test_degenerate_shapes():
     o = oracle.build_tree(np.arange(6, dtype=np.int32)[:, None], np.full((6, 1), -0.5, np.float32),
                           6, 10)
     assert o["parent"][0, :7].tolist() == [-1, 0, 1, 2, 3, 4, 5] and int(o["n_nodes"][0]) == 7
+
+
+def _fp32_case():
+    with open(os.path.join(GOLD, "bestfirst_fp32.json")) as fh:
+        g = json.load(fh)
+    lp = np.array([[int(x, 16) for x in row] for row in g["logprob_hex"]],
+                  np.uint32).view(np.float32)
+    return g, np.array(g["ids"], np.int32), lp
+
+
+def test_scores_accumulate_in_float32():
+    """Path scores are float32 sums of float32 log-probs (the builder's inputs and its score
+    output are float32), and the queue orders those float32 values.  In this hand-worked
+    case the unrounded sums would pop node 3 before node 2; their float32 sums tie, so node
+    2 (lower index) pops first and the two trees differ in nodes 5 and 6."""
+    g, ids, lp = _fp32_case()
+    o = oracle.build_tree(ids, lp, g["N"], g["B"], root_token=[g["root_token"]])
+    e = g["expected"]
+    assert o["parent"][0].tolist() == e["parent"]
+    assert o["tokens"][0].tolist() == e["tokens"]
+    want = np.array([int(x, 16) for x in e["score_hex"]], np.uint32)
+    assert np.array_equal(o["score"][0].view(np.uint32), want)
+    assert int(o["n_nodes"][0]) == e["n_nodes"]
+    # the case discriminates: exact sums order nodes 2 and 3 the other way
+    exact3 = float(lp[0, 0]) + float(lp[1, 0])
+    assert exact3 > float(lp[0, 1]) and np.float32(lp[0, 0] + lp[1, 0]) == lp[0, 1]
+    assert g["fp64_order_would_give"]["parent"] != e["parent"]

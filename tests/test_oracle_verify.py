@@ -19,6 +19,7 @@ import pytest
 
 import oracle
 from tree_causal_draft_amd import workload as wl
+from tree_util import enumerate_accept as _enumerate
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -39,24 +40,6 @@ def test_hand_worked_tree7():
     assert r["accept_len"][0] == e["accept_len"]
     assert r["accept_path"][0].tolist() == e["accept_path"]
     assert r["bonus"][0] == e["bonus"]
-
-
-def _enumerate(parent, ok, am):
-    """Independent set-based enumeration: accepted nodes grow from the root in index order."""
-    B = len(parent)
-    acc = {0}
-    depth = [0] * B
-    for u in range(1, B):
-        depth[u] = depth[parent[u]] + 1
-        if parent[u] in acc and ok[u]:
-            acc.add(u)
-    best = min(acc, key=lambda v: (-depth[v], v))
-    path = []
-    u = best
-    while u != -1:
-        path.append(u)
-        u = parent[u] if u else -1
-    return depth[best], path[::-1], am[best]
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7])

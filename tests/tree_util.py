@@ -3,8 +3,31 @@ and the GPU tests): parents come first; the children of a node are contiguous, i
 order, carry their depth's candidates and add that depth's increment to the parent's
 score; expansions leave the queue in (score descending, index ascending) order; and when
 the budget is spent, no unexpanded node above the depth limit would have popped earlier.
+
+enumerate_accept() is an independent set-based statement of greedy acceptance, used to
+check both the oracle and the GPU walk on every tiny tree.
 """
 import numpy as np
+
+
+def enumerate_accept(parent, ok, am):
+    """Accepted nodes grow from the root in index order (a parent precedes its children):
+    u joins when its parent has joined and its edge is ok.  The deepest accepted node,
+    lowest index on ties, ends the path; returns (accept_len, path, bonus)."""
+    B = len(parent)
+    acc = {0}
+    depth = [0] * B
+    for u in range(1, B):
+        depth[u] = depth[parent[u]] + 1
+        if parent[u] in acc and ok[u]:
+            acc.add(u)
+    best = min(acc, key=lambda v: (-depth[v], v))
+    path = []
+    u = best
+    while u != -1:
+        path.append(u)
+        u = parent[u] if u else -1
+    return depth[best], path[::-1], am[best]
 
 
 def check_invariants(ids, lp, N, W, B, o, ent=None, w_lp=1.0, w_ent=0.0):

@@ -24,7 +24,8 @@ EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
            "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
            "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy",
            "jt_step_workspace_size", "jt_draft_verify_step", "jt_build_tree_best_first",
-           "jt_commit_accepted_kv", "jt_verify_sampled_workspace_size", "jt_verify_sampled")
+           "jt_commit_accepted_kv", "jt_verify_sampled_workspace_size", "jt_verify_sampled",
+           "jt_probe_mfma_rate")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -77,9 +78,10 @@ def lib() -> ctypes.CDLL:
         L.jt_verify_sampled_workspace_size.argtypes = [_i32, _i32, _i32, ctypes.c_int]
         L.jt_verify_sampled.argtypes = ([_vp, _i64, _i32, ctypes.c_int, ctypes.c_float] +
                                         [_vp] * 5 + [_i32] * 3 + [_vp] * 6 + [_sz, _vp])
+        L.jt_probe_mfma_rate.argtypes = [_i32, _i32, _vp, _vp]
         for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
                    "jt_verify_greedy", "jt_draft_verify_step", "jt_build_tree_best_first",
-                   "jt_commit_accepted_kv", "jt_verify_sampled"):
+                   "jt_commit_accepted_kv", "jt_verify_sampled", "jt_probe_mfma_rate"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -403,3 +405,14 @@ def verify_sampled(target_logits, parent, tokens, anc, depth, N, temperature, un
                                    _stream(stream)), "jt_verify_sampled")
     return accept_len, accept_path, bonus, sample_out, err
 
+
+
+def probe_mfma_rate(iters, blocks, out=None, stream=None):
+    """Launch the matrix-core rate probe (blocks * 4 * iters * 8 * 32768 bf16 flops) on the
+    stream; returns the output buffer.  Time it with events on that stream."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    _need(out, "out")
+    _check(lib().jt_probe_mfma_rate(int(iters), int(blocks), _ptr(out), _stream(stream)),
+           "jt_probe_mfma_rate")
+    return out

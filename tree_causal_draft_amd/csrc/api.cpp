@@ -238,7 +238,11 @@ jt_status jt_verify_sampled(const void *target_logits, int64_t row_stride, int32
     jt_status st = verify_shape(S, B, V, N, dtype);
     if (st != JT_OK)
         return st;
-    if (row_stride < V || !(temperature > 0.f) || !(temperature < INFINITY))
+    // the draw weighs logits by 2^((x - max) * log2(e) / T): a temperature so small that
+    // log2(e) / T overflows fp32 (below about 4.2e-39) would turn the weight at the row
+    // maximum into 0 * inf = NaN, so it is refused like T <= 0
+    if (row_stride < V || !(temperature > 0.f) || !(temperature < INFINITY) ||
+        !(1.4426950408889634f / temperature < INFINITY))
         return JT_ERR_SHAPE;
     if (S == 0)
         return JT_OK;
@@ -415,6 +419,15 @@ jt_status jt_commit_accepted_kv(const int32_t *accept_len, const int32_t *accept
                             dtype == JT_BF16 ? 2 : 4, k_cache, v_cache, block_table,
                             max_blocks_per_seq, block_size, num_blocks, prefix_len, max_prefix,
                             new_prefix_len, err, as_stream(stream));
+}
+
+jt_status jt_probe_mfma_rate(int32_t iters, int32_t blocks, float *out, void *stream)
+{
+    if (iters < 1 || blocks < 1)
+        return JT_ERR_SHAPE;
+    if (!out)
+        return JT_ERR_NULL;
+    return launch_mfma_rate(iters, blocks, out, as_stream(stream));
 }
 
 } // extern "C"

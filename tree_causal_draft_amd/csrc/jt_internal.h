@@ -231,4 +231,6 @@ size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d,
                       int block_size);
 jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st);
 
+jt_status launch_mfma_rate(int iters, int blocks, float *out, hipStream_t st);
+
 } // namespace jt

@@ -9,3 +9,4 @@
 #include "step.hip"
 #include "tree.hip"
 #include "commit.hip"
+#include "probe.hip"
