@@ -4,21 +4,25 @@
 
 One step = jt_topw_per_depth (draft logits) -> jt_build_tree_mask -> jt_tree_attention
 -> jt_verify_greedy (target logits), all sequences; for bf16 it runs as one
-jt_draft_verify_step call (the same four steps in two launches).  The tree (parent,
-tokens) is an input of the step, built by the seeded workload generator, and is not
-timed.  Inputs are resident in HBM before the timed region; input sets are rotated so
-that one rotation exceeds twice the 256 MB last-level cache (cold-cache figures).
+jt_draft_verify_step call (the same four steps in two to four launches).  The tree
+(parent, tokens) is an input of the step, built by the seeded workload generator, and is
+not timed.  Inputs are resident in HBM before the timed region; step i reads input set
+i mod n, with n sets whose total exceeds twice the 256 MB last-level cache where memory
+allows (cold-cache figures).
 
-The JSON line reports the low-budget workload (B=16) as the headline and the
-high-budget workload (B=256) in "high_budget".  Every figure is timed with HIP events
-on the stream the work runs on, around back-to-back replays of a hipGraph that holds
-one step (or one call of one entry point) per cold input set:
-  value / ms_per_step   whole step (jt_draft_verify_step; the four calls with top-W and
-                        verification on side streams where it does not apply)
-  calls[*].us           each entry point alone (the roofline's per-launch time; "step" is
-                        jt_draft_verify_step)
-"cpu_baseline" times the CPU oracle (single thread) on full steps of the headline
-workload.
+Every figure is timed with HIP events on the stream the work runs on.  A hipGraph holds
+exactly K steps (or K launches of one entry point); after W untimed steps it is replayed
+R times, each replay bracketed by its own event pair, so every timed region is exactly K
+steps.  The reported time per step is the median replay over K; the line also gives the
+mean, p10 and p90 over the replays and the number of steps timed (R * K).
+
+The JSON line reports the low-budget workload (B=16) as the headline; high_budget
+(B=256), tiny, ragged and moe_verify each get an object of their own with the same
+figures: steps/s, each entry point alone (calls[*].us, the roofline's per-launch time;
+"step" is jt_draft_verify_step), the attention roofline (GB/s or TFLOP/s) and the
+oracle timed on this host ("cpu_baseline": the whole step for the light workloads, a
+stated sample scaled to one step for the heavy ones).  "measured_peaks" holds this
+device's copy bandwidth and sustained bf16 matrix-core rate beside the nominal peaks.
 
 Profiling modes (their output feeds the summaries kept under profiles/):
   --calls-only          time each entry point alone, nothing else (for a kernel trace)
@@ -133,23 +137,43 @@ def _capture(fns):
     return g
 
 
-def _time_graph(g, launches_per_replay, total_launches, warmup):
-    """Average time per launch (us): the graph replayed back-to-back on the current stream,
-    bracketed by HIP events on that stream."""
+def _replays(K):
+    """Replays of a K-step graph: enough for a spread, about 200 steps in all."""
+    return max(5, math.ceil(200 / max(1, K)))
+
+
+def _time_graph(g, K, warmup, replays=None):
+    """Times replays of a graph holding K steps (or K launches) back-to-back on the current
+    stream, each replay between its own pair of HIP events on that stream.  Returns the
+    per-step times (us) of the replays."""
     import torch
     cur = torch.cuda.current_stream()
-    for _ in range(max(1, warmup // max(1, launches_per_replay))):
+    for _ in range(max(1, math.ceil(warmup / max(1, K)))):
         g.replay()
     torch.cuda.synchronize()
-    reps = max(1, math.ceil(total_launches / launches_per_replay))
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(cur)
-    for _ in range(reps):
+    R = replays or _replays(K)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(R)]
+    for a, b in ev:
+        a.record(cur)
         g.replay()
-    b.record(cur)
+        b.record(cur)
     torch.cuda.synchronize()
-    return 1e3 * a.elapsed_time(b) / (reps * launches_per_replay), reps * launches_per_replay
+    return [1e3 * a.elapsed_time(b) / K for a, b in ev]
+
+
+def _stats(per_step_us, K):
+    """Median, mean and spread of per-step times from replays of K steps."""
+    x = np.asarray(per_step_us, np.float64)
+    return {"us_median": round(float(np.median(x)), 3), "us_mean": round(float(x.mean()), 3),
+            "us_p10": round(float(np.percentile(x, 10)), 3),
+            "us_p90": round(float(np.percentile(x, 90)), 3), "replays": len(x),
+            "steps_per_replay": K, "steps_timed": len(x) * K}
+
+
+def _k_of(rot, K, fn_name):
+    """K callables, step i on cold input set i mod n."""
+    return [getattr(rot.steps[i % len(rot.steps)], fn_name) for i in range(K)]
 
 
 def time_workload(name, steps, warmup, seed, log=print, calls_only=False):
@@ -162,15 +186,15 @@ def time_workload(name, steps, warmup, seed, log=print, calls_only=False):
     log(f"[bench] {name}: inputs generated in {time.time() - t0:.1f}s")
     st = DeviceStep(w, "cuda:0")
     fp = footprint(st)
-    nsets = max(1, min(64, math.ceil(2 * LLC_BYTES / max(fp, 1))))
+    nsets = max(1, min(64, steps, math.ceil(2 * LLC_BYTES / max(fp, 1))))
     rot = Rotation(st, nsets)
     log(f"[bench] {name}: footprint {fp / 1e6:.1f} MB per set, {nsets} sets rotated")
     cur = torch.cuda.current_stream()
-    eager_us = step_us = serial_us = None
-    graph_ok = None
     if calls_only:
-        return _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us,
-                           serial_us, graph_ok, log)
+        res = _time_calls(name, w, rot, st, steps, warmup, log)
+        res.update(eager_us=None, step_stats=None, serial_us=None, conc_us=None,
+                   fused_us=None, graph_ok=None, step_us=None)
+        return res
 
     # ---- eager reference run (also the graph-vs-eager check)
     for i in range(max(warmup, nsets)):
@@ -184,57 +208,60 @@ def time_workload(name, steps, warmup, seed, log=print, calls_only=False):
     b.record(cur)
     torch.cuda.synchronize()
     eager_us = 1e3 * a.elapsed_time(b) / steps
-    ref = [t.clone() for t in (st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob,
-                               st.attn_out, st.anc)]
 
-    # ---- whole step: one graph holding one step per input set, replayed back-to-back;
-    # once with the four calls on one stream, once with their independence exposed
-    # (top-W and verification on side streams), which is the reported figure
+    def got_bufs():
+        return [st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob, st.attn_out, st.anc]
+    ref = [t.clone() for t in got_bufs()]
+
+    # ---- whole step: one graph holding exactly `steps` steps (step i on cold set i mod n);
+    # the four calls on one stream, the four calls with their independence exposed (top-W
+    # and verification on side streams), and the fused call where it applies (reported)
     def graph_step(fn_name):
-        g = _capture([getattr(s, fn_name) for s in rot.steps])
-        us, n = _time_graph(g, nsets, steps, warmup)
+        g = _capture(_k_of(rot, steps, fn_name))
+        per = _time_graph(g, steps, warmup)
         for t in got_bufs():
             t.zero_()
         g.replay()
         torch.cuda.synchronize()
         ok = all(torch.equal(x, y) for x, y in zip(ref, got_bufs()))
         del g
-        return us, n, ok
+        return per, ok
 
-    def got_bufs():
-        return [st.accept_len, st.bonus, st.accept_path, st.ids, st.logprob, st.attn_out, st.anc]
-
-    serial_us, nsteps, serial_ok = graph_step("run")
-    conc_us, nsteps, conc_ok = graph_step("run_concurrent")
-    fused_us, fused_ok = None, True
+    serial, serial_ok = graph_step("run")
+    conc, conc_ok = graph_step("run_concurrent")
+    fused, fused_ok = None, True
     if hasattr(st, "step_ws"):
-        fused_us, nsteps, fused_ok = graph_step("run_fused")
+        fused, fused_ok = graph_step("run_fused")
     graph_ok = serial_ok and conc_ok and fused_ok
-    step_us = fused_us if fused_us is not None else conc_us
-    log(f"[bench] {name}: eager {eager_us:.1f} us/step, graph one-stream {serial_us:.1f} us/step, "
-        f"graph concurrent {conc_us:.1f} us/step, fused {fused_us} us/step ({nsteps} steps), "
-        f"replay == eager: {graph_ok}")
+    step_per = fused if fused is not None else conc
+    med = lambda x: None if x is None else float(np.median(x))
+    log(f"[bench] {name}: eager {eager_us:.2f} us/step, graph one-stream {med(serial):.2f}, "
+        f"concurrent {med(conc):.2f}, fused {med(fused)} us/step (median of replays of "
+        f"{steps} steps), replay == eager: {graph_ok}")
 
-    res = _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us,
-                      serial_us, graph_ok, log)
-    res["conc_us"], res["fused_us"] = conc_us, fused_us
+    res = _time_calls(name, w, rot, st, steps, warmup, log)
+    res.update(eager_us=eager_us, step_stats=_stats(step_per, steps), serial_us=med(serial),
+               conc_us=med(conc), fused_us=med(fused), graph_ok=graph_ok)
+    res["step_us"] = res["step_stats"]["us_median"]
     return res
 
 
-def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, serial_us,
-                graph_ok, log):
+def _time_calls(name, w, rot, st, steps, warmup, log):
     import torch
-    # ---- each entry point alone: one graph of nsets launches (one per cold input set)
-    per_call_us = {}
+    # ---- each entry point alone: one graph of exactly `steps` launches (launch i on cold
+    # input set i mod n)
+    per_call_us, call_stats = {}, {}
     calls_here = CALLS + (("step",) if hasattr(st, "step_ws") else ()) + \
         (("tree",) if hasattr(st, "tree_parent") else ()) + \
         (("commit",) if hasattr(st, "commit_k") else ()) + \
         (("sampled",) if hasattr(st, "smp_ws") else ())
     st.run()  # the tree call reads the top-W lists, the commit the accepted paths
     for c in calls_here:
-        g = _capture([getattr(s, "run_fused" if c == "step" else c) for s in rot.steps])
-        per_call_us[c], _ = _time_graph(g, nsets, steps, warmup)
+        g = _capture(_k_of(rot, steps, "run_fused" if c == "step" else c))
+        per = _time_graph(g, steps, warmup)
         del g
+        call_stats[c] = _stats(per, steps)
+        per_call_us[c] = call_stats[c]["us_median"]
     log(f"[bench] {name}: per call " + " ".join(f"{c}={per_call_us[c]:.2f}us" for c in calls_here))
 
     bytes_, flops = algorithmic(w)
@@ -246,60 +273,100 @@ def _time_calls(name, w, rot, st, nsets, steps, warmup, fp, eager_us, step_us, s
     calls = {}
     for c in calls_here:
         us = per_call_us[c]
-        calls[c] = {"us": round(us, 3), "bytes": int(bytes_[c]),
+        calls[c] = {"us": round(us, 3), "us_p10": call_stats[c]["us_p10"],
+                    "us_p90": call_stats[c]["us_p90"], "bytes": int(bytes_[c]),
                     "GBps": round(bytes_[c] / (us * 1e-6) / 1e9, 1)}
     att_us = per_call_us["attention"]
     calls["attention"]["TFLOPs"] = round(flops / (att_us * 1e-6) / 1e12, 2)
     calls["attention"]["flops"] = int(flops)
-    res = dict(workload=name, w=w, eager_us=eager_us, step_us=step_us, serial_us=serial_us,
-               graph_ok=graph_ok,
-               calls=calls, nsets=nsets, flops=flops, bytes=bytes_, per_call_us=per_call_us,
-               footprint=fp)
+    res = dict(workload=name, w=w, calls=calls, nsets=len(rot.steps), flops=flops,
+               bytes=bytes_, per_call_us=per_call_us, footprint=footprint(st))
     del rot, st
     torch.cuda.empty_cache()
     return res
 
 
-def roofline(res, call):
+def roofline(res, call, peaks=None):
     """Roofline of one entry point: the binding resource is the one whose floor (bytes at
-    the HBM peak, or flops at the bf16 MFMA peak) is longer."""
+    the HBM peak, or flops at the bf16 MFMA peak) is longer.  `frac_measured` relates the
+    same rate to this device's measured ceiling (copy bandwidth or matrix-core loop)."""
     w = res["w"]
     us = res["per_call_us"][call]
     byt = res["bytes"][call]
+    peaks = peaks or {}
     if call in ("attention", "step"):
         ai = res["flops"] / byt
         if ai > (MFMA_BF16_PEAK_TFS * 1e12) / (HBM_PEAK_GBS * 1e9) and w.cfg.dtype == "bf16":
             ach = res["flops"] / (us * 1e-6) / 1e12
+            m = peaks.get("mfma_bf16_TFLOPs")
             return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                    "frac_measured": round(ach / m, 4) if m else None,
                     "kernel": call, "kernels": KERNELS[call], "per_launch_us": round(us, 2)}
     ach = byt / (us * 1e-6) / 1e9
+    m = peaks.get("copy_GBps")
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": call,
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac_measured": round(ach / m, 4) if m else None, "kernel": call,
             "kernels": KERNELS[call], "per_launch_us": round(us, 2)}
 
 
-def cpu_baseline(name, seed, budget_s=20.0, log=print):
-    """The CPU oracle, single-threaded, on full steps of the same workload."""
+def cpu_baseline(name, seed, budget_s=20.0, log=print, w=None):
+    """The CPU oracle, single-threaded, timed on the same workload's inputs, stage by stage.
+
+    Light workloads run whole steps, repeated until `budget_s` is spent (at most 50).  For
+    the heavy ones a step is timed on a stated sample and scaled: top-W on the first rows
+    (scaled by the row count), the mask whole, attention on every k-th tree node of every
+    sequence and head (scaled by the visible keys, i.e. the flops), and verification whole.
+    """
     import oracle
     from tree_causal_draft_amd import workload as wl
-    w = wl.make(name, seed)
+    w = wl.make(name, seed) if w is None else w
     c = w.cfg
-    times = []
+    rows = c.S * c.N
+    # samples sized from the oracle's measured speed here (~35 ms per 151,936-logit row,
+    # ~1 GFLOP/s of attention) so that one sampled step costs a few seconds
+    rows_s = min(rows, max(1, int(64 * 151936 / max(c.V, 1))))
+    P = w.prefix_len.astype(np.int64)
+    vis = P[:, None] + w.depth.astype(np.int64) + 1              # keys visible per node
+    flops = 4.0 * c.Hq * c.d * vis.sum()
+    k = max(1, math.ceil(flops / 4e9))
+    nodes = np.arange(0, c.B, k)
+    sel = np.stack(np.meshgrid(np.arange(c.S), nodes, np.arange(c.Hq), indexing="ij"),
+                   -1).reshape(-1, 3).astype(np.int32)
+    flops_s = 4.0 * c.d * vis[:, nodes].sum() * c.Hq
+    draft = w.draft_logits[:rows_s]
+    kw = dict(block_table=w.block_table, block_size=c.block_size, num_blocks=w.num_blocks,
+              max_prefix=w.max_prefix)
+    stages = {"topw": [], "mask": [], "attention": [], "verify": []}
     t_all = time.perf_counter()
-    while not times or (time.perf_counter() - t_all < budget_s and len(times) < 50):
+    while not stages["verify"] or (time.perf_counter() - t_all < budget_s
+                                   and len(stages["verify"]) < 50):
         t = time.perf_counter()
-        oracle.topw(w.draft_logits, c.W)
+        oracle.topw(draft, c.W)
+        t1 = time.perf_counter()
         oracle.build_mask(w.parent)
+        t2 = time.perf_counter()
         oracle.tree_attention(w.q, w.k_tree, w.v_tree, w.k_prefix, w.v_prefix, w.prefix_len,
-                              w.parent, block_table=w.block_table, block_size=c.block_size,
-                              num_blocks=w.num_blocks, max_prefix=w.max_prefix)
+                              w.parent, sel=None if k == 1 else sel, **kw)
+        t3 = time.perf_counter()
         oracle.verify_greedy(w.target_logits, w.parent, w.tokens, c.N)
-        times.append(time.perf_counter() - t)
-    sec = float(np.mean(times))
-    log(f"[bench] cpu oracle {name}: {sec:.2f} s/step over {len(times)} steps")
-    return {"value": round(1.0 / sec, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} full steps of {name} (seed {seed}), single thread",
+        t4 = time.perf_counter()
+        for st_, dt in zip(stages, (t1 - t, t2 - t1, t3 - t2, t4 - t3)):
+            stages[st_].append(dt)
+    scale = {"topw": rows / rows_s, "mask": 1.0, "attention": flops / flops_s, "verify": 1.0}
+    per = {st_: float(np.mean(v)) * scale[st_] for st_, v in stages.items()}
+    sec = sum(per.values())
+    n = len(stages["verify"])
+    whole = rows_s == rows and k == 1
+    sample = (f"{n} whole steps of {name} (seed {seed})" if whole else
+              f"{n} sampled step(s) of {name} (seed {seed}): top-W on {rows_s} of {rows} rows "
+              f"(x{rows / rows_s:.2f}), mask whole, attention on nodes v % {k} == 0 of every "
+              f"sequence and head (x{flops / flops_s:.2f} by visible keys), verify whole")
+    log(f"[bench] cpu oracle {name}: {sec:.3f} s/step ({sample})")
+    return {"value": round(1.0 / sec, 5), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": sample + ", single thread",
+            "stage_seconds": {k2: round(v, 4) for k2, v in per.items()},
             "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
@@ -347,8 +414,8 @@ def traffic(workload, call):
     return int(rec["bytes_per_launch"])
 
 
-def roofline_line(res, call):
-    r = roofline(res, call)
+def roofline_line(res, call, peaks=None):
+    r = roofline(res, call, peaks)
     r["traffic"] = traffic(res["workload"], call)
     return r
 
@@ -477,8 +544,9 @@ def attention_only(name, seed, reps=20, log=print):
              for n in ("q", "k_tree", "v_tree", "k_prefix", "v_prefix"))
     nsets = max(1, min(32, math.ceil(2 * LLC_BYTES / fp)))
     rot = Rotation(st, nsets)
-    g = _capture([s.attention for s in rot.steps])
-    us, _ = _time_graph(g, nsets, reps * nsets, nsets)
+    K = reps * nsets
+    g = _capture(_k_of(rot, K, "attention"))
+    us = float(np.median(_time_graph(g, K, nsets)))
     b, fl = algorithmic(w)
     tf = fl / us / 1e6
     log(f"[bench] {name}: attention {us:.2f} us/call over {nsets} cold sets")
@@ -507,13 +575,36 @@ def copy_bandwidth(nbytes=1 << 30, reps=20):
     return round(2 * nbytes / us / 1e3, 1)
 
 
+def mfma_rate(iters=4000, blocks=1024, reps=10, warmup=10):
+    """Sustained bf16 matrix-core rate (TFLOP/s) of the library's probe kernel: 4 waves per
+    SIMD, each issuing independent v_mfma_f32_32x32x16_bf16; the best of `reps` runs after
+    `warmup` untimed ones (the clock settles under load)."""
+    import torch
+    import tree_causal_draft_amd as jt
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    flops = blocks * 4 * iters * 8 * 32768.0
+    for _ in range(warmup):
+        jt.probe_mfma_rate(iters, blocks, out)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        jt.probe_mfma_rate(iters, blocks, out)
+        t1.record()
+        t1.synchronize()
+        best = max(best, flops / (t0.elapsed_time(t1) * 1e-3) / 1e12)
+    return round(best, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="low_budget")
-    ap.add_argument("--secondary", default="high_budget", help="'' to skip")
+    ap.add_argument("--secondary", default="high_budget,tiny,ragged,moe_verify",
+                    help="comma-separated workloads reported beside the headline ('' for none)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calls-only", action="store_true")
@@ -547,13 +638,20 @@ def main():
             print(json.dumps(attention_only(n, seed_of(n), log=log)), flush=True)
         return
 
-    names = [args.workload] + [n for n in args.secondary.split(",") if n]
+    names = [args.workload] + [n for n in args.secondary.split(",") if n and n != args.workload]
     results = [time_workload(n, args.steps, args.warmup, seed_of(n), log=log,
                              calls_only=args.calls_only) for n in names]
-    cpu = None
+    peaks = {}
+    if not args.calls_only:
+        peaks = {"copy_GBps": copy_bandwidth(), "mfma_bf16_TFLOPs": mfma_rate(),
+                 "nominal_hbm_GBps": HBM_PEAK_GBS, "nominal_mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFS}
+        log(f"[bench] measured peaks: copy {peaks['copy_GBps']} GB/s, bf16 matrix cores "
+            f"{peaks['mfma_bf16_TFLOPs']} TFLOP/s")
+    cpu = {}
     if not args.no_cpu and not args.calls_only:
-        cpu = cpu_baseline(args.workload, seed_of(args.workload), args.cpu_seconds, log=log)
-    copy_gbps = None if args.calls_only else copy_bandwidth()
+        for i, (n, r) in enumerate(zip(names, results)):
+            budget = args.cpu_seconds if i == 0 else args.cpu_seconds / 2
+            cpu[n] = cpu_baseline(n, seed_of(n), budget, log=log, w=r["w"])
 
     def summary(r):
         c = r["w"].cfg
@@ -568,15 +666,17 @@ def main():
             return "step"
         return max(CALLS, key=lambda k: r["per_call_us"][k])
 
+    def timing(r):
+        if r["w"].cfg.dtype != "bf16":
+            return ("hipGraph of K steps (step i on cold input set i mod n), the four calls "
+                    "with top-W and verification on side streams; median of the replays")
+        return ("hipGraph of K jt_draft_verify_step calls (step i on cold input set i mod n; "
+                "two to four kernel launches each); median of the replays")
+
     prim = results[0]
     us = prim["step_us"]
     dom = dominant(prim)
     c = prim["w"].cfg
-    fused = prim.get("fused_us") is not None
-    timing = ("hipGraph replay of one jt_draft_verify_step (two kernel launches; three when "
-              "attention runs 8-wave groups) per cold input set"
-              if fused else "hipGraph replay of one step per cold input set; top-W and "
-              "verification on side streams")
     line = {
         "metric": "draft-verify steps/s + tree-attn HBM GB/s / MFMA % at B=16,256 (1xMI355X)",
         "value": rate(us),
@@ -590,30 +690,35 @@ def main():
         "vs_baseline": None,
         "dtype": c.dtype,
         "data": "synthetic (seeded; tree prebuilt, not timed)",
-        "config": {"workload": summary(prim), "timing": timing, "cold_sets": prim["nsets"]},
+        "config": {"workload": summary(prim), "timing": timing(prim), "cold_sets": prim["nsets"]},
+        "step_timing": prim["step_stats"],
         "eager_steps_per_s": rate(prim["eager_us"]),
         "one_stream_graph_steps_per_s": rate(prim["serial_us"]),
         "four_calls_concurrent_graph_steps_per_s": rate(prim.get("conc_us")),
         "graph_matches_eager": prim["graph_ok"],
         "calls": prim["calls"],
-        "roofline": roofline_line(prim, dom),
-        "attention_roofline": roofline_line(prim, "attention"),
-        "cpu_baseline": cpu,
-        "copy_bandwidth_GBps": copy_gbps,
+        "roofline": roofline_line(prim, dom, peaks),
+        "attention_roofline": roofline_line(prim, "attention", peaks),
+        "cpu_baseline": cpu.get(prim["workload"]),
+        "measured_peaks": peaks or None,
     }
     if args.calls_only:
         line["mode"] = "calls-only (entry points timed alone; no whole-step figure)"
     for r in results[1:]:
         line[r["workload"]] = {
             "workload": summary(r),
+            "timing": timing(r),
+            "cold_sets": r["nsets"],
             "steps_per_s": rate(r["step_us"]),
+            "step_timing": r["step_stats"],
             "eager_steps_per_s": rate(r["eager_us"]),
             "one_stream_graph_steps_per_s": rate(r["serial_us"]),
             "four_calls_concurrent_graph_steps_per_s": rate(r.get("conc_us")),
             "graph_matches_eager": r["graph_ok"],
             "calls": r["calls"],
-            "attention_roofline": roofline_line(r, "attention"),
-            "roofline": roofline_line(r, dominant(r)),
+            "attention_roofline": roofline_line(r, "attention", peaks),
+            "roofline": roofline_line(r, dominant(r), peaks),
+            "cpu_baseline": cpu.get(r["workload"]),
         }
     print(json.dumps(line), flush=True)
 
