@@ -72,7 +72,8 @@ def assert_lp_close(got, ref, what=""):
     # an infinite reference is matched only by the same infinity (|g - r| <= atol + rtol*inf
     # would accept any finite value); a finite one within the tolerance (an infinite g fails)
     inf = np.isinf(r)
-    bad = np.where(inf, g != r, ~(np.abs(g - r) <= LP_ATOL + LP_RTOL * np.abs(r)))
+    with np.errstate(invalid="ignore"):  # inf - inf where both are infinite: decided by g != r
+        bad = np.where(inf, g != r, ~(np.abs(g - r) <= LP_ATOL + LP_RTOL * np.abs(r)))
     assert not bad.any(), (f"{what}: {int(bad.sum())} entries off, "
                            f"max err {np.nanmax(np.abs(g - r)) if g.size else 0:.3e}")
 
@@ -84,8 +85,9 @@ def assert_lse_close(got, ref, dtype, what=""):
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, what
     inf = np.isinf(ref)
-    bad = np.where(inf, got != ref,
-                   ~(np.abs(got - ref) <= LSE_ATOL[dtype] + LSE_RTOL[dtype] * np.abs(ref)))
+    with np.errstate(invalid="ignore"):
+        bad = np.where(inf, got != ref,
+                       ~(np.abs(got - ref) <= LSE_ATOL[dtype] + LSE_RTOL[dtype] * np.abs(ref)))
     fin = ~inf
     err = np.abs(got[fin] - ref[fin]).max() if fin.any() else 0.0
     assert not bad.any(), f"{what}: {int(bad.sum())} LSE entries off, max err {err:.3e}"
