@@ -50,7 +50,9 @@ typedef enum {
     JT_ERR_DTYPE = 3,     /* unsupported element type for this call */
     JT_ERR_WORKSPACE = 4, /* workspace smaller than the *_workspace_size() answer */
     JT_ERR_LAUNCH = 5,    /* the HIP runtime rejected a kernel launch */
-    JT_ERR_ALIGN = 6      /* a pointer or stride breaks the stated alignment */
+    JT_ERR_ALIGN = 6,     /* a pointer or stride breaks the stated alignment */
+    JT_ERR_SCRATCH = 7    /* the shape needs more scratch than the static buffer of
+                             jt_draft_verify_step_noalloc holds */
 } jt_status;
 
 typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
@@ -241,6 +243,36 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
                                int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
                                int32_t *err, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * jt_draft_verify_step without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, outputs and results are those of jt_draft_verify_step (bit for
+ * bit the same); the scratch that call takes as `workspace` is instead a static device
+ * array of JT_STATIC_SCRATCH_BYTES (48 MiB) inside the library, one per GPU the call runs
+ * on, held until the process ends.  The call allocates nothing (the first call on a
+ * device only looks up that device's address of the array).  Every call on one GPU uses
+ * the same array, which keeps the last call's contents (the step needs none of them):
+ * calls that overlap in time on one GPU race and must be serialised by the caller.
+ * Returns JT_ERR_SCRATCH when jt_step_workspace_size() for the shape exceeds
+ * JT_STATIC_SCRATCH_BYTES (use jt_draft_verify_step with a workspace then).
+ */
+#define JT_STATIC_SCRATCH_BYTES (48u << 20)
+jt_status jt_draft_verify_step_noalloc(const void *draft_logits, int64_t draft_row_stride,
+                                       const void *target_logits, int64_t target_row_stride,
+                                       int32_t V, int32_t W, const int32_t *parent,
+                                       const int32_t *tokens, int32_t S, int32_t B, int32_t N,
+                                       const void *q, const void *k_tree, const void *v_tree,
+                                       const void *k_prefix, const void *v_prefix,
+                                       const int32_t *block_table, int32_t max_blocks_per_seq,
+                                       int32_t block_size, int32_t num_blocks,
+                                       const int32_t *prefix_len, int32_t max_prefix, int32_t Hq,
+                                       int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
+                                       int32_t *ids, float *logprob, float *row_lse,
+                                       float *row_entropy, uint64_t *anc, int32_t *depth,
+                                       void *out, float *lse, int32_t *accept_len,
+                                       int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                                       int32_t *err, void *stream);
 
 /*
  * Stochastic tree verification at temperature T > 0.  With a fixed draft every proposal

@@ -114,3 +114,23 @@ def test_workspace_queries_are_pure():
         table + slots * 8 + slots * d * 2
     assert jt.tree_attention_workspace_size(1, 16, 32, 8, 128, 1024, 1) > 0
     assert jt.tree_attention_workspace_size(1, 16, 4, 2, 64, 64, 0) == 0
+
+
+def test_noalloc_step_rejects_shapes_beyond_its_scratch():
+    """jt_draft_verify_step_noalloc refuses, on the host and before any device work, a shape
+    whose step workspace exceeds the static scratch (JT_ERR_SCRATCH); the pointers below are
+    never dereferenced."""
+    L = jt.lib()
+    assert L.jt_status_string(7).startswith(b"the shape needs more scratch")
+    fake = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never touched
+
+    def call(S, P, V=151936):
+        return L.jt_draft_verify_step_noalloc(
+            fake, V, fake, V, V, 8, fake, fake, S, 64, 8, fake, fake, fake, fake, fake, None,
+            0, 16, 0, fake, P, 32, 4, 128, ctypes.c_float(0.0), 1, fake, fake, fake, None, fake,
+            fake, fake, fake, fake, fake, fake, fake, fake, None)
+    big = jt.step_workspace_size(64, 64, 8, 8, 151936, 32, 4, 128, 4096, 1)
+    assert big > jt.STATIC_SCRATCH_BYTES
+    assert call(64, 4096) == 7
+    assert call(0, 4096) == 0          # nothing to do
+    assert call(64, 4096, V=0) == 2    # shape errors come first

@@ -19,13 +19,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libjt.so")
 
 JT_F32, JT_BF16 = 0, 1
+JT_ERR_SCRATCH = 7
+STATIC_SCRATCH_BYTES = 48 << 20  # JT_STATIC_SCRATCH_BYTES
 DEV_BAD_PARENT, DEV_DEPTH_GT_N, DEV_BAD_BLOCK, DEV_NAN, DEV_BAD_PREFIX = 1, 2, 4, 8, 16
 EXPORTS = ("jt_abi_version", "jt_status_string", "jt_build_tree_mask",
            "jt_tree_attention_workspace_size", "jt_tree_attention", "jt_topw_workspace_size",
            "jt_topw_per_depth", "jt_verify_workspace_size", "jt_verify_greedy",
            "jt_step_workspace_size", "jt_draft_verify_step", "jt_build_tree_best_first",
            "jt_commit_accepted_kv", "jt_verify_sampled_workspace_size", "jt_verify_sampled",
-           "jt_probe_mfma_rate")
+           "jt_probe_mfma_rate", "jt_draft_verify_step_noalloc")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -69,6 +71,7 @@ def lib() -> ctypes.CDLL:
             [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _i32, _i32, _i32] + [_vp] * 6 +
             [_i32, _i32, _i32, _vp] + [_i32] * 4 + [ctypes.c_float, ctypes.c_int] + [_vp] * 14 +
             [_sz, _vp])
+        L.jt_draft_verify_step_noalloc.argtypes = L.jt_draft_verify_step.argtypes[:-3] + [_vp]
         L.jt_build_tree_best_first.argtypes = ([_vp] * 3 + [ctypes.c_float] * 2 + [_vp] +
                                                [_i32] * 4 + [_vp] * 5)
         L.jt_commit_accepted_kv.argtypes = ([_vp, _vp, _i32, _vp, _vp] + [_i32] * 4 +
@@ -81,7 +84,8 @@ def lib() -> ctypes.CDLL:
         L.jt_probe_mfma_rate.argtypes = [_i32, _i32, _vp, _vp]
         for fn in ("jt_build_tree_mask", "jt_tree_attention", "jt_topw_per_depth",
                    "jt_verify_greedy", "jt_draft_verify_step", "jt_build_tree_best_first",
-                   "jt_commit_accepted_kv", "jt_verify_sampled", "jt_probe_mfma_rate"):
+                   "jt_commit_accepted_kv", "jt_verify_sampled", "jt_probe_mfma_rate",
+                   "jt_draft_verify_step_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -245,15 +249,12 @@ def step_workspace_size(S, B, N, W, V, Hq, Hkv, d, max_prefix, dtype, block_size
                                             dtype))
 
 
-def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tree, v_tree,
-                      k_prefix, v_prefix, prefix_len, *, V=None, block_table=None, block_size=16,
-                      num_blocks=None, max_prefix=None, scale=0.0, out=None, lse=None, ids=None,
-                      logprob=None, row_lse=None, anc=None, depth=None, accept_len=None,
-                      accept_path=None, bonus=None, argmax_out=None, err=None, workspace=None,
-                      row_entropy=None, stream=None):
-    """The four steps in one call (two launches).  draft_logits [S*N, stride] and
-    target_logits [S*B, stride] bf16; the rest as for the separate calls.  Returns a dict
-    of every output."""
+def _step_call(draft_logits, target_logits, parent, tokens, N, W, q, k_tree, v_tree,
+               k_prefix, v_prefix, prefix_len, V, block_table, block_size, num_blocks,
+               max_prefix, scale, out, lse, ids, logprob, row_lse, anc, depth, accept_len,
+               accept_path, bonus, argmax_out, err, row_entropy):
+    """Argument checks and output allocation shared by the two forms of the fused step;
+    returns (C arguments up to err, outputs, workspace size)."""
     for t, n in ((draft_logits, "draft_logits"), (target_logits, "target_logits"),
                  (parent, "parent"), (tokens, "tokens"), (q, "q"), (k_tree, "k_tree"),
                  (v_tree, "v_tree"), (k_prefix, "k_prefix"), (v_prefix, "v_prefix"),
@@ -289,18 +290,55 @@ def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tr
     err = e(S, torch.int32) if err is None else err
     need = step_workspace_size(S, B, N, W, V, Hq, Hkv, d, Pmax, dt,
                                0 if block_table is None else block_size)
-    ws, wsb = _workspace(need, dev, workspace)
-    _check(lib().jt_draft_verify_step(
-        _ptr(draft_logits), dstride, _ptr(target_logits), tstride, V, W, _ptr(parent),
-        _ptr(tokens), S, B, N, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
-        _ptr(v_prefix), _ptr(block_table), maxblk, block_size, nblk, _ptr(prefix_len), Pmax, Hq,
-        Hkv, d, float(scale), dt, _ptr(ids), _ptr(logprob), _ptr(row_lse), _ptr(row_entropy),
-        _ptr(anc),
-        _ptr(depth), _ptr(out), _ptr(lse), _ptr(accept_len), _ptr(accept_path), _ptr(bonus),
-        _ptr(argmax_out), _ptr(err), _ptr(ws), wsb, _stream(stream)), "jt_draft_verify_step")
-    return dict(ids=ids, logprob=logprob, row_lse=row_lse, row_entropy=row_entropy, anc=anc,
+    args = (_ptr(draft_logits), dstride, _ptr(target_logits), tstride, V, W, _ptr(parent),
+            _ptr(tokens), S, B, N, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_prefix),
+            _ptr(v_prefix), _ptr(block_table), maxblk, block_size, nblk, _ptr(prefix_len), Pmax,
+            Hq, Hkv, d, float(scale), dt, _ptr(ids), _ptr(logprob), _ptr(row_lse),
+            _ptr(row_entropy), _ptr(anc), _ptr(depth), _ptr(out), _ptr(lse), _ptr(accept_len),
+            _ptr(accept_path), _ptr(bonus), _ptr(argmax_out), _ptr(err))
+    outs = dict(ids=ids, logprob=logprob, row_lse=row_lse, row_entropy=row_entropy, anc=anc,
                 depth=depth, out=out, lse=lse, accept_len=accept_len, accept_path=accept_path,
                 bonus=bonus, argmax=argmax_out, err=err)
+    return args, outs, need
+
+
+def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tree, v_tree,
+                      k_prefix, v_prefix, prefix_len, *, V=None, block_table=None, block_size=16,
+                      num_blocks=None, max_prefix=None, scale=0.0, out=None, lse=None, ids=None,
+                      logprob=None, row_lse=None, anc=None, depth=None, accept_len=None,
+                      accept_path=None, bonus=None, argmax_out=None, err=None, workspace=None,
+                      row_entropy=None, stream=None):
+    """The four steps in one call (two to four launches).  draft_logits [S*N, stride] and
+    target_logits [S*B, stride] bf16; the rest as for the separate calls.  Returns a dict
+    of every output."""
+    args, outs, need = _step_call(draft_logits, target_logits, parent, tokens, N, W, q, k_tree,
+                                  v_tree, k_prefix, v_prefix, prefix_len, V, block_table,
+                                  block_size, num_blocks, max_prefix, scale, out, lse, ids,
+                                  logprob, row_lse, anc, depth, accept_len, accept_path, bonus,
+                                  argmax_out, err, row_entropy)
+    ws, wsb = _workspace(need, q.device, workspace)
+    _check(lib().jt_draft_verify_step(*args, _ptr(ws), wsb, _stream(stream)),
+           "jt_draft_verify_step")
+    return outs
+
+
+def draft_verify_step_noalloc(draft_logits, target_logits, parent, tokens, N, W, q, k_tree,
+                              v_tree, k_prefix, v_prefix, prefix_len, *, V=None,
+                              block_table=None, block_size=16, num_blocks=None, max_prefix=None,
+                              scale=0.0, out=None, lse=None, ids=None, logprob=None,
+                              row_lse=None, anc=None, depth=None, accept_len=None,
+                              accept_path=None, bonus=None, argmax_out=None, err=None,
+                              row_entropy=None, stream=None):
+    """jt_draft_verify_step_noalloc: the fused step with the library's static device scratch
+    (no workspace).  Pass every output to keep the call free of allocations."""
+    args, outs, _ = _step_call(draft_logits, target_logits, parent, tokens, N, W, q, k_tree,
+                               v_tree, k_prefix, v_prefix, prefix_len, V, block_table,
+                               block_size, num_blocks, max_prefix, scale, out, lse, ids, logprob,
+                               row_lse, anc, depth, accept_len, accept_path, bonus, argmax_out,
+                               err, row_entropy)
+    _check(lib().jt_draft_verify_step_noalloc(*args, _stream(stream)),
+           "jt_draft_verify_step_noalloc")
+    return outs
 
 
 def build_tree_best_first(ids, logprob, N, B, *, entropy=None, w_lp=1.0, w_ent=0.0,
@@ -414,5 +452,5 @@ def probe_mfma_rate(iters, blocks, out=None, stream=None):
         out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     _need(out, "out")
     _check(lib().jt_probe_mfma_rate(int(iters), int(blocks), _ptr(out), _stream(stream)),
-           "jt_probe_mfma_rate")
+           "jt_probe_mfma_rate", "jt_draft_verify_step_noalloc")
     return out

@@ -6,6 +6,8 @@
 
 using namespace jt;
 
+static_assert(kStaticScratchBytes == JT_STATIC_SCRATCH_BYTES, "static scratch size");
+
 namespace {
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
@@ -38,6 +40,9 @@ const char *jt_status_string(int status)
     case JT_ERR_WORKSPACE: return "workspace too small";
     case JT_ERR_LAUNCH: return "kernel launch failed";
     case JT_ERR_ALIGN: return "pointer or stride misaligned";
+    case JT_ERR_SCRATCH:
+        return "the shape needs more scratch than the library's static buffer holds "
+               "(use the call that takes a workspace)";
     default: return "unknown status";
     }
 }
@@ -270,7 +275,9 @@ size_t jt_step_workspace_size(int32_t S, int32_t B, int32_t N, int32_t W, int32_
     return step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_size > 0 ? block_size : 0);
 }
 
-jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_stride,
+} // extern "C"
+
+static jt_status step_setup(const void *draft_logits, int64_t draft_row_stride,
                                const void *target_logits, int64_t target_row_stride, int32_t V,
                                int32_t W, const int32_t *parent, const int32_t *tokens,
                                int32_t S, int32_t B, int32_t N, const void *q,
@@ -283,8 +290,7 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
                                float *row_entropy, uint64_t *anc,
                                int32_t *depth, void *out, float *lse, int32_t *accept_len,
                                int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
-                               int32_t *err, void *workspace, size_t workspace_bytes,
-                               void *stream)
+                               int32_t *err, StepLaunch &in, size_t &need)
 {
     if (dtype != JT_BF16)
         return JT_ERR_DTYPE;
@@ -299,8 +305,11 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
         return st;
     if (draft_row_stride < V || target_row_stride < V)
         return JT_ERR_SHAPE;
-    if (S == 0)
+    if (S == 0) {
+        in.attn.S = 0;
+        need = 0;
         return JT_OK;
+    }
     if (!target_logits || !parent || !tokens || !q || !k_tree || !v_tree || !prefix_len ||
         !anc || !depth || !out || !accept_len || !accept_path || !bonus)
         return JT_ERR_NULL;
@@ -319,13 +328,7 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
     if (!aligned16(target_logits) || target_row_stride % 8 != 0 ||
         (N > 0 && (!aligned16(draft_logits) || draft_row_stride % 8 != 0)))
         return JT_ERR_ALIGN;
-    const size_t need = step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix,
-                                       block_table ? block_size : 0);
-    if (!workspace || workspace_bytes < need)
-        return JT_ERR_WORKSPACE;
-    if (!aligned16(workspace))
-        return JT_ERR_ALIGN;
-    StepLaunch in;
+    need = step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_table ? block_size : 0);
     AttnArgs &a = in.attn;
     a.q = q;
     a.k_tree = k_tree;
@@ -372,7 +375,75 @@ jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_strid
     in.bonus = bonus;
     in.argmax_out = argmax_out;
     in.err = err;
+    return JT_OK;
+}
+
+extern "C" {
+
+jt_status jt_draft_verify_step(const void *draft_logits, int64_t draft_row_stride,
+                               const void *target_logits, int64_t target_row_stride, int32_t V,
+                               int32_t W, const int32_t *parent, const int32_t *tokens,
+                               int32_t S, int32_t B, int32_t N, const void *q,
+                               const void *k_tree, const void *v_tree, const void *k_prefix,
+                               const void *v_prefix, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               int32_t num_blocks, const int32_t *prefix_len, int32_t max_prefix,
+                               int32_t Hq, int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
+                               int32_t *ids, float *logprob, float *row_lse,
+                               float *row_entropy, uint64_t *anc,
+                               int32_t *depth, void *out, float *lse, int32_t *accept_len,
+                               int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                               int32_t *err, void *workspace, size_t workspace_bytes,
+                               void *stream)
+{
+    StepLaunch in;
+    size_t need = 0;
+    const jt_status st = step_setup(draft_logits, draft_row_stride, target_logits,
+                                    target_row_stride, V, W, parent, tokens, S, B, N, q, k_tree,
+                                    v_tree, k_prefix, v_prefix, block_table, max_blocks_per_seq,
+                                    block_size, num_blocks, prefix_len, max_prefix, Hq, Hkv, d,
+                                    scale, dtype, ids, logprob, row_lse, row_entropy, anc, depth,
+                                    out, lse, accept_len, accept_path, bonus, argmax_out, err, in,
+                                    need);
+    if (st != JT_OK || S == 0)
+        return st;
+    if (!workspace || workspace_bytes < need)
+        return JT_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return JT_ERR_ALIGN;
     return launch_step(in, workspace, as_stream(stream));
+}
+
+jt_status jt_draft_verify_step_noalloc(const void *draft_logits, int64_t draft_row_stride,
+                               const void *target_logits, int64_t target_row_stride, int32_t V,
+                               int32_t W, const int32_t *parent, const int32_t *tokens,
+                               int32_t S, int32_t B, int32_t N, const void *q,
+                               const void *k_tree, const void *v_tree, const void *k_prefix,
+                               const void *v_prefix, const int32_t *block_table,
+                               int32_t max_blocks_per_seq, int32_t block_size,
+                               int32_t num_blocks, const int32_t *prefix_len, int32_t max_prefix,
+                               int32_t Hq, int32_t Hkv, int32_t d, float scale, jt_dtype dtype,
+                               int32_t *ids, float *logprob, float *row_lse,
+                               float *row_entropy, uint64_t *anc,
+                               int32_t *depth, void *out, float *lse, int32_t *accept_len,
+                               int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
+                               int32_t *err,
+                                       void *stream)
+{
+    StepLaunch in;
+    size_t need = 0;
+    const jt_status st = step_setup(draft_logits, draft_row_stride, target_logits,
+                                    target_row_stride, V, W, parent, tokens, S, B, N, q, k_tree,
+                                    v_tree, k_prefix, v_prefix, block_table, max_blocks_per_seq,
+                                    block_size, num_blocks, prefix_len, max_prefix, Hq, Hkv, d,
+                                    scale, dtype, ids, logprob, row_lse, row_entropy, anc, depth,
+                                    out, lse, accept_len, accept_path, bonus, argmax_out, err, in,
+                                    need);
+    if (st != JT_OK || S == 0)
+        return st;
+    if (need > kStaticScratchBytes)
+        return JT_ERR_SCRATCH;
+    return launch_step_static(in, as_stream(stream));
 }
 
 jt_status jt_build_tree_best_first(const int32_t *ids, const float *logprob,

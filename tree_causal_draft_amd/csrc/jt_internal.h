@@ -231,6 +231,11 @@ size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d,
                       int block_size);
 jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st);
 
+// jt_draft_verify_step_noalloc: the step's scratch lives in a static device array of
+// this size (each GPU the call runs on holds one until the process ends)
+constexpr size_t kStaticScratchBytes = (size_t)48 << 20;
+jt_status launch_step_static(const StepLaunch &in, hipStream_t st);
+
 jt_status launch_mfma_rate(int iters, int blocks, float *out, hipStream_t st);
 
 } // namespace jt

@@ -7,6 +7,7 @@
 #include "sample.hip"
 #include "attn.hip"
 #include "step.hip"
+#include "step_static.hip"
 #include "tree.hip"
 #include "commit.hip"
 #include "probe.hip"
