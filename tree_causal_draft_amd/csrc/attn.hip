@@ -1025,10 +1025,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
 
     // ---- one 64-key tile of this wave, in two parts: (1) QK^T, mask and online softmax,
     // leaving the tile's P^T fragments in pf; (2) PV from pf.
-    auto qk_softmax = [&](const uint8_t *kb, uint64_t vis, bf16x8_t (&pf)[2][2]) {
+    auto qk = [&](const uint8_t *kb, f32x16_t (&sacc)[2]) {
         // S^T = K . Q^T for 2 key blocks of 32.  K row kbk*32 + col, segment 2*ks + hh;
         // the 32-row step keeps the swizzle, so it is an immediate offset.
-        f32x16_t sacc[2];
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -1069,6 +1068,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
                 sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, cur[q]), qf[k4 + q], sacc[kbk], 0, 0, 0);
         }
+    };
+    auto softmax = [&](f32x16_t (&sacc)[2], uint64_t vis, bf16x8_t (&pf)[2][2]) {
         if (vis != ~0ull) {
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk) {
@@ -1132,6 +1133,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
             }
         l_i += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     };
+    auto qk_softmax = [&](const uint8_t *kb, uint64_t vis, bf16x8_t (&pf)[2][2]) {
+        f32x16_t sacc[2];
+        qk(kb, sacc);
+        softmax(sacc, vis, pf);
+    };
     auto pv = [&](const uint8_t *vb, const bf16x8_t (&pf)[2][2]) {
         // O^T += V^T . P^T; V^T fragments by transposing reads of row-major V.  The key
         // rows of fragment (kbk, m2) are kbk*32 + 16*m2 + 4*hh + j16/4 (+8 for the upper
@@ -1178,52 +1184,59 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
     };
 
     if constexpr (NWR == 8) {
-        // ---- 8 waves, 4 stages, ping-pong.  Waves 0-3 (group A) and
-        // 4-7 (group B) share the SIMDs pairwise; B runs half a tile behind A, so on a SIMD
-        // one wave's softmax (VALU) runs under the other's MFMAs.  Barrier j is where A
-        // starts tile j and where B has finished the softmax of tile j - 1 (its PV of
-        // j - 1 follows); after it, every wave issues its share of the DMA of tile j + 2
-        // into the stage of tile j - 2, which both groups have finished.  Before barrier j
-        // each wave waits for its own share of tile j's DMA; only DMAs are in flight, so
-        // that wait is vmcnt(NOPS) while the DMA of tile j + 1 may still run.
+        // ---- 8 waves, 4 stages, two-phase ping-pong.  Waves 0-3 (group A) and 4-7 (group
+        // B) share the SIMDs pairwise (wave w and w + 4 on SIMD w).  A tile j takes two
+        // phases, each closed by a workgroup barrier, and in each phase one wave of every
+        // SIMD issues MFMAs while the other runs a softmax on the vector ALU:
+        //   phase a   A: PV of tile j-1, QK of tile j       B: softmax of tile j-1
+        //   phase b   A: softmax of tile j                  B: PV of tile j-1, QK of tile j
+        // (32 MFMAs against one softmax per phase).  At the barrier that opens tile j every
+        // wave issues its share of the DMA of tile j + 2 into the stage of tile j - 2, whose
+        // K and V both groups have finished (its last reader, B's PV, ran in phase b of
+        // tile j - 1).  Before that barrier each wave waits for its own share of tile j;
+        // only DMAs are in flight, so the wait is vmcnt(NOPS) while tile j + 1 may still
+        // run.  A rescale of O by the softmax of tile j follows the PV of tile j - 1 and
+        // precedes that of tile j, in both groups.
         const int grp = wid >> 2;
         bf16x8_t pf[2][2];
+        f32x16_t sacc[2];
         if (0 < ntiles && !have_pro[0])
             issue_tile(kbeg, stage(0));
         if (1 < ntiles && !have_pro[NPRO - 1])
             issue_tile(kbeg + TILE, stage(1));
-        auto wait_own = [&](bool newer_in_flight) {
-            if (newer_in_flight)
-                wait_vm<NOPS>();
-            else
-                wait_vm<0>();
+        auto mfma_phase = [&](int j) {
+            if (j > 0)
+                pv(stage((j - 1) & 3) + TILEB, pf);
+            if (j < ntiles)
+                qk(stage(j & 3), sacc);
         };
-        if (grp == 1)
-            wait_own(1 < ntiles);
-        for (int j = 0; j < ntiles; ++j) {
-            const int k = j & 3;
+        for (int j = 0; j <= ntiles; ++j) {
             const int kt = kbeg + j * TILE;
-            if (grp == 0)
-                wait_own(j + 1 < ntiles);
-            barrier_keep_dma();
+            if (j < ntiles) {
+                if (j + 1 < ntiles)
+                    wait_vm<NOPS>();
+                else
+                    wait_vm<0>();
+            }
+            barrier_keep_dma();  // phase a of tile j
             if (j + 2 < ntiles)
-                issue_tile(kt + 2 * TILE, stage((k + 2) & 3));
-            if (grp == 0) {
-                if (wave_has_rows) {
-                    qk_softmax(stage(k), vis_window(kt), pf);
-                    pv(stage(k) + TILEB, pf);
+                issue_tile(kt + 2 * TILE, stage((j + 2) & 3));
+            if (wave_has_rows) {
+                if (grp == 0)
+                    mfma_phase(j);
+                else if (j > 0)
+                    softmax(sacc, vis_window(kt - TILE), pf);
+            }
+            barrier_keep_dma();  // phase b of tile j
+            if (wave_has_rows) {
+                if (grp == 0) {
+                    if (j < ntiles)
+                        softmax(sacc, vis_window(kt), pf);
+                } else {
+                    mfma_phase(j);
                 }
-            } else {
-                if (wave_has_rows) {
-                    if (j > 0)
-                        pv(stage((k + 3) & 3) + TILEB, pf);
-                    qk_softmax(stage(k), vis_window(kt), pf);
-                }
-                wait_own(j + 2 < ntiles);
             }
         }
-        if (grp == 1 && wave_has_rows)  // B's PV of the last tile
-            pv(stage((ntiles - 1) & 3) + TILEB, pf);
     } else {
         // ---- 4 waves (few rows), double buffering: tiles 0 and 1 are fetched before the
         // loop (into the two stages); after barrier j (j >= 1), tile j + 1 goes to the
