@@ -53,7 +53,7 @@ CALLS = ("topw", "mask", "attention", "verify")
 KERNELS = {
     "topw": ["topw_partial_kernel", "topw_merge_kernel"],
     "mask": ["build_mask_kernel"],
-    "attention": ["attn_bf16_kernel", "attn_combine_kernel", "attn_simple_kernel"],
+    "attention": ["attn_bf16_kernel", "attn_combine_kernel", "attn_f32_kernel"],
     "verify": ["argmax_partial_kernel", "verify_walk_kernel"],
     "step": ["step_phase1", "step_scan_kernel", "step_phase2"],
     "tree": ["tree_build_kernel"],
@@ -62,7 +62,7 @@ KERNELS = {
 }
 # the kernel whose dispatches count the launches of each entry point
 MARKER = {"topw": "topw_partial_kernel", "mask": "build_mask_kernel",
-          "attention": ("attn_bf16_kernel", "attn_simple_kernel"),
+          "attention": ("attn_bf16_kernel", "attn_f32_kernel"),
           "verify": "argmax_partial_kernel", "step": "step_phase2", "tree": "tree_build_kernel",
           "commit": "commit_kv_kernel", "sampled": "sample_select_kernel"}
 

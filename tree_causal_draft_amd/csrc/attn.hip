@@ -32,7 +32,7 @@
 // (split-KV) until the chip is covered; each chunk writes a normalised bf16 partial with
 // its (max, sum) and attn_combine_kernel merges them.
 //
-// fp32 -> attn_simple_kernel: one workgroup per (s, v, g) on the vector ALU.
+// fp32 -> attn_f32_kernel: 16 query rows per workgroup on the vector ALU, K/V tiles in LDS.
 #include <type_traits>
 
 #include "jt_internal.h"
@@ -104,144 +104,154 @@ __device__ void attn_validate(const AttnArgs &a, int s)
 
 // ------------------------------------------------------------------ VALU kernel --
 
-template <typename T>
-__device__ __forceinline__ float ld(const T *p, int64_t i)
+// grid (ceil(B / NV), S * Hkv), 256 threads: one workgroup per block of NV = 16 / G nodes
+// (at least one) of one (sequence s, KV head g), i.e. kF32Rows = 16 query rows, node-major
+// (row r: node v0 + r / G, head g * G + r % G; rows past B or past NV * G stay idle).  Per
+// 64-key tile the K and V rows go to LDS with coalesced 16-byte loads.  Lane k of every
+// wave holds key k and scores it against the wave's four rows (wave w: rows w, w + 4, ...),
+// so the online softmax of a row is a wave reduction over the tile's keys; then thread
+// (column e, row group) accumulates P . V for its rows.  The scores are in the exp2 domain
+// (q is scaled by scale * log2 e when staged).
+constexpr int kF32Rows = 16;
+template <int D>
+__global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
 {
-    if constexpr (sizeof(T) == 2)
-        return bf16_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
-    else
-        return p[i];
-}
-template <typename T> __device__ __forceinline__ void st(T *p, int64_t i, float v)
-{
-    if constexpr (sizeof(T) == 2)
-        reinterpret_cast<uint16_t *>(p)[i] = f32_to_bf16(v);
-    else
-        p[i] = v;
-}
-
-// grid (B, S*Hkv); 256 threads; one node v and its G heads per workgroup.
-template <typename T>
-__global__ void __launch_bounds__(256) attn_simple_kernel(AttnArgs a)
-{
-    __shared__ float qs[8][128];
-    __shared__ float ps[8][64];
-    __shared__ float alpha_s[8];
-    __shared__ float m_s[8], l_s[8];
-    const int v = blockIdx.x;
+    constexpr int KP = D + 4;    // K row pitch in floats (staggers the lanes' 16-byte reads)
+    constexpr int RG = 256 / D;  // row groups of the P . V ownership
+    constexpr int NO = kF32Rows / RG;
+    __shared__ __attribute__((aligned(16))) float qs[kF32Rows][D];
+    __shared__ __attribute__((aligned(16))) float ks[64][KP];
+    __shared__ __attribute__((aligned(16))) float vs[64][D];
+    __shared__ float ps[kF32Rows][64];
+    __shared__ float alpha_s[kF32Rows], m_s[kF32Rows], l_s[kF32Rows];
+    __shared__ uint64_t anc_s[kF32Rows][4];
+    __shared__ int kval[64];
+    const int G = a.G, B = a.B;
+    const int NV = max(1, kF32Rows / G);
+    const int R = NV * G;
+    const int v0 = blockIdx.x * NV;
     const int s = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const int D = a.d, G = a.G;
-    const T *q = reinterpret_cast<const T *>(a.q);
-    const T *kp = reinterpret_cast<const T *>(a.k_prefix);
-    const T *vp = reinterpret_cast<const T *>(a.v_prefix);
-    const T *kt = reinterpret_cast<const T *>(a.k_tree);
-    const T *vt = reinterpret_cast<const T *>(a.v_tree);
+    const float *qg = reinterpret_cast<const float *>(a.q);
+    const float *kp = reinterpret_cast<const float *>(a.k_prefix);
+    const float *vp = reinterpret_cast<const float *>(a.v_prefix);
+    const float *ktr = reinterpret_cast<const float *>(a.k_tree);
+    const float *vtr = reinterpret_cast<const float *>(a.v_tree);
 
-    if (a.err && v == 0 && g == 0)
+    if (a.err && blockIdx.x == 0 && g == 0)
         attn_validate(a, s);
     const int P = clamp_prefix(a, s);
     const float c = a.scale * kLog2eA;
-    for (int i = t; i < G * D; i += 256) {
-        const int hh = i / D, e = i % D;
-        qs[hh][e] = ld(q, (((int64_t)s * a.B + v) * a.Hq + g * G + hh) * D + e) * c;
+    for (int i = t; i < kF32Rows * D; i += 256) {
+        const int r = i / D, e = i % D;
+        const int v = v0 + r / G;
+        qs[r][e] = (r < R && v < B)
+                       ? qg[(((int64_t)s * B + v) * a.Hq + g * G + r % G) * D + e] * c
+                       : 0.f;
     }
-    if (t < G) {
-        m_s[t] = -INFINITY;
-        l_s[t] = 0.f;
+    if (t < NV * 4) {
+        const int v = v0 + t / 4;
+        anc_s[t / 4][t % 4] = v < B ? a.anc[((int64_t)s * B + v) * 4 + t % 4] : 0ull;
     }
-    const uint64_t *ar = a.anc + ((int64_t)s * a.B + v) * 4;
-    const uint64_t w0 = ar[0], w1 = ar[1], w2 = ar[2], w3 = ar[3];
-    __syncthreads();
-
-    // PV ownership: column e = t % D, heads t / D + k * (256 / D)
-    const int e = t % D;
-    const int hstep = 256 / D;
-    float acc[8];
+    const int v_hi = min(B - 1, v0 + NV - 1);
+    const int kend = P + v_hi + 1;  // ancestors of v have indices <= v
+    float m_r[4], l_r[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-        acc[k] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+        m_r[i] = -INFINITY;
+        l_r[i] = 0.f;
+    }
+    const int e = t % D, rg = t / D;
+    float acc[NO];
+#pragma unroll
+    for (int j = 0; j < NO; ++j)
+        acc[j] = 0.f;
 
-    const int kend = P + v + 1;
-    for (int k0 = 0; k0 < kend; k0 += 64) {
-        // scores: key k0 + lane, heads wid, wid + 4
-        const int j = k0 + lane;
-        int64_t off = -1;
-        if (j < kend) {
-            off = kv_offset(a, s, g, P, j);
+    for (int kt = 0; kt < kend; kt += 64) {
+        __syncthreads();  // the previous tile's reads are done
+        for (int i = t; i < 64 * (D / 4); i += 256) {
+            const int kk = i / (D / 4), c4 = i % (D / 4);
+            const int j = kt + kk;
+            const int64_t off = j < kend ? kv_offset(a, s, g, P, j) : -1;
+            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+            if (off >= 0) {
+                kx = *reinterpret_cast<const float4 *>((j < P ? kp : ktr) + off + 4 * c4);
+                vx = *reinterpret_cast<const float4 *>((j < P ? vp : vtr) + off + 4 * c4);
+            }
+            *reinterpret_cast<float4 *>(&ks[kk][4 * c4]) = kx;
+            *reinterpret_cast<float4 *>(&vs[kk][4 * c4]) = vx;
+            if (c4 == 0)
+                kval[kk] = off >= 0;
+        }
+        __syncthreads();
+        // scores of key kt + lane for rows wid + 4i
+        const int j = kt + lane;
+        float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int x = 0; x < D; x += 4) {
+            const float4 kx = *reinterpret_cast<const float4 *>(&ks[lane][x]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 qx = *reinterpret_cast<const float4 *>(&qs[wid + 4 * i][x]);
+                sc[i] = __builtin_fmaf(qx.x, kx.x, sc[i]);
+                sc[i] = __builtin_fmaf(qx.y, kx.y, sc[i]);
+                sc[i] = __builtin_fmaf(qx.z, kx.z, sc[i]);
+                sc[i] = __builtin_fmaf(qx.w, kx.w, sc[i]);
+            }
+        }
+        const bool key_ok = kval[lane] != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wid + 4 * i;
+            bool vis = key_ok;
             if (j >= P) {
                 const int u = j - P;
-                const uint64_t wsel = u < 64 ? w0 : u < 128 ? w1 : u < 192 ? w2 : w3;
-                if (!((wsel >> (u & 63)) & 1ull))
-                    off = -1;
+                vis = vis && ((anc_s[r / G][u >> 6] >> (u & 63)) & 1ull);
             }
-        }
-        const T *kb = j < P ? kp : kt;
-        for (int hh = wid; hh < G; hh += 4) {
-            float sc = -INFINITY;
-            if (off >= 0) {
-                float dot = 0.f;
-                for (int x = 0; x < D; ++x)
-                    dot = __builtin_fmaf(qs[hh][x], ld(kb, off + x), dot);
-                sc = dot;
-            }
-            const float mx = wave_max_f32(sc);
-            const float m_old = m_s[hh];
-            const float m_new = fmaxf(m_old, mx);
+            vis = vis && r < R && v0 + r / G < B;
+            const float sv = vis ? sc[i] : -INFINITY;
+            const float m_new = fmaxf(m_r[i], wave_max_f32(sv));
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float p = __builtin_amdgcn_exp2f(sc - m_use);
-            float sum = p;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-                sum += __shfl_xor(sum, o, kWave);
-            ps[hh][lane] = p;
-            if (lane == 0) {
-                const float al = __builtin_amdgcn_exp2f(m_old - m_use);
-                alpha_s[hh] = al;
-                l_s[hh] = l_s[hh] * al + sum;
-                m_s[hh] = m_new;
-            }
+            const float p = __builtin_amdgcn_exp2f(sv - m_use);
+            const float al = __builtin_amdgcn_exp2f(m_r[i] - m_use);
+            l_r[i] = l_r[i] * al + wave_sum_f32(p);
+            m_r[i] = m_new;
+            ps[r][lane] = p;
+            if (lane == 0)
+                alpha_s[r] = al;
         }
         __syncthreads();
-        // PV for this tile
-        const int nk = min(64, kend - k0);
+        const int nk = min(64, kend - kt);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int hh = t / D + k * hstep;
-            if (hh < G)
-                acc[k] *= alpha_s[hh];
-        }
-        for (int jj = 0; jj < nk; ++jj) {
-            const int jv = k0 + jj;
-            const int64_t o2 = kv_offset(a, s, g, P, jv);
-            if (o2 < 0)
-                continue;
-            if (jv >= P) {
-                const int u = jv - P;
-                const uint64_t wsel = u < 64 ? w0 : u < 128 ? w1 : u < 192 ? w2 : w3;
-                if (!((wsel >> (u & 63)) & 1ull))
-                    continue;
-            }
-            const float vv = ld(jv < P ? vp : vt, o2 + e);
+        for (int jo = 0; jo < NO; ++jo)
+            acc[jo] *= alpha_s[rg + RG * jo];
+        for (int k2 = 0; k2 < nk; ++k2) {
+            const float vv = vs[k2][e];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int hh = t / D + k * hstep;
-                if (hh < G)
-                    acc[k] = __builtin_fmaf(ps[hh][jj], vv, acc[k]);
-            }
+            for (int jo = 0; jo < NO; ++jo)
+                acc[jo] = __builtin_fmaf(ps[rg + RG * jo][k2], vv, acc[jo]);
         }
-        __syncthreads();
     }
-    T *out = reinterpret_cast<T *>(a.out);
+    if (lane == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int hh = t / D + k * hstep;
-        if (hh >= G)
+        for (int i = 0; i < 4; ++i) {
+            m_s[wid + 4 * i] = m_r[i];
+            l_s[wid + 4 * i] = l_r[i];
+        }
+    }
+    __syncthreads();
+    float *out = reinterpret_cast<float *>(a.out);
+#pragma unroll
+    for (int jo = 0; jo < NO; ++jo) {
+        const int r = rg + RG * jo;
+        const int v = v0 + r / G;
+        if (r >= R || v >= B)
             continue;
-        const int64_t row = ((int64_t)s * a.B + v) * a.Hq + g * G + hh;
-        st(out, row * D + e, acc[k] / l_s[hh]);
+        const int64_t row = ((int64_t)s * B + v) * a.Hq + g * G + r % G;
+        const float l = l_s[r];
+        out[row * D + e] = l > 0.f ? acc[jo] / l : 0.f;
         if (a.lse && e == 0)
-            a.lse[row] = (m_s[hh] + __log2f(l_s[hh])) * kLn2;
+            a.lse[row] = l > 0.f ? (m_s[r] + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -1536,7 +1546,12 @@ jt_status launch_attention(const AttnArgs &a, void *ws, hipStream_t st)
         return JT_OK;
     if (a.dtype == JT_BF16)
         return a.d == 128 ? launch_mfma<128>(a, ws, st) : launch_mfma<64>(a, ws, st);
-    hipLaunchKernelGGL((attn_simple_kernel<float>), dim3(a.B, a.S * a.Hkv), dim3(256), 0, st, a);
+    const int nv = (kF32Rows / a.G) > 1 ? kF32Rows / a.G : 1;
+    const dim3 grid((unsigned)((a.B + nv - 1) / nv), (unsigned)(a.S * a.Hkv));
+    if (a.d == 128)
+        hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(256), 0, st, a);
     return launch_status(hipGetLastError());
 }
 
