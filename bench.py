@@ -667,9 +667,6 @@ def main():
         return max(CALLS, key=lambda k: r["per_call_us"][k])
 
     def timing(r):
-        if r["w"].cfg.dtype != "bf16":
-            return ("hipGraph of K steps (step i on cold input set i mod n), the four calls "
-                    "with top-W and verification on side streams; median of the replays")
         return ("hipGraph of K jt_draft_verify_step calls (step i on cold input set i mod n; "
                 "two to four kernel launches each); median of the replays")
 

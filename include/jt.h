@@ -204,7 +204,8 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
  * documented above, in two kernel launches instead of seven: the bandwidth-bound logit
  * scans (top-W partials, target arg-max partials), the mask and the attention's main pass
  * share the first launch; the split-KV merge, the top-W merge and the verification walk
- * share the second.  When a KV group holds more than 128 query rows (G*B > 128), the
+ * share the second.  In fp32 the attention (vector ALU, no split-KV) joins the second
+ * launch instead, after the mask.  When a KV group holds more than 128 query rows (G*B > 128), the
  * attention runs 256-row workgroups whose LDS leaves no room beside them, and the scans
  * and the mask take a launch of their own before it (three launches; a fourth, first, when
  * several sequences take the attention's balanced schedule, which spreads all sequences'
@@ -218,12 +219,13 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
  * attention and verification calls would report.
  *
  *   draft_logits   [S*N, draft_row_stride]   target_logits [S*B, target_row_stride]
- *   (both dtype, V used columns, 16-byte aligned with row strides a multiple of 8)
+ *   (both dtype, V used columns, 16-byte aligned, row strides a multiple of 16 bytes)
  *   W, N           as for jt_topw_per_depth (rows = S*N) and jt_verify_greedy
  *   row_entropy    optional, as for jt_topw_per_depth
  *   attention args as for jt_tree_attention (anc is produced here)
- * Supported: dtype JT_BF16 only; d in {64, 128}; the ranges of the four calls.  Anything
- * else returns JT_ERR_DTYPE / JT_ERR_ALIGN / JT_ERR_SHAPE: use the four calls instead.
+ * Supported: dtype JT_BF16 or JT_F32; d in {64, 128}; the ranges of the four calls.
+ * Anything else returns JT_ERR_DTYPE / JT_ERR_ALIGN / JT_ERR_SHAPE: use the four calls
+ * instead.
  */
 size_t jt_step_workspace_size(int32_t S, int32_t B, int32_t N, int32_t W, int32_t V, int32_t Hq,
                               int32_t Hkv, int32_t d, int32_t max_prefix, int32_t block_size,

@@ -98,17 +98,10 @@ def _against_oracle(w, st, sel=None):
 @pytest.mark.parametrize("name", ["tiny", "low_budget", "high_budget"])
 def test_bench_inputs_against_oracle(name):
     """The benchmarked call on the benchmark's own inputs (its seed, full vocabulary): equal
-    to the four calls bit for bit, and to the oracle on every output and attention row.
-    tiny is fp32, which the fused call does not take: its step is the four calls."""
+    to the four calls bit for bit, and to the oracle on every output and attention row
+    (tiny is fp32: two launches with the attention in the second)."""
     w = wl.make(name, BENCH_SEED[name])
-    if w.cfg.dtype == "f32":
-        need_gpu()
-        st = DeviceStep(w, "cuda:0")
-        st.run()
-        torch.cuda.synchronize()
-        err = st.err_mask | st.err_attn | st.err_verify
-    else:
-        st, err = _compare(w, name + " bench inputs")
+    st, err = _compare(w, name + " bench inputs")
     assert int(err.abs().sum()) == 0
     _against_oracle(w, st)
 
@@ -193,25 +186,33 @@ def test_fused_against_oracle():
     assert (np.abs(got - out) <= BF16_ATOL + BF16_RTOL * np.abs(out)).all()
 
 
-def test_rejects_fp32_and_misaligned_rows():
+@pytest.mark.parametrize("kw", [
+    dict(S=3, B=40, N=6, W=3, prefix=130, V=5000),            # several node blocks, G = 4
+    dict(S=2, B=9, N=4, W=2, prefix=0, V=1024, d=128, Hq=8, Hkv=1),   # no prefix, G = 8
+    dict(S=2, B=20, N=5, W=4, prefix=(40, 300), V=3000, Hq=6, Hkv=2,
+         paged=True, block_size=16),                                      # paged, G = 3
+])
+def test_fp32_shapes(kw):
+    """The fp32 step (two launches, attention in the second) against the four calls."""
+    kw = dict(kw)
+    w = wl.make("tiny", 816, tree="random", **kw)
+    _compare(w, f"fp32 {kw}")
+
+
+def test_rejects_misaligned_rows():
     need_gpu()
     import tree_causal_draft_amd as jt
-    w = wl.make("tiny", 816)
-    st = DeviceStep(w, "cuda:0")
-    assert not hasattr(st, "step_ws")  # fp32 has no fused path
-    with pytest.raises(jt.JTError, match="element type"):
-        jt.draft_verify_step(st.draft, st.target, st.parent, st.tokens, w.cfg.N, w.cfg.W, st.q,
-                             st.k_tree, st.v_tree, st.k_prefix, st.v_prefix, st.prefix_len)
-    w = wl.make("low_budget", 817, V=4096)
-    st = DeviceStep(w, "cuda:0")
-    rows, stride = st.draft.shape
-    buf = torch.empty(rows * stride + 1, dtype=st.draft.dtype, device=st.draft.device)
-    shifted = buf[1:].view(rows, stride)  # contiguous, 2 bytes past a 16-byte boundary
-    shifted.copy_(st.draft)
-    with pytest.raises(jt.JTError, match="misaligned"):
-        jt.draft_verify_step(shifted, st.target, st.parent, st.tokens, w.cfg.N, w.cfg.W, st.q,
-                             st.k_tree, st.v_tree, st.k_prefix, st.v_prefix, st.prefix_len,
-                             workspace=st.step_ws)
+    for name, shift in (("low_budget", 1), ("tiny", 1)):
+        w = wl.make(name, 817, V=4096)
+        st = DeviceStep(w, "cuda:0")
+        rows, stride = st.draft.shape
+        buf = torch.empty(rows * stride + shift, dtype=st.draft.dtype, device=st.draft.device)
+        shifted = buf[shift:].view(rows, stride)  # contiguous, off a 16-byte boundary
+        shifted.copy_(st.draft)
+        with pytest.raises(jt.JTError, match="misaligned"):
+            jt.draft_verify_step(shifted, st.target, st.parent, st.tokens, w.cfg.N, w.cfg.W,
+                                 st.q, st.k_tree, st.v_tree, st.k_prefix, st.v_prefix,
+                                 st.prefix_len, workspace=st.step_ws)
 
 
 @pytest.mark.parametrize("name", ["low_budget", "high_budget"])

@@ -452,5 +452,5 @@ def probe_mfma_rate(iters, blocks, out=None, stream=None):
         out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     _need(out, "out")
     _check(lib().jt_probe_mfma_rate(int(iters), int(blocks), _ptr(out), _stream(stream)),
-           "jt_probe_mfma_rate", "jt_draft_verify_step_noalloc")
+           "jt_probe_mfma_rate")
     return out

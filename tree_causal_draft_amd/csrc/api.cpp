@@ -268,11 +268,12 @@ size_t jt_step_workspace_size(int32_t S, int32_t B, int32_t N, int32_t W, int32_
                               int32_t Hkv, int32_t d, int32_t max_prefix, int32_t block_size,
                               jt_dtype dtype)
 {
-    if (dtype != JT_BF16 || attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype) != JT_OK ||
+    if (attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype) != JT_OK ||
         topw_shape(S * N, V, W, dtype) != JT_OK || verify_shape(S, B, V, N, dtype) != JT_OK ||
         S == 0)
         return 0;
-    return step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_size > 0 ? block_size : 0);
+    return step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_size > 0 ? block_size : 0,
+                          dtype);
 }
 
 } // extern "C"
@@ -292,7 +293,7 @@ static jt_status step_setup(const void *draft_logits, int64_t draft_row_stride,
                                int32_t *accept_path, int32_t *bonus, int32_t *argmax_out,
                                int32_t *err, StepLaunch &in, size_t &need)
 {
-    if (dtype != JT_BF16)
+    if (dtype != JT_BF16 && dtype != JT_F32)
         return JT_ERR_DTYPE;
     jt_status st = attn_shape(S, B, Hq, Hkv, d, max_prefix, dtype);
     if (st == JT_OK)
@@ -325,10 +326,12 @@ static jt_status step_setup(const void *draft_logits, int64_t draft_row_stride,
     if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
         (k_prefix && !aligned16(k_prefix)) || (v_prefix && !aligned16(v_prefix)))
         return JT_ERR_ALIGN;
-    if (!aligned16(target_logits) || target_row_stride % 8 != 0 ||
-        (N > 0 && (!aligned16(draft_logits) || draft_row_stride % 8 != 0)))
+    const int per16 = dtype == JT_BF16 ? 8 : 4;  // elements per 16 bytes
+    if (!aligned16(target_logits) || target_row_stride % per16 != 0 ||
+        (N > 0 && (!aligned16(draft_logits) || draft_row_stride % per16 != 0)))
         return JT_ERR_ALIGN;
-    need = step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_table ? block_size : 0);
+    need = step_workspace(S, B, N, W, V, Hq, Hkv, d, max_prefix, block_table ? block_size : 0,
+                          dtype);
     AttnArgs &a = in.attn;
     a.q = q;
     a.k_tree = k_tree;

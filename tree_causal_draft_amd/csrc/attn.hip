@@ -114,7 +114,7 @@ __device__ void attn_validate(const AttnArgs &a, int s)
 // (q is scaled by scale * log2 e when staged).
 constexpr int kF32Rows = 16;
 template <int D>
-__global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
+__device__ __forceinline__ void attn_f32_block(const AttnArgs &a, int bx, int by)
 {
     constexpr int KP = D + 4;    // K row pitch in floats (staggers the lanes' 16-byte reads)
     constexpr int RG = 256 / D;  // row groups of the P . V ownership
@@ -129,8 +129,8 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
     const int G = a.G, B = a.B;
     const int NV = max(1, kF32Rows / G);
     const int R = NV * G;
-    const int v0 = blockIdx.x * NV;
-    const int s = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
+    const int v0 = bx * NV;
+    const int s = by / a.Hkv, g = by % a.Hkv;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const float *qg = reinterpret_cast<const float *>(a.q);
     const float *kp = reinterpret_cast<const float *>(a.k_prefix);
@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
     const float *ktr = reinterpret_cast<const float *>(a.k_tree);
     const float *vtr = reinterpret_cast<const float *>(a.v_tree);
 
-    if (a.err && blockIdx.x == 0 && g == 0)
+    if (a.err && bx == 0 && g == 0)
         attn_validate(a, s);
     const int P = clamp_prefix(a, s);
     const float c = a.scale * kLog2eA;
@@ -253,6 +253,18 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
         if (a.lse && e == 0)
             a.lse[row] = l > 0.f ? (m_s[r] + __log2f(l)) * kLn2 : -INFINITY;
     }
+}
+
+// node blocks of the fp32 pass per (sequence, KV head)
+__host__ __device__ inline int attn_f32_blocks(int B, int G)
+{
+    const int nv = kF32Rows / G > 1 ? kF32Rows / G : 1;
+    return (B + nv - 1) / nv;
+}
+
+template <int D> __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
+{
+    attn_f32_block<D>(a, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ MFMA kernel --
@@ -1546,8 +1558,7 @@ jt_status launch_attention(const AttnArgs &a, void *ws, hipStream_t st)
         return JT_OK;
     if (a.dtype == JT_BF16)
         return a.d == 128 ? launch_mfma<128>(a, ws, st) : launch_mfma<64>(a, ws, st);
-    const int nv = (kF32Rows / a.G) > 1 ? kF32Rows / a.G : 1;
-    const dim3 grid((unsigned)((a.B + nv - 1) / nv), (unsigned)(a.S * a.Hkv));
+    const dim3 grid((unsigned)attn_f32_blocks(a.B, a.G), (unsigned)(a.S * a.Hkv));
     if (a.d == 128)
         hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(256), 0, st, a);
     else

@@ -228,7 +228,7 @@ jt_status launch_commit_kv(const int32_t *accept_len, const int32_t *accept_path
                            int32_t *new_prefix_len, int32_t *err, hipStream_t st);
 
 size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d, int max_prefix,
-                      int block_size);
+                      int block_size, int dtype);
 jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st);
 
 // jt_draft_verify_step_noalloc: the step's scratch lives in a static device array of

@@ -1,6 +1,7 @@
 // The whole draft-and-verify step in two launches (jt_draft_verify_step); three for
 // shapes whose attention needs 8-wave workgroups (see step_scan_kernel), and then a
-// fourth, the attention's schedule kernel, when several sequences share the pass.
+// fourth, the attention's schedule kernel, when several sequences share the pass.  An fp32
+// step takes two launches with the attention in the second (see step_scan_f32_kernel).
 //
 // Each launch runs several steps side by side, one role per range of workgroup ids:
 //   phase 1  attention   the split-KV MFMA pass; its workgroups build the tree's ancestor
@@ -48,7 +49,9 @@ struct StepPlan {
     AttnPlan ap;     // nwr >= 4: the phase-1 workgroup is 64 * ap.nwr threads
     TopwPlan tp;
     ArgPlan gp;
-    int nA, nT, nG, nM;  // phase-1 workgroups per role
+    int f32;             // fp32 step: attention on the vector ALU, in phase 2
+    int nA, nT, nG, nM;  // phase-1 workgroups per role (fp32: nA counts phase 2's)
+    int nV;              // fp32: the attention's prefix checks, one workgroup per sequence
     int nC, nR, nW;      // phase-2 workgroups per role
 };
 
@@ -68,23 +71,24 @@ template <int D, int NWR> struct StepLds {
 // workgroup.
 // kArgPrefetch: the arg-max role loads its next sub-chunk early, worth it in the scan
 // launch (three waves per SIMD) and not in the attention-sharing phase 1.
-template <int NW, bool kArgPrefetch>
+// T: the logits' element type (uint16_t words of bf16, or float).
+template <int NW, bool kArgPrefetch, typename T = uint16_t>
 __device__ __forceinline__ void step_scan_roles(const StepArgs &sa, const StepPlan &sp, int b,
                                                 uint8_t *pool)
 {
     if (b < sp.nT) {
         const int wid = threadIdx.x >> 6;
         uint64_t *cand = reinterpret_cast<uint64_t *>(pool) + wid * (kWaveCap + 2 * JT_MAX_W);
-        topw_partial_wave<uint16_t, true>(
-            static_cast<const uint16_t *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
+        topw_partial_wave<T, true>(
+            static_cast<const T *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
             sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, sa.tt, b * NW + wid, cand,
             cand + kWaveCap + JT_MAX_W);
         return;
     }
     b -= sp.nT;
     if (b < sp.nG) {
-        argmax_partial_block<uint16_t, true, 64 * NW, kArgPrefetch>(
-            static_cast<const uint16_t *>(sa.target), sa.target_stride, sa.V, sp.gp.nsub,
+        argmax_partial_block<T, true, 64 * NW, kArgPrefetch>(
+            static_cast<const T *>(sa.target), sa.target_stride, sa.V, sp.gp.nsub,
             sp.gp.sub_per_wg, sp.gp.nchunk, sa.gkeys, sa.gnan, b,
             reinterpret_cast<uint64_t *>(pool), reinterpret_cast<uint32_t *>(pool + NW * 8));
         return;
@@ -127,6 +131,50 @@ __global__ void __launch_bounds__(256) step_scan_kernel(StepArgs sa, StepPlan sp
     step_scan_roles<4, true>(sa, sp, blockIdx.x, pool);
 }
 
+// fp32 steps (the tiny configuration is fp32 end to end) have no split-KV pass, so the
+// attention moves to phase 2, after the mask: phase 1 (this kernel) runs the fp32 logit
+// scans, the mask and, per sequence, the attention's prefix-length and block checks
+// (which the verification walk of phase 2 ORs into err).
+__global__ void __launch_bounds__(256) step_scan_f32_kernel(StepArgs sa, StepPlan sp)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t pool[kScanLds];
+    const int b = blockIdx.x - (sp.nT + sp.nG + sp.nM);
+    if (b < 0)
+        step_scan_roles<4, true, float>(sa, sp, blockIdx.x, pool);
+    else
+        attn_validate(sa.attn, b);
+}
+
+// fp32 phase 2: the verification walk, the top-W merge and the fp32 attention pass (over
+// the mask's rows; its checks ran in phase 1).
+template <int D>
+__global__ void __launch_bounds__(256) step_phase2_f32(StepArgs sa, StepPlan sp)
+{
+    __shared__ __attribute__((aligned(16))) uint64_t mkeys[kStepRowsPerBlock][kMergeLds];
+    int b = blockIdx.x;
+    if (b < sp.nW) {
+        verify_walk_block(b, sa.B, sa.N, sp.gp.nchunk, sa.gkeys, sa.gnan, sa.parent, sa.tokens,
+                          sa.anc, sa.depth, sa.accept_len, sa.accept_path, sa.bonus,
+                          sa.argmax_out, sa.err, sa.err_mask, sa.err_attn);
+        return;
+    }
+    b -= sp.nW;
+    if (b < sp.nR) {
+        const int wid = threadIdx.x >> 6;
+        const int r = b * kStepRowsPerBlock + wid;
+        if (r < sa.S * sa.N)
+            topw_merge_row(r, sa.W, sp.tp.nlist, sa.tkeys, sa.tms, sa.tt, sa.ids, sa.logprob,
+                           sa.row_lse, sa.row_entropy, mkeys[wid]);
+        return;
+    }
+    b -= sp.nR;
+    AttnArgs a = sa.attn;
+    a.anc = sa.anc;
+    a.err = nullptr;
+    const int nvb = attn_f32_blocks(a.B, a.G);
+    attn_f32_block<D>(a, b % nvb, b / nvb);
+}
+
 template <int D, int NB>
 __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
 {
@@ -163,13 +211,32 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Work decomposition of the fused step.  For few rows the phase-1 grid should fit the
 // chip in one round (two 4-wave workgroups per CU); see the scan plan below.
 static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, int max_prefix,
-                          int block_size)
+                          int block_size, int dtype)
 {
     StepPlan sp;
+    const int rows_d = S * N, rows_t = S * B;
+    sp.nV = 0;
+    sp.f32 = dtype == JT_F32;
+    if (sp.f32) {
+        // no split-KV: an empty attention plan (no workspace), the scans as the separate
+        // calls plan them, the fp32 attention pass in phase 2
+        sp.ap = AttnPlan{};
+        sp.ap.n_chunks = 1;
+        sp.tp = topw_plan(rows_d, V);
+        sp.gp = arg_plan(rows_t, V);
+        sp.nA = attn_f32_blocks(B, Hq / Hkv) * S * Hkv;
+        sp.nT = (rows_d * sp.tp.nlist + 3) / 4;
+        sp.nG = rows_t * sp.gp.nchunk;
+        sp.nM = S;
+        sp.nV = S;
+        sp.nC = 0;
+        sp.nR = (rows_d + kStepRowsPerBlock - 1) / kStepRowsPerBlock;
+        sp.nW = S;
+        return sp;
+    }
     sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size, true);
     const bool split = sp.ap.nwr == 8;  // scans in a launch of their own
     const int nw = split ? 4 : sp.ap.nwr;  // waves per scan workgroup
-    const int rows_d = S * N, rows_t = S * B;
     if (split) {
         sp.tp = topw_plan(rows_d, V);
         sp.gp = arg_plan(rows_t, V);
@@ -250,15 +317,22 @@ static StepWs step_ws_layout(const StepPlan &sp, int S, int N, int B, int W, int
 }
 
 size_t step_workspace(int S, int B, int N, int W, int V, int Hq, int Hkv, int d, int max_prefix,
-                      int block_size)
+                      int block_size, int dtype)
 {
-    const StepPlan sp = step_plan(S, B, N, V, Hq, Hkv, d, max_prefix, block_size);
+    const StepPlan sp = step_plan(S, B, N, V, Hq, Hkv, d, max_prefix, block_size, dtype);
     return step_ws_layout(sp, S, N, B, W, d).total;
 }
 
 template <int D>
 static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st)
 {
+    if (sp.f32) {
+        hipLaunchKernelGGL(step_scan_f32_kernel, dim3((unsigned)(sp.nT + sp.nG + sp.nM + sp.nV)),
+                           dim3(256), 0, st, sa, sp);
+        hipLaunchKernelGGL((step_phase2_f32<D>), dim3((unsigned)(sp.nW + sp.nR + sp.nA)),
+                           dim3(256), 0, st, sa, sp);
+        return;
+    }
     if (sp.ap.nwr == 8) {
         if (sp.ap.bal)  // the attention pass's balanced schedule
             hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, sa.attn, sp.ap, sa.aws);
@@ -286,7 +360,7 @@ jt_status launch_step(const StepLaunch &in, void *ws, hipStream_t st)
         return JT_OK;
     const AttnArgs &aa = in.attn;
     const StepPlan sp = step_plan(aa.S, aa.B, in.N, in.V, aa.Hq, aa.Hkv, aa.d, aa.max_prefix,
-                                  aa.block_table ? aa.block_size : 0);
+                                  aa.block_table ? aa.block_size : 0, aa.dtype);
     const StepWs L = step_ws_layout(sp, aa.S, in.N, aa.B, in.W, aa.d);
     uint8_t *w = static_cast<uint8_t *>(ws);
     StepArgs sa;

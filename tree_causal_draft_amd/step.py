@@ -98,7 +98,7 @@ class DeviceStep:
             nb = verify_sampled_workspace_size(S, B, cfg.V, dt)
             self.smp_ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
 
-        if parts == ("topw", "mask", "attn", "verify") and dt == JT_BF16:
+        if parts == ("topw", "mask", "attn", "verify"):
             self.err_step = torch.empty(S, dtype=torch.int32, device=dev)
             nb = step_workspace_size(S, B, N, W, cfg.V, cfg.Hq, cfg.Hkv, cfg.d, w.max_prefix, dt,
                                      cfg.block_size if w.block_table is not None else 0)
