@@ -10,8 +10,9 @@
 //
 // One wave per sequence.  The queue is never materialised as a heap: lane L keeps the
 // score, depth and queued bit of nodes L, L+64, L+128, L+192 in registers, and a pop is
-// one wave-wide maximum of 32-bit order codes (DPP) followed by at most four ballots that
-// find the lowest node index holding it.  An expansion creates at most 16 children, so
+// one wave-wide maximum of 32-bit order codes (DPP) over each lane's best slot (found, with
+// its score and depth, beside the reduction), then one ballot for the lane holding it (a
+// tie between lanes takes three more, by slot, for the lowest node index).  An expansion creates at most 16 children, so
 // each lane owns at most one of them and computes its score itself from the increment
 // table in LDS: a pop moves no data between lanes beyond the popped node's score and
 // depth.  Parent and token stay in registers until the end.  Pops are inherently
@@ -96,27 +97,40 @@ __global__ void __launch_bounds__(64) tree_build_kernel(TreeArgs a)
     }
     int n = 1;
     while (n < B) {
-        const uint32_t M = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+        // the lane's best queued slot (lowest slot on equal keys) with its score and depth,
+        // found while the wave maximum runs
+        uint32_t best = key[0];
+        int bslot = 0;
+        float bsc = sc[0];
+        int bdp = dp[0];
+#pragma unroll
+        for (int k = 1; k < kTreeSlots; ++k) {
+            const bool gt = key[k] > best;
+            best = gt ? key[k] : best;
+            bslot = gt ? k : bslot;
+            bsc = gt ? sc[k] : bsc;
+            bdp = gt ? dp[k] : bdp;
+        }
+        const uint32_t M = wave_max_u32(best);
         if (M == 0u)
             break;  // queue empty
-        // the lowest node index holding M: slot k first (lower k, lower index), then lane
+        // the lowest node index holding M: one ballot when a single lane holds it; on a tie
+        // between lanes, the lowest slot first (lower slot, lower index), then the lowest lane
         static_assert(kTreeSlots == 4, "four slots per lane");
-        const uint64_t b0 = __ballot(key[0] == M), b1 = __ballot(key[1] == M),
-                       b2 = __ballot(key[2] == M), b3 = __ballot(key[3] == M);
-        const int kk = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
-        const uint64_t hit = b0 ? b0 : b1 ? b1 : b2 ? b2 : b3;
-        const int ln = (int)__builtin_ctzll(hit);
+        const uint64_t hit = __ballot(best == M);
+        int ln;
+        if (__popcll(hit) == 1) {
+            ln = (int)__builtin_ctzll(hit);
+        } else {
+            const uint64_t b0 = __ballot(best == M && bslot == 0),
+                           b1 = __ballot(best == M && bslot == 1),
+                           b2 = __ballot(best == M && bslot == 2);
+            ln = (int)__builtin_ctzll(b0 ? b0 : b1 ? b1 : b2 ? b2 : hit);
+        }
+        const int kk = __builtin_amdgcn_readlane(bslot, ln);
         const int v = ln + kWave * kk;
-        float s_sel = sc[0];
-        int d_sel = dp[0];
-#pragma unroll
-        for (int k = 1; k < kTreeSlots; ++k)
-            if (k == kk) {
-                s_sel = sc[k];
-                d_sel = dp[k];
-            }
-        const float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sel), ln));
-        const int dv = __builtin_amdgcn_readlane(d_sel, ln);
+        const float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsc), ln));
+        const int dv = __builtin_amdgcn_readlane(bdp, ln);
         if (lane == ln) {
 #pragma unroll
             for (int k = 0; k < kTreeSlots; ++k)
