@@ -967,7 +967,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
         pre = key < P;
         if (pre) {
             if (paged) {
-                const int blk = bt_lds[(key >> bshift) - bt0];
+                // inline-asm read: a compiler-visible LDS access here would make it wait for
+                // every copy in flight (vmcnt(0)) before each tile's copy is issued
+                const int blk = lds_read_i32(lds_off(&bt_lds[(key >> bshift) - bt0]));
                 off = (blk >= 0 && blk < nblocks)
                           ? (((int64_t)blk * bsize + (key & (bsize - 1))) * Hkv + g) * D
                           : -1;
