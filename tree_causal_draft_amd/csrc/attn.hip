@@ -343,7 +343,10 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
             p.nwg = (int)max(1L, nwg);
             p.ch = 0;
             p.n_chunks = 0;
-            p.remap = 0;
+            // The two row tiles of one (sequence, KV head) need about as many key tiles,
+            // so neighbouring shares read the same keys at the same time; with the remap
+            // they run on one XCD and the second read hits its L2.
+            p.remap = (p.nwg % 8 == 0) ? 1 : 0;
             return p;
         }
     }
@@ -1406,8 +1409,11 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR)  // 2 waves per SIMD: no AG
 attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[AttnLds<D, NWR>::BYTES];
-    if (pl.bal)
-        attn_main_bal<D, NWR>(a, pl, ws, blockIdx.x, lds);
+    if (pl.bal) {
+        // logical share w: XCD (blockIdx & 7) runs shares [x nwg/8, (x + 1) nwg/8)
+        const int b = blockIdx.x;
+        attn_main_bal<D, NWR>(a, pl, ws, pl.remap ? (b & 7) * (pl.nwg >> 3) + (b >> 3) : b, lds);
+    }
     else
         attn_main<D, NWR, false>(a, pl, ws, blockIdx.x, gridDim.x, lds);
 }
