@@ -113,8 +113,10 @@ __device__ void attn_validate(const AttnArgs &a, int s)
 // (column e, row group) accumulates P . V for its rows.  The scores are in the exp2 domain
 // (q is scaled by scale * log2 e when staged).
 constexpr int kF32Rows = 16;
+// anc: the ancestor rows to read; validate: run the argument checks (they write a.err).
 template <int D>
-__device__ __forceinline__ void attn_f32_block(const AttnArgs &a, int bx, int by)
+__device__ __forceinline__ void attn_f32_block(const AttnArgs &a, const uint64_t *anc, bool validate,
+                                               int bx, int by)
 {
     constexpr int KP = D + 4;    // K row pitch in floats (staggers the lanes' 16-byte reads)
     constexpr int RG = 256 / D;  // row groups of the P . V ownership
@@ -138,7 +140,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs &a, int bx, int by
     const float *ktr = reinterpret_cast<const float *>(a.k_tree);
     const float *vtr = reinterpret_cast<const float *>(a.v_tree);
 
-    if (a.err && bx == 0 && g == 0)
+    if (validate && a.err && bx == 0 && g == 0)
         attn_validate(a, s);
     const int P = clamp_prefix(a, s);
     const float c = a.scale * kLog2eA;
@@ -151,7 +153,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs &a, int bx, int by
     }
     if (t < NV * 4) {
         const int v = v0 + t / 4;
-        anc_s[t / 4][t % 4] = v < B ? a.anc[((int64_t)s * B + v) * 4 + t % 4] : 0ull;
+        anc_s[t / 4][t % 4] = v < B ? anc[((int64_t)s * B + v) * 4 + t % 4] : 0ull;
     }
     const int v_hi = min(B - 1, v0 + NV - 1);
     const int kend = P + v_hi + 1;  // ancestors of v have indices <= v
@@ -264,7 +266,7 @@ __host__ __device__ inline int attn_f32_blocks(int B, int G)
 
 template <int D> __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
 {
-    attn_f32_block<D>(a, blockIdx.x, blockIdx.y);
+    attn_f32_block<D>(a, a.anc, true, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ MFMA kernel --

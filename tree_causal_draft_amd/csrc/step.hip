@@ -168,11 +168,9 @@ __global__ void __launch_bounds__(256) step_phase2_f32(StepArgs sa, StepPlan sp)
         return;
     }
     b -= sp.nR;
-    AttnArgs a = sa.attn;
-    a.anc = sa.anc;
-    a.err = nullptr;
-    const int nvb = attn_f32_blocks(a.B, a.G);
-    attn_f32_block<D>(a, b % nvb, b / nvb);
+    // the mask role's rows; the argument checks ran in phase 1
+    const int nvb = attn_f32_blocks(sa.attn.B, sa.attn.G);
+    attn_f32_block<D>(sa.attn, sa.anc, false, b % nvb, b / nvb);
 }
 
 template <int D, int NB>
