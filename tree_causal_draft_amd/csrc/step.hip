@@ -72,14 +72,15 @@ template <int D, int NWR> struct StepLds {
 // kArgPrefetch: the arg-max role loads its next sub-chunk early, worth it in the scan
 // launch (three waves per SIMD) and not in the attention-sharing phase 1.
 // T: the logits' element type (uint16_t words of bf16, or float).
-template <int NW, bool kArgPrefetch, typename T = uint16_t>
+// kEnt: the top-W role may compute the row entropies (when asked for at run time).
+template <int NW, bool kArgPrefetch, typename T = uint16_t, bool kEnt = true>
 __device__ __forceinline__ void step_scan_roles(const StepArgs &sa, const StepPlan &sp, int b,
                                                 uint8_t *pool)
 {
     if (b < sp.nT) {
         const int wid = threadIdx.x >> 6;
         uint64_t *cand = reinterpret_cast<uint64_t *>(pool) + wid * (kWaveCap + 2 * JT_MAX_W);
-        topw_partial_wave<T, true>(
+        topw_partial_wave<T, true, kEnt>(
             static_cast<const T *>(sa.draft), sa.draft_stride, sa.S * sa.N, sa.V, sa.W,
             sp.tp.npiece, sp.tp.ppw, sp.tp.nlist, sa.tkeys, sa.tms, sa.tt, b * NW + wid, cand,
             cand + kWaveCap + JT_MAX_W);
@@ -125,10 +126,12 @@ __global__ void __launch_bounds__(256, 2) step_phase1_w4(StepArgs sa, StepPlan s
 constexpr int kScanLds = 4 * (kWaveCap + 2 * JT_MAX_W) * 8 > JT_MAX_NODES * 40
                              ? 4 * (kWaveCap + 2 * JT_MAX_W) * 8
                              : JT_MAX_NODES * 40;
+// Without entropies (kEnt = false) the kernel holds 125 VGPRs, four waves per SIMD.
+template <bool kEnt>
 __global__ void __launch_bounds__(256) step_scan_kernel(StepArgs sa, StepPlan sp)
 {
     __shared__ __attribute__((aligned(16))) uint8_t pool[kScanLds];
-    step_scan_roles<4, true>(sa, sp, blockIdx.x, pool);
+    step_scan_roles<4, true, uint16_t, kEnt>(sa, sp, blockIdx.x, pool);
 }
 
 // fp32 steps (the tiny configuration is fp32 end to end) have no split-KV pass, so the
@@ -335,7 +338,10 @@ static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st
         if (sp.ap.bal)  // the attention pass's balanced schedule
             hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, sa.attn, sp.ap, sa.aws);
         const unsigned gs = (unsigned)(sp.nT + sp.nG + sp.nM);
-        hipLaunchKernelGGL(step_scan_kernel, dim3(gs), dim3(256), 0, st, sa, sp);
+        if (sa.tt)
+            hipLaunchKernelGGL(step_scan_kernel<true>, dim3(gs), dim3(256), 0, st, sa, sp);
+        else
+            hipLaunchKernelGGL(step_scan_kernel<false>, dim3(gs), dim3(256), 0, st, sa, sp);
         AttnArgs a = sa.attn;
         a.anc = sa.anc;  // the mask role's rows
         a.parent = nullptr;

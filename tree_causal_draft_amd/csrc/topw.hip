@@ -225,7 +225,10 @@ __device__ __forceinline__ void count_greater(const uint64_t *keys, int n, const
 // Output per wave: its W best keys, descending, 0-padded, its (max, sum) pair and, when
 // ws_t is not null, the entropy sum T of its logits (relative to the same max).
 // `cand` holds kWaveCap + JT_MAX_W keys and `best` JT_MAX_W keys of this wave's LDS.
-template <typename T, bool kAligned>
+// kEnt = false compiles the entropy sums out (fewer registers: with them the fused scan
+// launch holds 131 VGPRs and three waves per SIMD, without them 125 and four); with
+// kEnt = true they run when ws_t is not null.
+template <typename T, bool kAligned, bool kEnt = true>
 __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, int64_t row_stride,
                                                   int rows, int V, int W, int npiece, int ppw,
                                                   int nlist, uint64_t *__restrict__ ws_keys,
@@ -234,7 +237,7 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
                                                   uint64_t *cand, uint64_t *best)
 {
     constexpr int E = Vec<T>::kElems;
-    const bool want_t = ws_t != nullptr;
+    const bool want_t = kEnt && ws_t != nullptr;
     const int lane = threadIdx.x & 63;
     if (gl >= rows * nlist)
         return;
@@ -420,18 +423,20 @@ __device__ __forceinline__ void topw_partial_wave(const T *__restrict__ logits, 
         ws_keys[(int64_t)gl * W + lane] = run;
 }
 
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kEnt>
 __global__ void __launch_bounds__(kTopwThreads)
 topw_partial_kernel(const T *__restrict__ logits, int64_t row_stride, int rows, int V, int W,
                     int npiece, int ppw, int nlist, uint64_t *__restrict__ ws_keys,
                     float2 *__restrict__ ws_ms, float *__restrict__ ws_t)
 {
-    __shared__ __attribute__((aligned(16))) uint64_t cand_all[4][kWaveCap + JT_MAX_W];
-    __shared__ uint64_t best_all[4][JT_MAX_W];
+    // per wave: kWaveCap + JT_MAX_W candidate keys, then JT_MAX_W list keys
+    constexpr int kSlice = kWaveCap + 2 * JT_MAX_W;
+    __shared__ __attribute__((aligned(16))) uint64_t pool[4 * kSlice];
     const int wid = threadIdx.x >> 6;
-    topw_partial_wave<T, kAligned>(logits, row_stride, rows, V, W, npiece, ppw, nlist, ws_keys,
-                                   ws_ms, ws_t, blockIdx.x * 4 + wid, cand_all[wid],
-                                   best_all[wid]);
+    uint64_t *cand = pool + wid * kSlice;
+    topw_partial_wave<T, kAligned, kEnt>(logits, row_stride, rows, V, W, npiece, ppw, nlist,
+                                         ws_keys, ws_ms, ws_t, blockIdx.x * 4 + wid, cand,
+                                         cand + kWaveCap + JT_MAX_W);
 }
 
 constexpr int kMergeCand = JT_MAX_W * JT_MAX_W;  // candidate keys a row merge can keep
@@ -667,26 +672,29 @@ jt_status launch_topw(const void *logits, int64_t row_stride, int rows, int V, i
     float *wt = row_entropy ? reinterpret_cast<float *>(tp) : nullptr;
     const dim3 grid((unsigned)((parts + 3) / 4)), block(kTopwThreads);
     const uintptr_t addr = reinterpret_cast<uintptr_t>(logits);
+    const bool ent = wt != nullptr;
+    auto go = [&](auto kern, const auto *x) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, x, row_stride, rows, V, W, p.npiece, p.ppw,
+                           p.nlist, wk, wm, wt);
+    };
     if (dtype == JT_BF16) {
+        const uint16_t *x = (const uint16_t *)logits;
         const bool al = (addr % 16 == 0) && (row_stride % 8 == 0);
         if (al)
-            hipLaunchKernelGGL((topw_partial_kernel<uint16_t, true>), grid, block, 0, st,
-                               (const uint16_t *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm, wt);
+            ent ? go(topw_partial_kernel<uint16_t, true, true>, x)
+                : go(topw_partial_kernel<uint16_t, true, false>, x);
         else
-            hipLaunchKernelGGL((topw_partial_kernel<uint16_t, false>), grid, block, 0, st,
-                               (const uint16_t *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm, wt);
+            ent ? go(topw_partial_kernel<uint16_t, false, true>, x)
+                : go(topw_partial_kernel<uint16_t, false, false>, x);
     } else {
+        const float *x = (const float *)logits;
         const bool al = (addr % 16 == 0) && (row_stride % 4 == 0);
         if (al)
-            hipLaunchKernelGGL((topw_partial_kernel<float, true>), grid, block, 0, st,
-                               (const float *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm, wt);
+            ent ? go(topw_partial_kernel<float, true, true>, x)
+                : go(topw_partial_kernel<float, true, false>, x);
         else
-            hipLaunchKernelGGL((topw_partial_kernel<float, false>), grid, block, 0, st,
-                               (const float *)logits, row_stride, rows, V, W, p.npiece, p.ppw,
-                               p.nlist, wk, wm, wt);
+            ent ? go(topw_partial_kernel<float, false, true>, x)
+                : go(topw_partial_kernel<float, false, false>, x);
     }
     jt_status e = launch_status(hipGetLastError());
     if (e != JT_OK)
