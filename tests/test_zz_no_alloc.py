@@ -1,9 +1,10 @@
 """GPU check of jt_draft_verify_step_noalloc (the fused step with the library's static
 device scratch) against jt_draft_verify_step (the same step with a caller's workspace).
 
-Three calls in a row with shrinking inputs -- ragged at a reduced vocabulary (four
-launches, balanced schedule), high_budget (three launches), then a small low_budget (two
-launches) -- so each call runs on scratch that holds the previous, larger call's contents.
+Four calls in a row with shrinking inputs -- ragged at a reduced vocabulary (four
+launches, balanced schedule), high_budget (three launches), a small low_budget (two
+launches), then the fp32 tiny step -- so each call runs on scratch that holds the previous,
+larger call's contents.
 Every output must equal the workspace call's bit for bit.  The call goes through the C
 ABI (ctypes) and allocates nothing: every output is passed in.
 """
@@ -34,15 +35,16 @@ def _run(st, fn, **extra):
 
 
 @pytest.mark.parametrize("cases", [(("ragged", dict(V=8192)), ("high_budget", {}),
-                                    ("low_budget", dict(V=20000, prefix=200)))])
+                                    ("low_budget", dict(V=20000, prefix=200)), ("tiny", {}))])
 def test_noalloc_equals_workspace_call(cases):
     need_gpu()
     for name, kw in cases:
         w = wl.make(name, 931, **kw)
         c = w.cfg
         st = DeviceStep(w, "cuda:0")
+        dt = jt.JT_F32 if c.dtype == "f32" else jt.JT_BF16
         need = jt.step_workspace_size(c.S, c.B, c.N, c.W, c.V, c.Hq, c.Hkv, c.d, w.max_prefix,
-                                      jt.JT_BF16, c.block_size if w.block_table is not None else 0)
+                                      dt, c.block_size if w.block_table is not None else 0)
         assert 0 < need <= jt.STATIC_SCRATCH_BYTES, (name, need)
         print(f"[noalloc] {name} {kw}: scratch {need / 2**20:.1f} MiB", flush=True)
         ref = _run(st, jt.draft_verify_step, workspace=st.step_ws)
