@@ -381,6 +381,13 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     return p;
 }
 
+// Rows a split-KV merge covers per unit: a row tile, or all G * B rows when they fill less
+// than one (the merge's threads cover only rows that exist).
+__host__ __device__ inline int attn_merge_rows(const AttnPlan &p, int G, int B)
+{
+    return p.rt < G * B ? p.rt : G * B;
+}
+
 static size_t attn_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Partial slots: (unit, chunk) in the chunked schedule; in the balanced one, unit u's
@@ -1508,7 +1515,7 @@ __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_unit = (int64_t)pl.rt * (D / 8);
+    const int64_t per_unit = (int64_t)attn_merge_rows(pl, a.G, a.B) * (D / 8);
     const int unit = (int)(t / per_unit);
     if (unit >= pl.units)
         return;
@@ -1551,11 +1558,13 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
     jt_status e = launch_status(hipGetLastError());
     if (e != JT_OK || (!p.bal && p.n_chunks == 1))
         return e;
-    const long threads = (long)p.units * p.rt * (D / 8);
+    const long threads = (long)p.units * attn_merge_rows(p, a.G, a.B) * (D / 8);
     const dim3 cgrid((unsigned)((threads + 255) / 256)), cblock(256);
-    // 16 chunks per round trip only where that makes it a single trip; wider batches cost
-    // more in registers (occupancy) and padded loads than the trips they save
-    if (!p.bal && p.n_chunks > 8 && p.n_chunks <= 16)
+    // 12 or 16 chunks per round trip only where that makes it a single trip; wider batches
+    // cost more in registers (occupancy) and padded loads than the trips they save
+    if (!p.bal && p.n_chunks > 8 && p.n_chunks <= 12)
+        hipLaunchKernelGGL((attn_combine_kernel<D, 12>), cgrid, cblock, 0, st, a, p, w);
+    else if (!p.bal && p.n_chunks > 12 && p.n_chunks <= 16)
         hipLaunchKernelGGL((attn_combine_kernel<D, 16>), cgrid, cblock, 0, st, a, p, w);
     else
         hipLaunchKernelGGL((attn_combine_kernel<D, 8>), cgrid, cblock, 0, st, a, p, w);

@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
     }
     b -= sp.nR;
     const int64_t t = (int64_t)b * 256 + threadIdx.x;
-    const int64_t per_unit = (int64_t)sp.ap.rt * (D / 8);
+    const int64_t per_unit = (int64_t)attn_merge_rows(sp.ap, sa.attn.G, sa.attn.B) * (D / 8);
     const int unit = (int)(t / per_unit);
     if (unit < sp.ap.units)
         attn_merge_unit<D, NB>(sa.attn, sp.ap, sa.aws, unit, (int)(t % per_unit), (int)per_unit);
@@ -282,7 +282,7 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
     sp.nG = rows_t * sp.gp.nchunk;
     sp.nM = S;
     sp.nC = sp.ap.bal || sp.ap.n_chunks > 1
-                ? (int)(((long)sp.ap.units * sp.ap.rt * (d / 8) + 255) / 256)
+                ? (int)(((long)sp.ap.units * attn_merge_rows(sp.ap, Hq / Hkv, B) * (d / 8) + 255) / 256)
                 : 0;
     sp.nR = (rows_d + kStepRowsPerBlock - 1) / kStepRowsPerBlock;
     sp.nW = S;
@@ -352,7 +352,9 @@ static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st
         hipLaunchKernelGGL((step_phase1_w4<D>), dim3(g1), dim3(256), 0, st, sa, sp);
     }
     const unsigned g2 = (unsigned)(sp.nC + sp.nR + sp.nW);
-    if (sp.ap.n_chunks > 8 && sp.ap.n_chunks <= 16)
+    if (sp.ap.n_chunks > 8 && sp.ap.n_chunks <= 12)
+        hipLaunchKernelGGL((step_phase2<D, 12>), dim3(g2), dim3(256), 0, st, sa, sp);
+    else if (sp.ap.n_chunks > 12 && sp.ap.n_chunks <= 16)
         hipLaunchKernelGGL((step_phase2<D, 16>), dim3(g2), dim3(256), 0, st, sa, sp);
     else
         hipLaunchKernelGGL((step_phase2<D, 8>), dim3(g2), dim3(256), 0, st, sa, sp);
