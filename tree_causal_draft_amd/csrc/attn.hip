@@ -793,11 +793,17 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
         reinterpret_cast<uint64_t(*)[32][5]>(lds + AttnLds<D, NWR>::ANC_OFF);
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wr = wid;  // the wave's 32-row block
+    const int wr = wid;  // the wave's share of the tile copies
     const int col = lane & 31, hh = lane >> 5;
 
     const int G = a.G, B = a.B, R = G * B;
     const int r0 = rt * pl.rt;
+    // Paired 4-wave mode: at most 64 rows (two waves' worth) and chunks of at most two
+    // tiles.  Waves 2 and 3 then take the rows of waves 0 and 1 over the chunk's second
+    // tile while waves 0 and 1 take the first, and the two halves are merged in LDS: no
+    // wave idles and the chunk costs one tile's time instead of two.
+    const bool paired = NWR == 4 && R - r0 <= 64 && !pl.bal && pl.ch > 0 && pl.ch <= 2 * 64;
+    const int wblk = paired ? (wid & 1) : wid;  // the wave's 32-row block
     const int v_hi = min(B - 1, (r0 + pl.rt - 1) / G);
 
     const uintptr_t kpre_a = reinterpret_cast<uintptr_t>(a.k_prefix);
@@ -894,7 +900,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
 
     // ---- rows of this wave: one 32-row block, lane holds row `col`; its Q^T fragments
     // stay in registers.  Loaded, like the speculative copies, before the prefix length.
-    const int wrow0 = r0 + wr * 32;
+    const int wrow0 = r0 + wblk * 32;
     const bool wave_has_rows = wrow0 < R;
     const int rr = wrow0 + col;
     const bool row_ok = rr < R;
@@ -1283,25 +1289,74 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
             issue_tile(kbeg, stage(0));
         if (1 < ntiles && !have_pro[1])
             issue_tile(kbeg + TILE, stage(1));
-        for (int j = 0; j < ntiles; ++j) {
-            const int k = j & 1;
-            const int kt = kbeg + j * TILE;
-            if (j == 0 && 1 < ntiles)
-                wait_vm<NOPS>();
-            else
-                wait_vm<0>();
+        if (paired) {
+            // ntiles <= 2: tile j goes to the waves 2j and 2j + 1
+            wait_vm<0>();
             barrier_keep_dma();
-            if (j >= 1 && j + 1 < ntiles)
-                issue_tile(kt + TILE, stage(k ^ 1));
-            if (wave_has_rows)
-                compute_tile(stage(k), stage(k) + TILEB, vis_window(kt));
+            const int j = wid >> 1;
+            if (wave_has_rows && j < ntiles)
+                compute_tile(stage(j), stage(j) + TILEB, vis_window(kbeg + j * TILE));
+            // merge: waves 2 and 3 leave (m, l, O) in LDS, beyond the epilogue staging of
+            // waves 0 and 1, register by register (64 lanes x 4 bytes per store)
+            // (16 bytes per lane per access: O as DB * 4 float4, then (m, l) as a float2)
+            constexpr int NQ = DB * 4 + 1;
+            constexpr int MOFF = (2 * 32 * (D * 2 + 16) + 255) / 256 * 256;
+            static_assert(MOFF + 2 * NQ * 1024 <= NST * BUFB, "merge area fits the stages");
+            float4 *mg = reinterpret_cast<float4 *>(L0 + MOFF) + (wid & 1) * NQ * 64 + lane;
+            __syncthreads();  // every wave has read its tile
+            if (wid >= 2 && wave_has_rows) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        mg[(db * 4 + q4) * 64] =
+                            make_float4(o_acc[db][4 * q4], o_acc[db][4 * q4 + 1],
+                                        o_acc[db][4 * q4 + 2], o_acc[db][4 * q4 + 3]);
+                mg[DB * 4 * 64] = make_float4(m_i, l_i, 0.f, 0.f);
+            }
+            __syncthreads();
+            if (wid < 2 && wave_has_rows) {
+                const float4 ml1 = mg[DB * 4 * 64];
+                const float m1 = ml1.x, l1 = ml1.y;
+                const float M = fmaxf(m_i, m1);
+                if (M != -INFINITY) {  // both -inf: nothing visible, keep (-inf, 0, 0)
+                    const float s0 = m_i == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_i - M);
+                    const float s1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+                    l_i = l_i * s0 + l1 * s1;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const float4 o1 = mg[(db * 4 + q4) * 64];
+                            o_acc[db][4 * q4] = o_acc[db][4 * q4] * s0 + o1.x * s1;
+                            o_acc[db][4 * q4 + 1] = o_acc[db][4 * q4 + 1] * s0 + o1.y * s1;
+                            o_acc[db][4 * q4 + 2] = o_acc[db][4 * q4 + 2] * s0 + o1.z * s1;
+                            o_acc[db][4 * q4 + 3] = o_acc[db][4 * q4 + 3] * s0 + o1.w * s1;
+                        }
+                    m_i = M;
+                }
+            }
+        } else {
+            for (int j = 0; j < ntiles; ++j) {
+                const int k = j & 1;
+                const int kt = kbeg + j * TILE;
+                if (j == 0 && 1 < ntiles)
+                    wait_vm<NOPS>();
+                else
+                    wait_vm<0>();
+                barrier_keep_dma();
+                if (j >= 1 && j + 1 < ntiles)
+                    issue_tile(kt + TILE, stage(k ^ 1));
+                if (wave_has_rows)
+                    compute_tile(stage(k), stage(k) + TILEB, vis_window(kt));
+            }
         }
     }
 
     // ---- epilogue: final output (one chunk), or a normalised bf16 partial plus (m, l)
     const float l = half_swap_add(l_i);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t slot0 = slot_tile * pl.rt + wr * 32;
+    const int64_t slot0 = slot_tile * pl.rt + wblk * 32;
     // The accumulator spreads one row over the registers of 16 lanes.  A row-major copy of
     // the wave's 32 rows in LDS (row pitch D*2 + 16 bytes, which staggers the banks) lets
     // every lane store 16 contiguous bytes of a row instead of 8-byte pieces of 32 rows.
@@ -1311,7 +1366,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
     __syncthreads();  // every wave has finished reading the tiles
     // stored only now: vmcnt counts stores too, so a store before wait_dma() would make it
     // wait for the store's completion (measured: about 2 us per workgroup)
-    if (wave_has_rows && row_ok && hh == 0) {
+    const bool writer = wave_has_rows && !(paired && wid >= 2);  // merged into waves 0, 1
+    if (writer && row_ok && hh == 0) {
         if (final) {
             if (a.lse)
                 a.lse[row_g] = l > 0.f ? (m_i + __log2f(l)) * kLn2 : -INFINITY;
@@ -1319,7 +1375,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
             ws.ml[slot0 + col] = make_float2(m_i, l);
         }
     }
-    if (wave_has_rows) {
+    if (writer) {
         uint8_t *ob = L0 + wid * 32 * OPITCH;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
