@@ -105,9 +105,15 @@ template <int D, int NWR>
 __device__ __forceinline__ void step_phase1_body(const StepArgs &sa, const StepPlan &sp)
 {
     __shared__ __attribute__((aligned(16))) uint8_t pool[StepLds<D, NWR>::BYTES];
+    // Workgroups are dispatched in id order: the top-W role first, then the attention,
+    // then the arg-max and mask roles.  The top-W and attention roles end last, so they
+    // start first (low_budget step: 14.37 us with the attention first, 14.07 us so;
+    // 14.37 us with every scan role before the attention).
     const int b = blockIdx.x;
-    if (b < sp.nA)
-        attn_main<D, NWR, true>(sa.attn, sp.ap, sa.aws, b, sp.nA, pool);
+    if (b < sp.nT)
+        step_scan_roles<NWR, false>(sa, sp, b, pool);
+    else if (b < sp.nT + sp.nA)
+        attn_main<D, NWR, true>(sa.attn, sp.ap, sa.aws, b - sp.nT, sp.nA, pool);
     else
         step_scan_roles<NWR, false>(sa, sp, b - sp.nA, pool);
 }
