@@ -4,7 +4,7 @@
 
 One step = jt_topw_per_depth (draft logits) -> jt_build_tree_mask -> jt_tree_attention
 -> jt_verify_greedy (target logits), all sequences, run as one jt_draft_verify_step
-call (the same four steps in two to four launches; bf16 or fp32).  The tree
+call (the same four steps in two or three launches; bf16 or fp32).  The tree
 (parent, tokens) is an input of the step, built by the seeded workload generator, and is
 not timed.  Inputs are resident in HBM before the timed region; step i reads input set
 i mod n, with n sets whose total exceeds twice the 256 MB last-level cache where memory

@@ -207,9 +207,10 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
  * share the second.  In fp32 the attention (vector ALU, no split-KV) joins the second
  * launch instead, after the mask.  When a KV group holds more than 128 query rows (G*B > 128), the
  * attention runs 256-row workgroups whose LDS leaves no room beside them, and the scans
- * and the mask take a launch of their own before it (three launches; a fourth, first, when
- * several sequences take the attention's balanced schedule, which spreads all sequences'
- * key tiles evenly over the workgroups whatever their prefix lengths).  In the two-launch
+ * and the mask take a launch of their own before it (three launches).  Several sequences
+ * with such workgroups take the attention's balanced schedule, which spreads all
+ * sequences' key tiles evenly over the workgroups whatever their prefix lengths; each
+ * workgroup finds its own share from the prefix lengths.  In the two-launch
  * form the attention builds the ancestor rows it needs from `parent` itself, so it does
  * not wait for the mask.  The integer outputs (ids, anc, depth, the accepted path, bonus,
  * arg-max) and the attention outputs equal bit for bit what the four separate calls

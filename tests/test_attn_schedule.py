@@ -3,10 +3,10 @@
 With several sequences and 8-wave workgroups the pass does not cut each sequence's keys
 into fixed chunks: the units' key tiles -- unit = (sequence, KV head, 256-row tile), in
 that order, each unit holding the tiles its rows can see -- form one run of T tiles, and
-workgroup w of n = min(nwg, T) takes tiles floor(w T / n) .. floor((w + 1) T / n) - 1.  A
-schedule kernel turns the device-side prefix lengths into tile offsets and, per workgroup,
-the unit and tile its share starts at; every workgroup writes one partial per unit it
-meets into slot unit + w; the merge finds a unit's pieces from the same offsets.  This
+workgroup w of n = min(nwg, T) takes tiles floor(w T / n) .. floor((w + 1) T / n) - 1.
+Every workgroup turns the device-side prefix lengths into tile offsets and finds the unit
+and tile its share starts at; it writes one partial per unit it meets into slot unit + w;
+the merge finds a unit's pieces from the same offsets (stored by workgroup 0).  This
 test restates that arithmetic in Python and checks the invariants the kernels rely on,
 over random shapes and prefix lengths:
   * every (unit, tile) is covered by exactly one workgroup, and every share is nonempty;
@@ -40,7 +40,7 @@ def plan_nwg(S, B, G, Hkv, max_prefix, block_size, rows_per_tile=256):
 
 
 def schedule(S, B, G, Hkv, Ps, nwg, nrt, rows_per_tile=256):
-    """The schedule kernel: tile offsets per sequence and each workgroup's start."""
+    """Tile offsets per sequence and each workgroup's start, as each workgroup finds them."""
     tab, c = [], 0
     for s in range(S):
         tab.append(c)
@@ -54,13 +54,10 @@ def schedule(S, B, G, Hkv, Ps, nwg, nrt, rows_per_tile=256):
             starts.append((-1, 0))
             continue
         a0 = w * T // nw
-        lo, hi = 0, S - 1            # the last sequence whose offset is <= a0
-        while lo < hi:
-            mid = (lo + hi + 1) >> 1
-            if tab[mid] <= a0:
-                lo = mid
-            else:
-                hi = mid - 1
+        # the sequence whose tile range holds a0 (ranges are nonempty and partition [0, T))
+        holders = [s for s in range(S) if tab[s] <= a0 < tab[s + 1]]
+        assert len(holders) == 1
+        lo = holders[0]
         rel = a0 - tab[lo]
         ts = (tab[lo + 1] - tab[lo]) // Hkv
         g = rel // ts

@@ -109,7 +109,7 @@ def test_bench_inputs_against_oracle(name):
 @pytest.mark.parametrize("name", ["ragged", "moe_verify"])
 def test_full_vocab_balanced_schedule(name):
     """ragged and moe_verify at full size (V = 151,936; moe_verify reads 622 MB of target
-    logits) through the four-launch balanced schedule, on the benchmark's inputs: equal to
+    logits) through the balanced-schedule path, on the benchmark's inputs: equal to
     the four calls bit for bit, and to the oracle on ids, acceptance and every row of one
     whole 256-row block of query rows per sequence."""
     w = wl.make(name, BENCH_SEED[name])

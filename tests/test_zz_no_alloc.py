@@ -1,7 +1,7 @@
 """GPU check of jt_draft_verify_step_noalloc (the fused step with the library's static
 device scratch) against jt_draft_verify_step (the same step with a caller's workspace).
 
-Four calls in a row with shrinking inputs -- ragged at a reduced vocabulary (four
+Four calls in a row with shrinking inputs -- ragged at a reduced vocabulary (three
 launches, balanced schedule), high_budget (three launches), a small low_budget (two
 launches), then the fp32 tiny step -- so each call runs on scratch that holds the previous,
 larger call's contents.

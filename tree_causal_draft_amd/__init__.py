@@ -308,7 +308,7 @@ def draft_verify_step(draft_logits, target_logits, parent, tokens, N, W, q, k_tr
                       logprob=None, row_lse=None, anc=None, depth=None, accept_len=None,
                       accept_path=None, bonus=None, argmax_out=None, err=None, workspace=None,
                       row_entropy=None, stream=None):
-    """The four steps in one call (two to four launches).  draft_logits [S*N, stride] and
+    """The four steps in one call (two or three launches).  draft_logits [S*N, stride] and
     target_logits [S*B, stride] bf16; the rest as for the separate calls.  Returns a dict
     of every output."""
     args, outs, need = _step_call(draft_logits, target_logits, parent, tokens, N, W, q, k_tree,

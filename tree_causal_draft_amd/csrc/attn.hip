@@ -294,10 +294,10 @@ struct AttnWs {
     float2 *ml;
     uint16_t *o;
     int32_t *sched;  // balanced schedule: S + 1 tile offsets of the sequences (last: total)
-    int2 *wstart;    // balanced schedule: per workgroup, its first unit and tile (-1: idle)
 };
 
-// Sequences the balanced schedule handles (its schedule kernel keeps them in LDS).
+// Sequences the balanced schedule handles (each attention workgroup keeps their tile
+// offsets in LDS while it finds its share).
 constexpr int kBalMaxS = 4096;
 
 // Key tiles of row tile rt of a sequence with prefix length P: the keys its rows can see.
@@ -405,14 +405,13 @@ static size_t attn_ws_bytes(const AttnPlan &p, int S, int d)
     const size_t slots = attn_ws_slots(p);
     size_t head = 0;
     if (p.bal)
-        head = attn_align256(((size_t)S + 1) * sizeof(int32_t)) +
-               attn_align256((size_t)p.nwg * sizeof(int2));
+        head = attn_align256(((size_t)S + 1) * sizeof(int32_t));
     return head + slots * sizeof(float2) + slots * (size_t)d * 2;
 }
 
 static AttnWs attn_ws_split(const AttnPlan &p, int S, void *ws)
 {
-    AttnWs w{nullptr, nullptr, nullptr, nullptr};
+    AttnWs w{nullptr, nullptr, nullptr};
     const size_t slots = attn_ws_slots(p);
     if (slots == 0 || !ws)
         return w;
@@ -420,8 +419,6 @@ static AttnWs attn_ws_split(const AttnPlan &p, int S, void *ws)
     if (p.bal) {
         w.sched = reinterpret_cast<int32_t *>(b);
         b += attn_align256(((size_t)S + 1) * sizeof(int32_t));
-        w.wstart = reinterpret_cast<int2 *>(b);
-        b += attn_align256((size_t)p.nwg * sizeof(int2));
     }
     w.ml = reinterpret_cast<float2 *>(b);
     w.o = reinterpret_cast<uint16_t *>(b + slots * sizeof(float2));
@@ -1432,21 +1429,109 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
                                  pl.n_chunks == 1, rt == 0 && chunk == 0 && g == 0, true, lds);
 }
 
+// Balanced schedule, found by every workgroup at its start from the device-side prefix
+// lengths (no launch of its own): per sequence its tile offset (each thread sums a run of
+// sequences; the runs' offsets come from a scan of the NT sums); the thread whose run
+// holds this workgroup's first tile then finds the unit and tile there (KV head and row
+// tile within the sequence).  Workgroup 0 also stores the offsets for the merge.  `tab`
+// (2 S + 3 + NT / 64 integers) lies in LDS that no copy has touched yet; the closing
+// barrier orders every read of it before the tile copies reuse that memory.  Returns the
+// total tile count T; u0 = -1 for an empty share (with fewer tiles than workgroups only the
+// first T take a share, of one tile each, so that the merge finds a piece from every
+// workgroup it spans).
+template <int NT>
+__device__ __forceinline__ int64_t attn_bal_start(const AttnArgs &a, const AttnPlan &pl,
+                                                  const AttnWs &ws, int w, int32_t *tab,
+                                                  int &u0, int &off0)
+{
+    constexpr int NWV = NT / kWave;
+    const int S = a.S, tid = threadIdx.x;
+    int32_t *pre = tab + S + 1;
+    int32_t *part = pre + S;
+    int32_t *found = part + NWV;
+    const int per = (S + NT - 1) / NT;
+    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
+    int sum = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int P = clamp_prefix(a, s);
+        pre[s] = P;
+        int r = 0;
+        for (int rt = 0; rt < pl.n_rtiles; ++rt)
+            r += attn_unit_tiles(P, rt, pl.rt, a.B, a.G);
+        tab[s] = a.Hkv * r;
+        sum += a.Hkv * r;
+    }
+    // exclusive scan of the run sums: inclusive within each wave, then the wave totals
+    const int lane = tid & 63, wid = tid >> 6;
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, kWave);
+        if (lane >= o)
+            inc += v;
+    }
+    if (lane == 63)
+        part[wid] = inc;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < NWV; ++k) {
+        base += k < wid ? part[k] : 0;
+        total += part[k];
+    }
+    const int64_t T = total;
+    const int64_t nw = min((int64_t)pl.nwg, T);
+    // the first tile of this workgroup's share (-1: an empty share)
+    const int64_t a0 = w < nw ? (int64_t)w * T / nw : -1;
+    int c = base + inc - sum;
+    for (int s = s0; s < s1; ++s) {
+        const int v = tab[s];  // every sequence has tiles: v >= Hkv
+        tab[s] = c;
+        if (a0 >= c && a0 < c + v) {
+            int rel = (int)(a0 - c);
+            const int ts = v / a.Hkv;  // tiles of one KV head
+            const int g = rel / ts;
+            rel -= g * ts;
+            int rt = 0;
+            for (; rt < pl.n_rtiles - 1; ++rt) {
+                const int t = attn_unit_tiles(pre[s], rt, pl.rt, a.B, a.G);
+                if (rel < t)
+                    break;
+                rel -= t;
+            }
+            found[0] = (s * a.Hkv + g) * pl.n_rtiles + rt;
+            found[1] = rel;
+        }
+        c += v;
+    }
+    if (tid == 0)
+        tab[S] = total;
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int s = tid; s <= S; s += NT)
+            ws.sched[s] = tab[s];
+    u0 = a0 >= 0 ? found[0] : -1;
+    off0 = a0 >= 0 ? found[1] : 0;
+    __syncthreads();
+    return T;
+}
+
 // Balanced schedule: the units' key tiles, in unit order, form one sequence of T tiles;
 // workgroup w < n = min(nwg, T) takes tiles floor(w T / n) .. floor((w + 1) T / n) - 1, one
-// piece per unit it meets, starting from the unit and tile the schedule kernel found.
+// piece per unit it meets, starting from the unit and tile attn_bal_start found.
 template <int D, int NWR>
 __device__ __forceinline__ void attn_main_bal(const AttnArgs &a, const AttnPlan &pl, const AttnWs &ws,
                                               int w, uint8_t *lds)
 {
-    const int2 st = ws.wstart[w];
-    if (st.x < 0)
+    static_assert((2 * kBalMaxS + 3 + NWR) * 4 <= AttnLds<D, NWR>::NST * AttnLds<D, NWR>::BUFB,
+                  "the schedule's offsets must fit the tile stages");
+    int u, off;
+    const int64_t T = attn_bal_start<64 * NWR>(a, pl, ws, w, reinterpret_cast<int32_t *>(lds), u, off);
+    if (u < 0)
         return;  // an empty share
-    const int64_t T = ws.sched[a.S];
     const int64_t nw = min((int64_t)pl.nwg, T);  // every share nonempty
     int64_t left = (int64_t)(w + 1) * T / nw - (int64_t)w * T / nw;
     const int per_seq = a.Hkv * pl.n_rtiles;
-    int u = st.x, off = st.y;
     int s = u / per_seq;
     int P = clamp_prefix(a, s);
     bool first = true;
@@ -1474,95 +1559,16 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR)  // 2 waves per SIMD: no AG
 attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[AttnLds<D, NWR>::BYTES];
-    if (pl.bal) {
-        // logical share w: XCD (blockIdx & 7) runs shares [x nwg/8, (x + 1) nwg/8)
-        const int b = blockIdx.x;
-        attn_main_bal<D, NWR>(a, pl, ws, pl.remap ? (b & 7) * (pl.nwg >> 3) + (b >> 3) : b, lds);
-    }
-    else
-        attn_main<D, NWR, false>(a, pl, ws, blockIdx.x, gridDim.x, lds);
-}
-
-// The balanced schedule, one workgroup of 256 threads: per sequence its tile offset (each
-// thread sums a run of sequences, the runs' offsets come from a scan of the 256 sums),
-// then per workgroup of the main pass the unit and tile its share starts at (a binary
-// search over the offsets, then the KV head and row tile within the sequence).
-__global__ void __launch_bounds__(256) attn_sched_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
-{
-    __shared__ int32_t tab[kBalMaxS + 1];
-    __shared__ int32_t pre[kBalMaxS];
-    __shared__ int32_t part[256];
-    const int tid = threadIdx.x, S = a.S;
-    const int per = (S + 255) / 256;
-    const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
-    int sum = 0;
-    for (int s = s0; s < s1; ++s) {
-        const int P = clamp_prefix(a, s);
-        pre[s] = P;
-        int r = 0;
-        for (int rt = 0; rt < pl.n_rtiles; ++rt)
-            r += attn_unit_tiles(P, rt, pl.rt, a.B, a.G);
-        tab[s] = a.Hkv * r;
-        sum += a.Hkv * r;
-    }
-    // exclusive scan of the 256 run sums: inclusive within each wave, then the wave totals
-    const int lane = tid & 63, wid = tid >> 6;
-    int inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(inc, o, kWave);
-        if (lane >= o)
-            inc += v;
-    }
-    if (lane == 63)
-        part[wid] = inc;
-    __syncthreads();
-    int base = 0;
-    for (int k = 0; k < wid; ++k)
-        base += part[k];
-    const int total = part[0] + part[1] + part[2] + part[3];
-    int c = base + inc - sum;
-    for (int s = s0; s < s1; ++s) {
-        const int v = tab[s];
-        tab[s] = c;
-        c += v;
-    }
-    if (tid == 0)
-        tab[S] = total;
-    __syncthreads();
-    for (int s = tid; s <= S; s += 256)
-        ws.sched[s] = tab[s];
-    // With fewer tiles than workgroups, only the first T take a share (of one tile each), so
-    // that no share is empty: the merge expects a piece from every workgroup it spans.
-    const int64_t T = total;
-    const int64_t nw = min((int64_t)pl.nwg, T);
-    for (int w = tid; w < pl.nwg; w += 256) {
-        int2 r = make_int2(-1, 0);
-        if (w < nw) {
-            const int64_t a0 = (int64_t)w * T / nw;
-            int lo = 0, hi = S - 1;  // the last sequence whose offset is <= a0
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (tab[mid] <= a0)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            int rel = (int)(a0 - tab[lo]);
-            const int ts = (tab[lo + 1] - tab[lo]) / a.Hkv;  // tiles of one KV head
-            const int g = rel / ts;
-            rel -= g * ts;
-            int rt = 0;
-            for (; rt < pl.n_rtiles - 1; ++rt) {
-                const int t = attn_unit_tiles(pre[lo], rt, pl.rt, a.B, a.G);
-                if (rel < t)
-                    break;
-                rel -= t;
-            }
-            r = make_int2((lo * a.Hkv + g) * pl.n_rtiles + rt, rel);
+    if constexpr (NWR == 8) {  // only 8-wave plans take the balanced schedule
+        if (pl.bal) {
+            // logical share w: XCD (blockIdx & 7) runs shares [x nwg/8, (x + 1) nwg/8)
+            const int b = blockIdx.x;
+            attn_main_bal<D, NWR>(a, pl, ws, pl.remap ? (b & 7) * (pl.nwg >> 3) + (b >> 3) : b,
+                                  lds);
+            return;
         }
-        ws.wstart[w] = r;
     }
+    attn_main<D, NWR, false>(a, pl, ws, blockIdx.x, gridDim.x, lds);
 }
 
 // Separate merge pass for large units: one thread per (unit, row, 8 output columns).
@@ -1601,12 +1607,6 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
     const AttnPlan p = attn_plan(a.S, a.B, a.Hq, a.Hkv, a.max_prefix,
                                  a.block_table ? a.block_size : 0, true);
     const AttnWs w = attn_ws_split(p, a.S, ws);
-    if (p.bal) {
-        hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, a, p, w);
-        jt_status e = launch_status(hipGetLastError());
-        if (e != JT_OK)
-            return e;
-    }
     if (p.nwr == 4)
         launch_main<D, 4>(a, p, w, st);
     else

@@ -1,7 +1,6 @@
 // The whole draft-and-verify step in two launches (jt_draft_verify_step); three for
-// shapes whose attention needs 8-wave workgroups (see step_scan_kernel), and then a
-// fourth, the attention's schedule kernel, when several sequences share the pass.  An fp32
-// step takes two launches with the attention in the second (see step_scan_f32_kernel).
+// shapes whose attention needs 8-wave workgroups (see step_scan_kernel).  An fp32 step
+// takes two launches with the attention in the second (see step_scan_f32_kernel).
 //
 // Each launch runs several steps side by side, one role per range of workgroup ids:
 //   phase 1  attention   the split-KV MFMA pass; its workgroups build the tree's ancestor
@@ -341,8 +340,6 @@ static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st
         return;
     }
     if (sp.ap.nwr == 8) {
-        if (sp.ap.bal)  // the attention pass's balanced schedule
-            hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, sa.attn, sp.ap, sa.aws);
         const unsigned gs = (unsigned)(sp.nT + sp.nG + sp.nM);
         if (sa.tt)
             hipLaunchKernelGGL(step_scan_kernel<true>, dim3(gs), dim3(256), 0, st, sa, sp);
