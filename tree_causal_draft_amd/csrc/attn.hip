@@ -466,21 +466,22 @@ __device__ __forceinline__ uint32_t lds_off(const void *p)
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
 
-// Four 16-byte LDS reads (ds_read_b128) at four row addresses plus one immediate offset
-// -- the K fragments of QK^T -- issued without a wait: they are in flight until an
-// lgkm_wait4 on them, so the reads of the next k-group overlap the current MFMAs.  Inline
-// asm for the same reason as the transposing reads below.
+// Four 16-byte LDS reads (ds_read_b128) -- K fragments of QK^T: two row addresses at two
+// immediate offsets, (a0, O0), (a1, O0), (a0, O1), (a1, O1), i.e. two k-steps of two
+// 32-key blocks -- issued without a wait: they are in flight until an lgkm_wait4 on them,
+// so the reads of the next k-group overlap the current MFMAs.  Inline asm for the same
+// reason as the transposing reads below.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-template <int OFF>
-__device__ __forceinline__ void k_issue4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                         u32x4_t &k0, u32x4_t &k1, u32x4_t &k2, u32x4_t &k3)
+template <int O0, int O1>
+__device__ __forceinline__ void k_issue2x2(uint32_t a0, uint32_t a1, u32x4_t &k0, u32x4_t &k1,
+                                           u32x4_t &k2, u32x4_t &k3)
 {
-    asm volatile("ds_read_b128 %0, %4 offset:%8\n\t"
-                 "ds_read_b128 %1, %5 offset:%8\n\t"
-                 "ds_read_b128 %2, %6 offset:%8\n\t"
-                 "ds_read_b128 %3, %7 offset:%8"
+    asm volatile("ds_read_b128 %0, %4 offset:%6\n\t"
+                 "ds_read_b128 %1, %5 offset:%6\n\t"
+                 "ds_read_b128 %2, %4 offset:%7\n\t"
+                 "ds_read_b128 %3, %5 offset:%7"
                  : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3)
-                 : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF));
+                 : "v"(a0), "v"(a1), "i"(O0), "i"(O1));
 }
 // Waits until at most N LDS operations are outstanding.  LDS reads complete in order, so
 // with N = the number of reads issued after these fragments they have arrived; naming
@@ -491,25 +492,27 @@ __device__ __forceinline__ void lgkm_wait4(u32x4_t &k0, u32x4_t &k1, u32x4_t &k2
     asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(k0), "+v"(k1), "+v"(k2), "+v"(k3) : "i"(N));
 }
 
-// Eight transposing LDS reads (ds_read_b64_tr_b16) from two row addresses at four row
-// offsets, issued without a wait (see k_issue4; lgkm_wait8 is the matching wait).  Inline
-// asm because the builtin's memory operand carries no LDS alias information, which makes
-// the compiler wait for every pending HBM->LDS copy (including the next tile's) before
-// the read.
-template <int O0, int O1, int O2, int O3>
-__device__ __forceinline__ void tr16_issue8(uint32_t aa, uint32_t ab, i32x2_t (&r)[8])
+// Eight transposing LDS reads (ds_read_b64_tr_b16) for two output blocks (row addresses
+// aa0/ab0 and aa1/ab1) at two row offsets -- block 0 at O0, O1, then block 1 at O0, O1 --
+// issued without a wait (see k_issue2x2; lgkm_wait8 is the matching wait).  Inline asm
+// because the builtin's memory operand carries no LDS alias information, which makes the
+// compiler wait for every pending HBM->LDS copy (including the next tile's) before the
+// read.
+template <int O0, int O1>
+__device__ __forceinline__ void tr16_issue2x2(uint32_t aa0, uint32_t ab0, uint32_t aa1,
+                                              uint32_t ab1, i32x2_t (&r)[8])
 {
-    asm volatile("ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
-                 "ds_read_b64_tr_b16 %1, %9 offset:%10\n\t"
-                 "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-                 "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
-                 "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
-                 "ds_read_b64_tr_b16 %5, %9 offset:%12\n\t"
-                 "ds_read_b64_tr_b16 %6, %8 offset:%13\n\t"
-                 "ds_read_b64_tr_b16 %7, %9 offset:%13"
+    asm volatile("ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+                 "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+                 "ds_read_b64_tr_b16 %2, %8 offset:%13\n\t"
+                 "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+                 "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+                 "ds_read_b64_tr_b16 %5, %11 offset:%12\n\t"
+                 "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+                 "ds_read_b64_tr_b16 %7, %11 offset:%13"
                  : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
                    "=&v"(r[6]), "=&v"(r[7])
-                 : "v"(aa), "v"(ab), "i"(O0), "i"(O1), "i"(O2), "i"(O3));
+                 : "v"(aa0), "v"(ab0), "v"(aa1), "v"(ab1), "i"(O0), "i"(O1));
 }
 template <int N> __device__ __forceinline__ void lgkm_wait8(i32x2_t (&r)[8])
 {
@@ -1077,19 +1080,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
         const uint32_t kbase =
             lds_off(kb) + opaque((uint32_t)(col * ROWB + (hh ^ (zs & 1)) * 16));
         const int zk = opaque(zs >> 1);
-        // k-groups of 4 MFMAs; the reads of group n+1 are in flight during group n's MFMAs
-        constexpr int NKG = 2 * (KS / 4);
+        // k-groups of 4 MFMAs: k-steps k2, k2 + 1 of both key blocks, so that the two
+        // accumulator chains alternate; the reads of group n+1 are in flight during group
+        // n's MFMAs
+        constexpr int NKG = KS / 2;
         u32x4_t kf[2][4];
         auto kissue = [&](int n, u32x4_t (&dst)[4]) {
-            const int k4 = (n % (KS / 4)) * 4;
-            const uint32_t a0 = kbase + (uint32_t)(((k4 + 0) ^ zk) * 32);
-            const uint32_t a1 = kbase + (uint32_t)(((k4 + 1) ^ zk) * 32);
-            const uint32_t a2 = kbase + (uint32_t)(((k4 + 2) ^ zk) * 32);
-            const uint32_t a3 = kbase + (uint32_t)(((k4 + 3) ^ zk) * 32);
-            if (n < KS / 4)
-                k_issue4<0>(a0, a1, a2, a3, dst[0], dst[1], dst[2], dst[3]);
-            else
-                k_issue4<32 * ROWB>(a0, a1, a2, a3, dst[0], dst[1], dst[2], dst[3]);
+            const uint32_t a0 = kbase + (uint32_t)(((2 * n) ^ zk) * 32);
+            const uint32_t a1 = kbase + (uint32_t)(((2 * n + 1) ^ zk) * 32);
+            k_issue2x2<0, 32 * ROWB>(a0, a1, dst[0], dst[1], dst[2], dst[3]);
         };
         kissue(0, kf[0]);
 #pragma unroll
@@ -1101,11 +1100,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
             } else {
                 lgkm_wait4<0>(cur[0], cur[1], cur[2], cur[3]);
             }
-            const int kbk = n / (KS / 4), k4 = (n % (KS / 4)) * 4;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, cur[q]), qf[k4 + q], sacc[kbk], 0, 0, 0);
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int kbk = 0; kbk < 2; ++kbk)
+                    sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, cur[2 * kbk + q]), qf[2 * n + q], sacc[kbk],
+                        0, 0, 0);
         }
     };
     auto softmax = [&](f32x16_t (&sacc)[2], uint64_t vis, bf16x8_t (&pf)[2][2]) {
@@ -1191,29 +1192,44 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, const AttnPlan &pl,
         const uint32_t basea = vbase + opaque((uint32_t)(rowa * ROWB + (xs ^ (za & 3)) * 16 + half));
         const uint32_t baseb = vbase + opaque((uint32_t)(rowb * ROWB + (xs ^ (zb & 3)) * 16 + half));
         const int zda = opaque(za >> 2), zdb = opaque(zb >> 2);
-        // the reads of output block db+1 are in flight during block db's MFMAs
+        // groups of 4 MFMAs: fragments f0, f0 + 1 (f = 2*kbk + m2) of output blocks db0 and
+        // db0 + 1, so that two accumulator chains alternate; the reads of group n+1 are in
+        // flight during group n's MFMAs
         i32x2_t vr[2][8];
-        auto vissue = [&](int db, i32x2_t (&dst)[8]) {
-            const uint32_t aa = basea + (uint32_t)((db ^ zda) * 64);
-            const uint32_t ab = baseb + (uint32_t)((db ^ zdb) * 64);
-            tr16_issue8<0, 16 * ROWB, 32 * ROWB, 48 * ROWB>(aa, ab, dst);
+        auto vissue = [&](int n, i32x2_t (&dst)[8]) {
+            const int db0 = (n >> 1) * 2;
+            const uint32_t aa0 = basea + (uint32_t)((db0 ^ zda) * 64);
+            const uint32_t ab0 = baseb + (uint32_t)((db0 ^ zdb) * 64);
+            const uint32_t aa1 = basea + (uint32_t)(((db0 + 1) ^ zda) * 64);
+            const uint32_t ab1 = baseb + (uint32_t)(((db0 + 1) ^ zdb) * 64);
+            if ((n & 1) == 0)
+                tr16_issue2x2<0, 16 * ROWB>(aa0, ab0, aa1, ab1, dst);
+            else
+                tr16_issue2x2<32 * ROWB, 48 * ROWB>(aa0, ab0, aa1, ab1, dst);
         };
+        constexpr int NVG = DB;  // (DB / 2 block pairs) x (2 fragment pairs)
+        static_assert(DB % 2 == 0, "output blocks in pairs");
         vissue(0, vr[0]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            i32x2_t (&r)[8] = vr[db & 1];
-            if (db + 1 < DB) {
-                vissue(db + 1, vr[(db + 1) & 1]);
+        for (int n = 0; n < NVG; ++n) {
+            i32x2_t (&r)[8] = vr[n & 1];
+            if (n + 1 < NVG) {
+                vissue(n + 1, vr[(n + 1) & 1]);
                 lgkm_wait8<8>(r);
             } else {
                 lgkm_wait8<0>(r);
             }
+            const int db0 = (n >> 1) * 2, f0 = (n & 1) * 2;
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {  // f = 2*kbk + m2
-                const bf16x8_t vf = __builtin_bit_cast(
-                    bf16x8_t, __builtin_shufflevector(r[2 * f], r[2 * f + 1], 0, 1, 2, 3));
-                o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[f >> 1][f & 1], o_acc[db], 0, 0, 0);
-            }
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int f = f0 + q;
+                    const bf16x8_t vf = __builtin_bit_cast(
+                        bf16x8_t, __builtin_shufflevector(r[4 * e + 2 * q], r[4 * e + 2 * q + 1], 0, 1, 2, 3));
+                    o_acc[db0 + e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        vf, pf[f >> 1][f & 1], o_acc[db0 + e], 0, 0, 0);
+                }
         }
     };
     auto compute_tile = [&](const uint8_t *kb, const uint8_t *vb, uint64_t vis) {
