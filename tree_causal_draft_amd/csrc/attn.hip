@@ -1592,7 +1592,14 @@ template <int D, int NB>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // With the chunked schedule's XCD placement, a unit's pieces were written on one XCD
+    // (in order: XCD x holds the x-th eighth of the units) and are still in its L2;
+    // workgroup b runs on XCD b mod 8, so the same placement of the merge reads them
+    // there.  (The balanced schedule's units differ in length, so that an eighth of them
+    // need not sit on one XCD.)
+    const int nb = (int)gridDim.x, b0 = (int)blockIdx.x;
+    const int b = pl.remap && !pl.bal && nb % 8 == 0 ? (b0 & 7) * (nb >> 3) + (b0 >> 3) : b0;
+    const int64_t t = (int64_t)b * 256 + threadIdx.x;
     const int64_t per_unit = (int64_t)attn_merge_rows(pl, a.G, a.B) * (D / 8);
     const int unit = (int)(t / per_unit);
     if (unit >= pl.units)

@@ -203,6 +203,14 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
         return;
     }
     b -= sp.nR;
+    // With the chunked schedule's XCD placement a unit's pieces were written on one XCD
+    // and are still in its L2: the x-th eighth of the units on XCD (x + o) mod 8, o = the
+    // attention role's first workgroup (0 in a launch of its own).  Merge workgroup i runs
+    // on XCD (i + nW + nR) mod 8 and takes the units of that XCD, so it reads them there.
+    if (sp.ap.remap && !sp.ap.bal && sp.nC % 8 == 0) {
+        const int o = sp.ap.nwr == 8 ? 0 : sp.nT;
+        b = ((((int)blockIdx.x) - o) & 7) * (sp.nC >> 3) + (b >> 3);
+    }
     const int64_t t = (int64_t)b * 256 + threadIdx.x;
     const int64_t per_unit = (int64_t)attn_merge_rows(sp.ap, sa.attn.G, sa.attn.B) * (D / 8);
     const int unit = (int)(t / per_unit);
