@@ -104,6 +104,19 @@ __device__ void attn_validate(const AttnArgs &a, int s)
 
 // ------------------------------------------------------------------ VALU kernel --
 
+// Workgroup barrier for LDS only, which does not drain the loads in flight:
+// __syncthreads() carries a workgroup fence, which the compiler implements with
+// s_waitcnt vmcnt(0) and would wait for the copies or prefetches of later tiles too.  A
+// wave waits for the global data it uses itself (vmcnt, or the compiler's own wait on the
+// registers); LDS accesses are drained (lgkmcnt(0)) so that LDS written before the barrier
+// is seen, and may be rewritten, after it.  The asm memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_dma()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // grid (ceil(B / NV), S * Hkv), 256 threads: one workgroup per block of NV = 16 / G nodes
 // (at least one) of one (sequence s, KV head g), i.e. kF32Rows = 16 query rows, node-major
 // (row r: node v0 + r / G, head g * G + r % G; rows past B or past NV * G stay idle).  Per
@@ -114,7 +127,9 @@ __device__ void attn_validate(const AttnArgs &a, int s)
 // (q is scaled by scale * log2 e when staged).
 constexpr int kF32Rows = 16;
 // anc: the ancestor rows to read; validate: run the argument checks (they write a.err).
-template <int D>
+// kPrefetch: issue the next tile's loads before the current tile is computed (measured:
+// the fused step's fp32 phase 2 gains, the standalone pass loses, so each takes its form).
+template <int D, bool kPrefetch>
 __device__ __forceinline__ void attn_f32_block(const AttnArgs &a, const uint64_t *anc, bool validate,
                                                int bx, int by)
 {
@@ -169,23 +184,48 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs &a, const uint64_t
     for (int j = 0; j < NO; ++j)
         acc[j] = 0.f;
 
-    for (int kt = 0; kt < kend; kt += 64) {
-        __syncthreads();  // the previous tile's reads are done
-        for (int i = t; i < 64 * (D / 4); i += 256) {
+    // A tile's K and V go through registers into LDS.  With kPrefetch the next tile's
+    // loads are issued before the current tile is computed, so one HBM round trip overlaps
+    // the compute (the pass is latency-bound: a few workgroups, each a short run of tiles).
+    constexpr int NL = 64 * (D / 4) / 256;  // float4 loads of K (and of V) per thread
+    static_assert(NL * 256 == 64 * (D / 4), "tile split");
+    float4 kx[NL], vx[NL];
+    bool kok[NL];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int q = 0; q < NL; ++q) {
+            const int i = t + 256 * q;
             const int kk = i / (D / 4), c4 = i % (D / 4);
             const int j = kt + kk;
             const int64_t off = j < kend ? kv_offset(a, s, g, P, j) : -1;
-            float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+            kx[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            vx[q] = kx[q];
+            kok[q] = off >= 0;
             if (off >= 0) {
-                kx = *reinterpret_cast<const float4 *>((j < P ? kp : ktr) + off + 4 * c4);
-                vx = *reinterpret_cast<const float4 *>((j < P ? vp : vtr) + off + 4 * c4);
+                kx[q] = *reinterpret_cast<const float4 *>((j < P ? kp : ktr) + off + 4 * c4);
+                vx[q] = *reinterpret_cast<const float4 *>((j < P ? vp : vtr) + off + 4 * c4);
             }
-            *reinterpret_cast<float4 *>(&ks[kk][4 * c4]) = kx;
-            *reinterpret_cast<float4 *>(&vs[kk][4 * c4]) = vx;
-            if (c4 == 0)
-                kval[kk] = off >= 0;
         }
-        __syncthreads();
+    };
+    if (kPrefetch && kend > 0)
+        load_tile(0);
+    for (int kt = 0; kt < kend; kt += 64) {
+        // LDS-only barriers inside the loop, so that a prefetch stays in flight
+        barrier_keep_dma();  // the previous tile's reads are done (first: q rows staged)
+        if (!kPrefetch)
+            load_tile(kt);
+#pragma unroll
+        for (int q = 0; q < NL; ++q) {
+            const int i = t + 256 * q;
+            const int kk = i / (D / 4), c4 = i % (D / 4);
+            *reinterpret_cast<float4 *>(&ks[kk][4 * c4]) = kx[q];
+            *reinterpret_cast<float4 *>(&vs[kk][4 * c4]) = vx[q];
+            if (c4 == 0)
+                kval[kk] = kok[q];
+        }
+        barrier_keep_dma();
+        if (kPrefetch && kt + 64 < kend)
+            load_tile(kt + 64);
         // scores of key kt + lane for rows wid + 4i
         const int j = kt + lane;
         float sc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -222,7 +262,7 @@ __device__ __forceinline__ void attn_f32_block(const AttnArgs &a, const uint64_t
             if (lane == 0)
                 alpha_s[r] = al;
         }
-        __syncthreads();
+        barrier_keep_dma();
         const int nk = min(64, kend - kt);
 #pragma unroll
         for (int jo = 0; jo < NO; ++jo)
@@ -266,7 +306,7 @@ __host__ __device__ inline int attn_f32_blocks(int B, int G)
 
 template <int D> __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a)
 {
-    attn_f32_block<D>(a, a.anc, true, blockIdx.x, blockIdx.y);
+    attn_f32_block<D, false>(a, a.anc, true, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ MFMA kernel --
@@ -650,17 +690,6 @@ template <int N> __device__ __forceinline__ void wait_vm_asm()
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Workgroup barrier that does not drain the DMA pipeline: __syncthreads() carries a
-// workgroup fence, which the compiler implements with s_waitcnt vmcnt(0) and would wait
-// for the copies of later tiles too.  Each wave has already waited for its share of
-// the current tile (vmcnt) before this point; LDS reads are drained (lgkmcnt(0)) so a
-// buffer may be refilled after the barrier.  The asm memory clobber keeps the compiler
-// from moving memory accesses across it.
-__device__ __forceinline__ void barrier_keep_dma()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-}
 
 
 // LDS accesses of the in-kernel ancestor rows, as inline asm for the same reason as the

@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256) step_phase2_f32(StepArgs sa, StepPlan sp)
     b -= sp.nR;
     // the mask role's rows; the argument checks ran in phase 1
     const int nvb = attn_f32_blocks(sa.attn.B, sa.attn.G);
-    attn_f32_block<D>(sa.attn, sa.anc, false, b % nvb, b / nvb);
+    attn_f32_block<D, true>(sa.attn, sa.anc, false, b % nvb, b / nvb);
 }
 
 template <int D, int NB>
