@@ -668,7 +668,7 @@ def main():
 
     def timing(r):
         return ("hipGraph of K jt_draft_verify_step calls (step i on cold input set i mod n; "
-                "two to four kernel launches each); median of the replays")
+                "two or three kernel launches each); median of the replays")
 
     prim = results[0]
     us = prim["step_us"]
