@@ -4,7 +4,9 @@ The fused call must reproduce, bit for bit, every integer and attention output o
 four separate calls on the same inputs (those are held to the oracle by the other GPU
 tests), and its err must be the OR of their flags.  Log-probs and row LSE agree to the
 log-prob tolerance: the step may cut a row into pieces differently, so its sums add in
-another order.  The benchmark's own inputs (every configuration at full size) are also compared with the
+another order.  So may the attention of one bf16 sequence with more than 128 rows per KV
+head: the step runs it beside the logit scans on fewer workgroups, with longer key
+chunks, so there its outputs agree to the bf16 attention bounds.  The benchmark's own inputs (every configuration at full size) are also compared with the
 oracle directly.  Attention outputs of
 a sequence with a bad parent array are unspecified and are not compared.
 """
@@ -50,9 +52,16 @@ def _compare(w, what, tamper=None):
     torch.cuda.synchronize()
     assert torch.equal(st.err_step, err_sep), (what, host(st.err_step), host(err_sep))
     bad_parent = (err_sep & 1) != 0
+    own_split = c.dtype == "bf16" and c.S == 1 and (c.Hq // c.Hkv) * c.B > 128
     for k in OUTS:
         if k in SUMS:
             assert_lp_close(host(getattr(st, k)), host(sep[k]), f"{what} {k}")
+            continue
+        if k in ATTN and own_split and not bool(bad_parent.any()):
+            if k == "attn_out":
+                assert_attention_close(host(st.attn_out), host(sep[k]), c.dtype, f"{what} {k}")
+            else:
+                assert_lse_close(host(st.lse), host(sep[k]), c.dtype, f"{what} {k}")
             continue
         a, b = _bits(getattr(st, k)), _bits(sep[k])
         if k in ATTN and bool(bad_parent.any()):

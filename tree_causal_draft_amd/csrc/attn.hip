@@ -350,8 +350,12 @@ __host__ __device__ inline int attn_unit_tiles(int P, int rt, int rtrows, int B,
 // allow_bal: several sequences with 8-wave workgroups take the balanced schedule, whose
 // key ranges follow the prefix lengths on the device.  (The fused step's 4-wave phase-1
 // attention keeps chunks; both entry points plan alike, so their outputs stay bit-equal.)
+// w4_target > 0: 4-wave workgroups whatever the row count (several 128-row tiles per KV
+// head), in chunks sized for about w4_target workgroups: the fused step's plan for one
+// sequence with many rows, whose attention then shares its launch and its CUs with the
+// logit scans (two workgroups per CU).
 static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int block_size,
-                          bool allow_bal = false)
+                          bool allow_bal = false, int w4_target = 0)
 {
     AttnPlan p;
     p.bal = 0;
@@ -361,7 +365,9 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     // LDS allows one wave per SIMD), and it then keeps the O accumulators in AGPRs and
     // copies all 64 to VGPRs and back around every tile (measured 15.9 us against 15.0 us
     // with 4 waves, two of them idle, on the 16-node, 1024-key shape).
-    p.nwr = rows <= 128 ? 4 : 8;
+    p.nwr = rows <= 128 || w4_target > 0 ? 4 : 8;
+    if (w4_target > 0)
+        allow_bal = false;
     p.rt = 32 * p.nwr;
     p.n_rtiles = (rows + p.rt - 1) / p.rt;
     p.units = S * Hkv * p.n_rtiles;
@@ -400,7 +406,7 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     // fewer, longer chunks cost less in the split-KV merge than they add to the pass
     // (measured on the 16-node, 1024-key shape: 17 one-tile chunks per unit 17.5 us,
     // 9 two-tile chunks 15.8 us), and they leave CUs to the logit scans of the fused step.
-    const int target = p.nwr == 8 ? 256 : 128;
+    const int target = w4_target > 0 ? w4_target : (p.nwr == 8 ? 256 : 128);
     int want = (target + p.units - 1) / p.units;
     if (want > maxc)
         want = maxc;
