@@ -427,6 +427,24 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     return p;
 }
 
+// The plan of the attention entry points.  One sequence with more than 128 rows per KV
+// head takes 4-wave workgroups over 128-row tiles, in chunks for about `w4` workgroups,
+// instead of the 8-wave pass: the fixed costs of its short items (startup, epilogue,
+// merge) weigh more than the 8-wave loop saves.  Measured on high_budget (one box): the
+// attention call alone, over inputs beyond the Infinity Cache, 27.98 us with 8 waves and
+// 24.64 us with w4 = 256 (24.83 us at 512); over inputs it holds, 23.87 and 23.61 us.
+// The fused step runs the same form in phase 1, beside its logit scans (one launch
+// instead of two), with w4 = 192: 47.2 us per step with the 8-wave pass, 39.7 us so
+// (40.6 us at 256, 43.3 us at 384).
+static AttnPlan attn_plan_call(int S, int B, int Hq, int Hkv, int max_prefix, int block_size,
+                               int w4 = 256)
+{
+    AttnPlan p = attn_plan(S, B, Hq, Hkv, max_prefix, block_size, true);
+    if (p.nwr == 8 && !p.bal)
+        p = attn_plan(S, B, Hq, Hkv, max_prefix, block_size, false, w4);
+    return p;
+}
+
 // Rows a split-KV merge covers per unit: a row tile, or all G * B rows when they fill less
 // than one (the merge's threads cover only rows that exist).
 __host__ __device__ inline int attn_merge_rows(const AttnPlan &p, int G, int B)
@@ -1649,7 +1667,7 @@ size_t attention_workspace(int S, int B, int Hq, int Hkv, int d, int max_prefix,
 {
     if (dtype != JT_BF16)
         return 0;
-    return attn_ws_bytes(attn_plan(S, B, Hq, Hkv, max_prefix, block_size, true), S, d);
+    return attn_ws_bytes(attn_plan_call(S, B, Hq, Hkv, max_prefix, block_size), S, d);
 }
 
 template <int D, int NWR>
@@ -1662,8 +1680,8 @@ static void launch_main(const AttnArgs &a, const AttnPlan &p, const AttnWs &w, h
 template <int D>
 static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
 {
-    const AttnPlan p = attn_plan(a.S, a.B, a.Hq, a.Hkv, a.max_prefix,
-                                 a.block_table ? a.block_size : 0, true);
+    const AttnPlan p = attn_plan_call(a.S, a.B, a.Hq, a.Hkv, a.max_prefix,
+                                      a.block_table ? a.block_size : 0);
     const AttnWs w = attn_ws_split(p, a.S, ws);
     if (p.nwr == 4)
         launch_main<D, 4>(a, p, w, st);

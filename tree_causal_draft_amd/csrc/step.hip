@@ -249,17 +249,14 @@ static StepPlan step_plan(int S, int B, int N, int V, int Hq, int Hkv, int d, in
         sp.nW = S;
         return sp;
     }
-    sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size, true);
-    if (sp.ap.nwr == 8 && !sp.ap.bal) {
-        // One sequence with more than 128 rows per KV head: rather than the 8-wave pass in
-        // a launch between the scans and phase 2, 4-wave workgroups over 128-row tiles run
-        // in phase 1 beside the scans.  (high_budget step, one box: 47.2 us in three
-        // launches, 39.3 us so; 40.6 us with 256 attention workgroups, 43.3 us with 384.
-        // Keeping the 8-wave pass and giving the scans 8-wave workgroups on the CUs it
-        // leaves free measured 50.7-53.6 us: one scan workgroup per CU hides too little
-        // latency.)
-        sp.ap = attn_plan(S, B, Hq, Hkv, max_prefix, block_size, false, kStepAttnW4);
-    }
+    // One sequence with more than 128 rows per KV head: 4-wave attention workgroups over
+    // 128-row tiles in phase 1, beside the scans, rather than the 8-wave pass in a launch
+    // between the scans and phase 2.  (Keeping the 8-wave pass and giving the scans 8-wave
+    // workgroups on the CUs it leaves free measured 50.7-53.6 us per high_budget step,
+    // against 47.2 us in three launches: one scan workgroup per CU hides too little
+    // latency.)  The chunks aim at fewer workgroups than the standalone call's, leaving
+    // slots to the scans, so the two split keys differently.
+    sp.ap = attn_plan_call(S, B, Hq, Hkv, max_prefix, block_size, kStepAttnW4);
     const bool split = sp.ap.nwr == 8;  // scans in a launch of their own
     const int nw = split ? 4 : sp.ap.nwr;  // waves per scan workgroup
     if (split) {
