@@ -129,8 +129,8 @@ def test_noalloc_step_rejects_shapes_beyond_its_scratch():
             fake, V, fake, V, V, 8, fake, fake, S, 64, 8, fake, fake, fake, fake, fake, None,
             0, 16, 0, fake, P, 32, 4, 128, ctypes.c_float(0.0), 1, fake, fake, fake, None, fake,
             fake, fake, fake, fake, fake, fake, fake, fake, None)
-    big = jt.step_workspace_size(64, 64, 8, 8, 151936, 32, 4, 128, 4096, 1)
+    big = jt.step_workspace_size(128, 64, 8, 8, 151936, 32, 4, 128, 4096, 1)
     assert big > jt.STATIC_SCRATCH_BYTES
-    assert call(64, 4096) == 7
+    assert call(128, 4096) == 7
     assert call(0, 4096) == 0          # nothing to do
-    assert call(64, 4096, V=0) == 2    # shape errors come first
+    assert call(128, 4096, V=0) == 2   # shape errors come first

@@ -351,9 +351,9 @@ __host__ __device__ inline int attn_unit_tiles(int P, int rt, int rtrows, int B,
 // key ranges follow the prefix lengths on the device.  (The fused step's 4-wave phase-1
 // attention keeps chunks; both entry points plan alike, so their outputs stay bit-equal.)
 // w4_target > 0: 4-wave workgroups whatever the row count (several 128-row tiles per KV
-// head), in chunks sized for about w4_target workgroups: the fused step's plan for one
-// sequence with many rows, whose attention then shares its launch and its CUs with the
-// logit scans (two workgroups per CU).
+// head), in chunks sized for about w4_target workgroups: the plan for one sequence with
+// many rows (the fused step's attention then shares its launch and its CUs with the logit
+// scans, two workgroups per CU).
 static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int block_size,
                           bool allow_bal = false, int w4_target = 0)
 {
@@ -1576,7 +1576,8 @@ __device__ __forceinline__ int64_t attn_bal_start(const AttnArgs &a, const AttnP
     if (tid == 0)
         tab[S] = total;
     __syncthreads();
-    if (blockIdx.x == 0)
+    // share 0, whichever workgroup runs it, stores the offsets for the merge
+    if (w == 0)
         for (int s = tid; s <= S; s += NT)
             ws.sched[s] = tab[s];
     u0 = a0 >= 0 ? found[0] : -1;
