@@ -205,18 +205,21 @@ jt_status jt_verify_greedy(const void *target_logits, int64_t row_stride, int32_
  * scans (top-W partials, target arg-max partials), the mask and the attention's main pass
  * share the first launch; the split-KV merge, the top-W merge and the verification walk
  * share the second.  In fp32 the attention (vector ALU, no split-KV) joins the second
- * launch instead, after the mask.  When a KV group holds more than 128 query rows (G*B > 128), the
- * attention runs 256-row workgroups whose LDS leaves no room beside them, and the scans
- * and the mask take a launch of their own before it (three launches).  Several sequences
- * with such workgroups take the attention's balanced schedule, which spreads all
- * sequences' key tiles evenly over the workgroups whatever their prefix lengths; each
- * workgroup finds its own share from the prefix lengths.  In the two-launch
- * form the attention builds the ancestor rows it needs from `parent` itself, so it does
- * not wait for the mask.  The integer outputs (ids, anc, depth, the accepted path, bonus,
- * arg-max) and the attention outputs equal bit for bit what the four separate calls
- * produce; logprob, row_lse and row_entropy agree to float rounding, because the step
- * may cut a logit row into pieces differently from jt_topw_per_depth (the sums then add
- * in another order).  `err` (int32 [S], optional) receives the OR of the flags the mask,
+ * launch instead, after the mask.  When a KV group holds more than 128 query rows (G*B > 128)
+ * in several sequences, the attention runs 256-row workgroups whose LDS leaves no room
+ * beside them, and the scans and the mask take a launch of their own before it (three
+ * launches); those sequences take the attention's balanced schedule, which spreads all
+ * sequences' key tiles evenly over the workgroups whatever their prefix lengths (each
+ * workgroup finds its own share from the prefix lengths).  A single such sequence keeps
+ * two launches: its attention runs 128-row workgroups in the first, beside the scans, in
+ * fewer and longer key chunks than jt_tree_attention uses.  In the two-launch form the
+ * attention builds the ancestor rows it needs from `parent` itself, so it does not wait
+ * for the mask.  The integer outputs (ids, anc, depth, the accepted path, bonus, arg-max)
+ * and the attention outputs equal bit for bit what the four separate calls produce,
+ * except that single sequence's attention outputs, whose other key split makes them agree
+ * to bf16 rounding; logprob, row_lse and row_entropy agree to float rounding, because the
+ * step may cut a logit row into pieces differently from jt_topw_per_depth (the sums then
+ * add in another order).  `err` (int32 [S], optional) receives the OR of the flags the mask,
  * attention and verification calls would report.
  *
  *   draft_logits   [S*N, draft_row_stride]   target_logits [S*B, target_row_stride]
