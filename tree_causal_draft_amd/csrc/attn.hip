@@ -1693,10 +1693,12 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
         return e;
     const long threads = (long)p.units * attn_merge_rows(p, a.G, a.B) * (D / 8);
     const dim3 cgrid((unsigned)((threads + 255) / 256)), cblock(256);
-    // 9, 12 or 16 chunks per round trip only where that makes it a single trip; wider
+    // 4, 9, 12 or 16 chunks per round trip only where that makes it a single trip; wider
     // batches cost more in registers (occupancy) and padded loads than the trips they save
     // (a batch of 12 for 9 chunks: 15.0 us per low_budget step against 14.75 with 9)
-    if (!p.bal && p.n_chunks == 9)
+    if (!p.bal && p.n_chunks <= 4)  // one sequence of many rows (128-row workgroups)
+        hipLaunchKernelGGL((attn_combine_kernel<D, 4>), cgrid, cblock, 0, st, a, p, w);
+    else if (!p.bal && p.n_chunks == 9)
         hipLaunchKernelGGL((attn_combine_kernel<D, 9>), cgrid, cblock, 0, st, a, p, w);
     else if (!p.bal && p.n_chunks > 9 && p.n_chunks <= 12)
         hipLaunchKernelGGL((attn_combine_kernel<D, 12>), cgrid, cblock, 0, st, a, p, w);

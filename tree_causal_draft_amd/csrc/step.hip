@@ -371,7 +371,9 @@ static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st
         hipLaunchKernelGGL((step_phase1_w4<D>), dim3(g1), dim3(256), 0, st, sa, sp);
     }
     const unsigned g2 = (unsigned)(sp.nC + sp.nR + sp.nW);
-    if (sp.ap.n_chunks == 9)  // 1024-key prefixes in two-tile chunks
+    if (!sp.ap.bal && sp.ap.n_chunks <= 4)  // one sequence of many rows
+        hipLaunchKernelGGL((step_phase2<D, 4>), dim3(g2), dim3(256), 0, st, sa, sp);
+    else if (sp.ap.n_chunks == 9)  // 1024-key prefixes in two-tile chunks
         hipLaunchKernelGGL((step_phase2<D, 9>), dim3(g2), dim3(256), 0, st, sa, sp);
     else if (sp.ap.n_chunks > 9 && sp.ap.n_chunks <= 12)
         hipLaunchKernelGGL((step_phase2<D, 12>), dim3(g2), dim3(256), 0, st, sa, sp);
