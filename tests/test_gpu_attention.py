@@ -79,6 +79,18 @@ def test_bf16_edge_shapes(B, P):
     _check(w, f"edge B={B} P={P}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("paged", [False, True])
+def test_bf16_one_sequence_many_rows(d, paged):
+    """One sequence with more than 128 rows per KV head: 4-wave workgroups over several
+    128-row tiles (the last one 16 rows, paired where its chunks are short) and split-KV
+    over a prefix that ends inside a tile; paged with the chunk's block-table entries staged
+    in LDS."""
+    w = wl.make("ragged", 425 + d + int(paged), parts=("attn",), qk_std=1.0,
+                **_small(S=1, B=100, prefix=1000, d=d, paged=paged, N=9, W=4))
+    _check(w, f"one sequence, many rows, d={d} paged={paged}")
+
+
 @pytest.mark.parametrize("tree", ["chain", "star"])
 def test_bf16_chain_and_star(tree):
     B = 200

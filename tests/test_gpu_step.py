@@ -154,7 +154,7 @@ def test_other_configs_small_vocab(name):
     dict(S=3, B=1, N=1, W=2, prefix=70),                      # root only, tiny prefix
     dict(S=2, B=37, N=5, W=3, prefix=0),                      # no prefix at all
     dict(S=2, B=256, N=16, W=16, prefix=200, V=5000),         # widest W, ragged vocab tail
-    dict(S=1, B=100, N=9, W=4, prefix=333, d=64),             # head dim 64, 8-wave groups
+    dict(S=1, B=100, N=9, W=4, prefix=333, d=64),             # head dim 64, 128-row tiles
     dict(S=5, B=20, N=6, W=5, prefix=129, Hq=24, Hkv=3),      # G = 8
 ])
 def test_shapes(kw):
@@ -162,6 +162,16 @@ def test_shapes(kw):
     V = kw.pop("V", 4096)
     w = wl.make("low_budget", 813, tree="random", V=V, **kw)
     _compare(w, f"shape {kw}")
+
+
+def test_one_sequence_paged():
+    """One paged sequence with more than 128 rows per KV head: the step's 4-wave attention
+    runs beside the scans in its own key split, each chunk staging its block-table
+    entries."""
+    w = wl.make("ragged", 816, S=1, B=150, N=8, W=4, prefix=700, V=4096, tree="random")
+    st, err = _compare(w, "one paged sequence")
+    assert int(err.abs().sum()) == 0
+    _against_oracle(w, st)
 
 
 def test_flags_bad_parent_nan_bad_block():
