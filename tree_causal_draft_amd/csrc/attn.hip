@@ -429,13 +429,12 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
 
 // The plan of the attention entry points.  One sequence with more than 128 rows per KV
 // head takes 4-wave workgroups over 128-row tiles, in chunks for about `w4` workgroups,
-// instead of the 8-wave pass: the fixed costs of its short items (startup, epilogue,
-// merge) weigh more than the 8-wave loop saves.  Measured on high_budget (one box): the
-// attention call alone, over inputs beyond the Infinity Cache, 27.98 us with 8 waves and
-// 24.64 us with w4 = 256 (24.83 us at 512); over inputs it holds, 23.87 and 23.61 us.
-// The fused step runs the same form in phase 1, beside its logit scans (one launch
-// instead of two), with w4 = 192: 47.2 us per step with the 8-wave pass, 39.7 us so
-// (40.6 us at 256, 43.3 us at 384).
+// instead of the 8-wave pass.  Measured on high_budget (one box, two runs each, the
+// attention call alone): over inputs beyond the Infinity Cache 24.83 us with 8 waves and
+// 24.15 us with w4 = 256; over inputs it holds, 23.90 and 23.10 us.  The fused step runs
+// the same form in phase 1, beside its logit scans (one launch instead of two), with
+// w4 = 192: 47.2 us per step with the 8-wave pass, 39.7 us so (40.6 us at 256, 43.3 us
+// at 384).
 static AttnPlan attn_plan_call(int S, int B, int Hq, int Hkv, int max_prefix, int block_size,
                                int w4 = 256)
 {
