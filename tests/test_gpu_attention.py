@@ -91,6 +91,40 @@ def test_bf16_one_sequence_many_rows(d, paged):
     _check(w, f"one sequence, many rows, d={d} paged={paged}")
 
 
+def _min_depth(B, W):
+    """The least depth limit at which a tree of at most W children per node holds B nodes."""
+    n, cap, level = 0, 1, 1
+    while cap < B:
+        level *= W
+        cap += level
+        n += 1
+    return n
+
+
+def _one_sequence_shape(seed):
+    """A seeded single-sequence shape with more than 128 rows per KV head."""
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(128 // G + 1, 257))
+    W = int(rng.integers(2, 7))
+    N = _min_depth(B, W) + int(rng.integers(0, 8))
+    return dict(S=1, B=B, N=N, W=W, Hq=G * Hkv, Hkv=Hkv, prefix=int(rng.integers(0, 1500)),
+                d=int(rng.choice([64, 128])), paged=bool(rng.integers(0, 2)),
+                block_size=int(rng.choice([4, 16])))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bf16_one_sequence_random_shapes(seed):
+    """Seeded random single-sequence shapes through the 128-row-tile plan: head groups 2 to
+    8, 1 to 4 KV heads, 65 to 256 nodes, prefixes from empty to 1,499 keys, both head dims,
+    contiguous or paged (block size 4 or 16), sharp scores."""
+    kw = _one_sequence_shape(4300 + seed)
+    w = wl.make("ragged", 4300 + seed, parts=("attn",), qk_std=1.0, tree="random",
+                **_small(**kw))
+    _check(w, f"one sequence, random shape {kw}")
+
+
 @pytest.mark.parametrize("tree", ["chain", "star"])
 def test_bf16_chain_and_star(tree):
     B = 200

@@ -174,6 +174,28 @@ def test_one_sequence_paged():
     _against_oracle(w, st)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_one_sequence_random_shapes(seed):
+    """Seeded random single-sequence bf16 shapes with more than 128 rows per KV head through
+    the fused step: against the four calls and the oracle."""
+    rng = np.random.default_rng(4400 + seed)
+    G = int(rng.choice([2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(128 // G + 1, 257))
+    W = int(rng.integers(2, 7))
+    n, cap, level = 0, 1, 1
+    while cap < B:  # the least depth limit that holds B nodes of at most W children each
+        level *= W
+        cap += level
+        n += 1
+    kw = dict(S=1, B=B, N=n + int(rng.integers(0, 8)), W=W, Hq=G * Hkv, Hkv=Hkv, prefix=int(rng.integers(0, 1200)),
+              d=int(rng.choice([64, 128])), V=8 * int(rng.integers(125, 750)))  # 16-byte rows
+    w = wl.make("ragged", 4400 + seed, tree="random", **kw)
+    st, err = _compare(w, f"one sequence {kw}")
+    assert int(err.abs().sum()) == 0
+    _against_oracle(w, st)
+
+
 def test_flags_bad_parent_nan_bad_block():
     w = wl.make("ragged", 814, V=4096)
 
