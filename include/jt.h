@@ -125,9 +125,9 @@ jt_status jt_build_tree_mask(const int32_t *parent, int32_t S, int32_t B, uint64
  */
 /* block_size: the paged pool's block size, or 0 for a contiguous prefix.  The workspace
  * holds split-KV partial rows (and, for several sequences with more than 128 query rows
- * per KV head, the schedule that gives every workgroup an equal share of all sequences'
- * key tiles); its contents need no initialisation.  Calls that overlap on one workspace
- * race. */
+ * per KV head, where every workgroup takes an equal share of all sequences' key tiles,
+ * each unit's first and last share); its contents need no initialisation.  Calls that
+ * overlap on one workspace race. */
 size_t jt_tree_attention_workspace_size(int32_t S, int32_t B, int32_t Hq, int32_t Hkv,
                                         int32_t d, int32_t max_prefix, int32_t block_size,
                                         jt_dtype dtype);

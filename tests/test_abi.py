@@ -104,12 +104,12 @@ def test_host_validation_returns_before_launch():
 def test_workspace_queries_are_pure():
     assert jt.topw_workspace_size(16, 151936, 4, 1) > 0
     assert jt.verify_workspace_size(1, 16, 151936, 1) > 0
-    # several sequences take the balanced schedule: its table of tile offsets and a partial
+    # several sequences take the balanced schedule: a table of units' share ranges and a partial
     # slot per (unit + workgroup; 256 workgroups of 8 waves here), since prefix lengths are
     # known on the device only; one short sequence is split into chunks; fp32 needs none
     units, nwg, rows, d = 32 * 4 * 2, 256, 256, 128
     slots = (units + nwg) * rows
-    table = -(-33 * 4 // 256) * 256
+    table = -(-units * 8 // 256) * 256  # each unit's first and last share
     assert jt.tree_attention_workspace_size(32, 64, 32, 4, 128, 4096, 1) == \
         table + slots * 8 + slots * d * 2
     assert jt.tree_attention_workspace_size(1, 16, 32, 8, 128, 1024, 1) > 0

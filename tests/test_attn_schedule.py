@@ -5,15 +5,18 @@ into fixed chunks: the units' key tiles -- unit = (sequence, KV head, 256-row ti
 that order, each unit holding the tiles its rows can see -- form one run of T tiles, and
 workgroup w of n = min(nwg, T) takes tiles floor(w T / n) .. floor((w + 1) T / n) - 1.
 Every workgroup turns the device-side prefix lengths into tile offsets and finds the unit
-and tile its share starts at; it writes one partial per unit it meets into slot unit + w;
-the merge finds a unit's pieces from the same offsets (stored by workgroup 0).  This
-test restates that arithmetic in Python and checks the invariants the kernels rely on,
-over random shapes and prefix lengths:
+and tile its share starts at; it writes one partial per unit it meets into slot unit + w,
+and records itself as the unit's first share (its piece starts at the unit's first tile)
+or last share (its piece ends at the unit's last tile); the merge reads a unit's pieces
+from slots unit + first .. unit + last.  This test restates that arithmetic in Python and
+checks the invariants the kernels rely on, over random shapes and prefix lengths:
   * every (unit, tile) is covered by exactly one workgroup, and every share is nonempty;
   * the start (unit, tile) of each share is where the previous share ended;
   * partial slots unit + w are unique and inside the workspace (units + nwg slots);
-  * a unit's merge range [wf, wl] is exactly the workgroups that wrote a piece of it, and
-    a unit held by one workgroup is written as output, never as a partial;
+  * each unit's first and last share are recorded exactly once, the range between them is
+    exactly the workgroups that wrote a piece of it (the same range the tile offsets
+    give), and a unit held by one workgroup (first = last) is written as output, never as
+    a partial;
   * a paged share's block-table entries fit the staging area.
 """
 import random
@@ -80,6 +83,7 @@ def check(S, B, G, Hkv, Ps, max_prefix, block_size):
     tab, T, starts = schedule(S, B, G, Hkv, Ps, nwg, nrt)
     nw = min(nwg, T)
     covered, slots, finals, writers = {}, set(), set(), {}
+    first, last = {}, {}  # the shares each unit records
     per_seq = Hkv * nrt
     prev_end = (0, 0)
     for w in range(nwg):
@@ -100,6 +104,12 @@ def check(S, B, G, Hkv, Ps, max_prefix, block_size):
             for t in range(off, off + n):
                 assert (u, t) not in covered
                 covered[(u, t)] = w
+            if off == 0:
+                assert u not in first
+                first[u] = w
+            if off + n == tu:
+                assert u not in last
+                last[u] = w
             if off == 0 and n == tu:
                 finals.add(u)
             else:
@@ -123,6 +133,7 @@ def check(S, B, G, Hkv, Ps, max_prefix, block_size):
         A = tab[s] + g * ts + sum(unit_tiles(Ps[s], r2, rows_per_tile, B, G) for r2 in range(rt))
         tu = unit_tiles(Ps[s], rt, rows_per_tile, B, G)
         wf, wl = wg_of(A), wg_of(A + tu - 1)
+        assert (first[u], last[u]) == (wf, wl), (u, first[u], last[u], wf, wl)
         if wf == wl:
             assert u in finals and u not in writers
         else:

@@ -333,7 +333,7 @@ struct AttnPlan {
 struct AttnWs {
     float2 *ml;
     uint16_t *o;
-    int32_t *sched;  // balanced schedule: S + 1 tile offsets of the sequences (last: total)
+    int2 *ufl;  // balanced schedule: per unit, the first and last share that holds its tiles
 };
 
 // Sequences the balanced schedule handles (each attention workgroup keeps their tile
@@ -468,7 +468,8 @@ static size_t attn_ws_bytes(const AttnPlan &p, int S, int d)
     const size_t slots = attn_ws_slots(p);
     size_t head = 0;
     if (p.bal)
-        head = attn_align256(((size_t)S + 1) * sizeof(int32_t));
+        head = attn_align256((size_t)p.units * sizeof(int2));
+    (void)S;
     return head + slots * sizeof(float2) + slots * (size_t)d * 2;
 }
 
@@ -478,10 +479,11 @@ static AttnWs attn_ws_split(const AttnPlan &p, int S, void *ws)
     const size_t slots = attn_ws_slots(p);
     if (slots == 0 || !ws)
         return w;
+    (void)S;
     uint8_t *b = reinterpret_cast<uint8_t *>(ws);
     if (p.bal) {
-        w.sched = reinterpret_cast<int32_t *>(b);
-        b += attn_align256(((size_t)S + 1) * sizeof(int32_t));
+        w.ufl = reinterpret_cast<int2 *>(b);
+        b += attn_align256((size_t)p.units * sizeof(int2));
     }
     w.ml = reinterpret_cast<float2 *>(b);
     w.o = reinterpret_cast<uint16_t *>(b + slots * sizeof(float2));
@@ -589,7 +591,9 @@ template <int N> __device__ __forceinline__ void lgkm_wait8(i32x2_t (&r)[8])
 // `stride`.  Partial c of a row holds m_c (log2 domain), l_c and O_c / l_c in bf16; the
 // merged row is sum_c 2^(m_c - M) l_c (O_c/l_c) / sum_c 2^(m_c - M) l_c, M = max_c m_c.
 // NB chunks are loaded per round trip (the host picks NB >= the chunk count when it can).
-template <int D, int NB>
+// kBal: the balanced schedule (pl.bal), whose pass recorded each unit's first and last
+// share; a separate instantiation, so that the chunked merges keep their own code.
+template <int D, int NB, bool kBal = false>
 __device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPlan &pl, const AttnWs &w,
                                 int unit, int it, int stride)
 {
@@ -598,28 +602,19 @@ __device__ __forceinline__ void attn_merge_unit(const AttnArgs &a, const AttnPla
     const int sg = unit / pl.n_rtiles;
     const int s = sg / a.Hkv, g = sg % a.Hkv;
     const int G = a.G, B = a.B;
-    const int P = clamp_prefix(a, s);
-    const int v_hi = min(B - 1, (rt * pl.rt + pl.rt - 1) / G);
     // pieces: nk slots from `first`, one slot apart per piece, of which nact hold keys
     int nk = pl.n_chunks, nact = 0;
     int64_t first = (int64_t)unit * pl.n_chunks;
-    if (pl.bal) {
-        // the unit's tiles start at A (sequences' offsets, then KV heads, then row tiles)
-        // and go to workgroups wf .. wl of the equal shares of T tiles
-        const int64_t T = w.sched[a.S];
-        const int64_t nw = min((int64_t)pl.nwg, T);
-        const int ts = (w.sched[s + 1] - w.sched[s]) / a.Hkv;  // tiles of one KV head
-        int64_t A = w.sched[s] + (int64_t)g * ts;
-        for (int r2 = 0; r2 < rt; ++r2)
-            A += attn_unit_tiles(P, r2, pl.rt, B, G);
-        const int tu = attn_unit_tiles(P, rt, pl.rt, B, G);
-        auto wg_of = [&](int64_t x) { return (int)(((x + 1) * nw + T - 1) / T - 1); };
-        const int wf = wg_of(A), wl = wg_of(A + tu - 1);
-        if (wf == wl)
+    if constexpr (kBal) {
+        // shares wf .. wl held the unit's tiles; share x wrote its piece to slot unit + x
+        const int2 fl = w.ufl[unit];
+        if (fl.x == fl.y)
             return;  // one workgroup held the whole unit and wrote its output
-        nk = nact = wl - wf + 1;
-        first = (int64_t)unit + wf;
+        nk = nact = fl.y - fl.x + 1;
+        first = (int64_t)unit + fl.x;
     } else {
+        const int P = clamp_prefix(a, s);
+        const int v_hi = min(B - 1, (rt * pl.rt + pl.rt - 1) / G);
         nact = (P + v_hi + 1 + pl.ch - 1) / pl.ch;
     }
     for (; it < pl.rt * SPR; it += stride) {
@@ -1501,7 +1496,7 @@ __device__ __forceinline__ void attn_main(const AttnArgs &a, const AttnPlan &pl,
 // lengths (no launch of its own): per sequence its tile offset (each thread sums a run of
 // sequences; the runs' offsets come from a scan of the NT sums); the thread whose run
 // holds this workgroup's first tile then finds the unit and tile there (KV head and row
-// tile within the sequence).  Workgroup 0 also stores the offsets for the merge.  `tab`
+// tile within the sequence).  `tab`
 // (2 S + 3 + NT / 64 integers) lies in LDS that no copy has touched yet; the closing
 // barrier orders every read of it before the tile copies reuse that memory.  Returns the
 // total tile count T; u0 = -1 for an empty share (with fewer tiles than workgroups only the
@@ -1575,10 +1570,6 @@ __device__ __forceinline__ int64_t attn_bal_start(const AttnArgs &a, const AttnP
     if (tid == 0)
         tab[S] = total;
     __syncthreads();
-    // share 0, whichever workgroup runs it, stores the offsets for the merge
-    if (w == 0)
-        for (int s = tid; s <= S; s += NT)
-            ws.sched[s] = tab[s];
     u0 = a0 >= 0 ? found[0] : -1;
     off0 = a0 >= 0 ? found[1] : 0;
     __syncthreads();
@@ -1613,6 +1604,13 @@ __device__ __forceinline__ void attn_main_bal(const AttnArgs &a, const AttnPlan 
         first = false;
         attn_item<D, NWR, false>(a, pl, ws, s, g, rt, off * 64, (off + n) * 64, (int64_t)u + w,
                                  off == 0 && n == tu, off == 0 && g == 0 && rt == 0, false, lds);
+        if (threadIdx.x == 0) {
+            // the merge finds the unit's pieces from its first and last share
+            if (off == 0)
+                ws.ufl[u].x = w;
+            if (off + n == tu)
+                ws.ufl[u].y = w;
+        }
         left -= n;
         off = 0;
         ++u;
@@ -1641,7 +1639,7 @@ attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 }
 
 // Separate merge pass for large units: one thread per (unit, row, 8 output columns).
-template <int D, int NB>
+template <int D, int NB, bool kBal = false>
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
@@ -1657,7 +1655,7 @@ attn_combine_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
     const int unit = (int)(t / per_unit);
     if (unit >= pl.units)
         return;
-    attn_merge_unit<D, NB>(a, pl, ws, unit, (int)(t % per_unit), (int)per_unit);
+    attn_merge_unit<D, NB, kBal>(a, pl, ws, unit, (int)(t % per_unit), (int)per_unit);
 }
 
 // ------------------------------------------------------------------ host side --
@@ -1695,7 +1693,9 @@ static jt_status launch_mfma(const AttnArgs &a, void *ws, hipStream_t st)
     // 4, 9, 12 or 16 chunks per round trip only where that makes it a single trip; wider
     // batches cost more in registers (occupancy) and padded loads than the trips they save
     // (a batch of 12 for 9 chunks: 15.0 us per low_budget step against 14.75 with 9)
-    if (!p.bal && p.n_chunks <= 4)  // one sequence of many rows (128-row workgroups)
+    if (p.bal)
+        hipLaunchKernelGGL((attn_combine_kernel<D, 8, true>), cgrid, cblock, 0, st, a, p, w);
+    else if (!p.bal && p.n_chunks <= 4)  // one sequence of many rows (128-row workgroups)
         hipLaunchKernelGGL((attn_combine_kernel<D, 4>), cgrid, cblock, 0, st, a, p, w);
     else if (!p.bal && p.n_chunks == 9)
         hipLaunchKernelGGL((attn_combine_kernel<D, 9>), cgrid, cblock, 0, st, a, p, w);

@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(256) step_phase2_f32(StepArgs sa, StepPlan sp)
     attn_f32_block<D, true>(sa.attn, sa.anc, false, b % nvb, b / nvb);
 }
 
-template <int D, int NB>
+template <int D, int NB, bool kBal = false>
 __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
 {
     __shared__ __attribute__((aligned(16))) uint64_t mkeys[kStepRowsPerBlock][kMergeLds];
@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(256) step_phase2(StepArgs sa, StepPlan sp)
     const int64_t per_unit = (int64_t)attn_merge_rows(sp.ap, sa.attn.G, sa.attn.B) * (D / 8);
     const int unit = (int)(t / per_unit);
     if (unit < sp.ap.units)
-        attn_merge_unit<D, NB>(sa.attn, sp.ap, sa.aws, unit, (int)(t % per_unit), (int)per_unit);
+        attn_merge_unit<D, NB, kBal>(sa.attn, sp.ap, sa.aws, unit, (int)(t % per_unit), (int)per_unit);
 }
 
 // ------------------------------------------------------------------ host side --
@@ -371,7 +371,9 @@ static void launch_step_d(const StepArgs &sa, const StepPlan &sp, hipStream_t st
         hipLaunchKernelGGL((step_phase1_w4<D>), dim3(g1), dim3(256), 0, st, sa, sp);
     }
     const unsigned g2 = (unsigned)(sp.nC + sp.nR + sp.nW);
-    if (!sp.ap.bal && sp.ap.n_chunks <= 4)  // one sequence of many rows
+    if (sp.ap.bal)
+        hipLaunchKernelGGL((step_phase2<D, 8, true>), dim3(g2), dim3(256), 0, st, sa, sp);
+    else if (sp.ap.n_chunks <= 4)  // one sequence of many rows
         hipLaunchKernelGGL((step_phase2<D, 4>), dim3(g2), dim3(256), 0, st, sa, sp);
     else if (sp.ap.n_chunks == 9)  // 1024-key prefixes in two-tile chunks
         hipLaunchKernelGGL((step_phase2<D, 9>), dim3(g2), dim3(256), 0, st, sa, sp);
