@@ -1,6 +1,7 @@
 // The whole draft-and-verify step in two launches (jt_draft_verify_step); three for
-// shapes whose attention needs 8-wave workgroups (see step_scan_kernel).  An fp32 step
-// takes two launches with the attention in the second (see step_scan_f32_kernel).
+// several sequences of more than 128 rows per KV head, whose attention needs 8-wave
+// workgroups (see step_scan_kernel).  An fp32 step takes two launches with the attention
+// in the second (see step_scan_f32_kernel).
 //
 // Each launch runs several steps side by side, one role per range of workgroup ids:
 //   phase 1  attention   the split-KV MFMA pass; its workgroups build the tree's ancestor
@@ -125,10 +126,11 @@ __global__ void __launch_bounds__(256, 2) step_phase1_w4(StepArgs sa, StepPlan s
     step_phase1_body<D, 4>(sa, sp);
 }
 
-// Shapes whose attention needs 8-wave workgroups (128 KB of LDS each, one per CU) would
-// leave the scans one workgroup slot per CU if they shared its launch.  There the scans and
-// the mask run first in a launch of their own (small LDS, many workgroups per CU), then
-// the attention pass (reading the mask's rows), then phase 2.
+// Plans whose attention needs 8-wave workgroups (128 KB of LDS each, one per CU: the
+// balanced schedule of several sequences) would leave the scans one workgroup slot per CU
+// if they shared its launch.  There the scans and the mask run first in a launch of their
+// own (small LDS, many workgroups per CU), then the attention pass (reading the mask's
+// rows), then phase 2.
 constexpr int kScanLds = 4 * (kWaveCap + 2 * JT_MAX_W) * 8 > JT_MAX_NODES * 40
                              ? 4 * (kWaveCap + 2 * JT_MAX_W) * 8
                              : JT_MAX_NODES * 40;
