@@ -431,7 +431,8 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
 // head takes 4-wave workgroups over 128-row tiles, in chunks for about `w4` workgroups,
 // instead of the 8-wave pass.  Measured on high_budget (one box, two runs each, the
 // attention call alone): over inputs beyond the Infinity Cache 24.83 us with 8 waves and
-// 24.15 us with w4 = 256; over inputs it holds, 23.90 and 23.10 us.  The fused step runs
+// 24.15 us with w4 = 256; over inputs it holds, 23.90 and 23.10 us (and with w4 = 128,
+// 384 and 512: 34.3, 26.2 and 24.6 us against 24.1 us at 256).  The fused step runs
 // the same form in phase 1, beside its logit scans (one launch instead of two), with
 // w4 = 192: 47.2 us per step with the 8-wave pass, 39.7 us so (40.6 us at 256, 43.3 us
 // at 384).
