@@ -5,8 +5,9 @@ bit for bit.  Each case captures one call, then replays it several times with th
 program's own eager work (the four separate calls, or the stochastic verifier) and
 synchronisations in between.  Before each replay it overwrites every output, and it
 checks every replay.  The shapes cover the launch schedules of the step: two launches
-(4-wave attention), three (8-wave attention over one sequence, or over several that take
-the balanced schedule), and the fp32 step's two.
+(4-wave attention over one 64-row tile, or over 128-row tiles of one sequence with many
+rows), three (8-wave attention over several sequences, the balanced schedule), and the
+fp32 step's two.
 """
 import pytest
 import torch
@@ -63,7 +64,7 @@ def _replays_match(st, fn, outs, between, what):
 
 @pytest.mark.parametrize("name,kw", [
     ("low_budget", {}),                    # two launches
-    ("high_budget", dict(V=8192)),         # three: 8-wave attention
+    ("high_budget", dict(V=8192)),         # two: 128-row tiles beside the scans
     ("moe_verify", dict(V=8192)),          # three: balanced schedule over 32 sequences
     ("tiny", {}),                          # fp32: two launches, attention in the second
 ])

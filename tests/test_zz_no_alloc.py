@@ -2,7 +2,8 @@
 device scratch) against jt_draft_verify_step (the same step with a caller's workspace).
 
 Four calls in a row with shrinking inputs -- ragged at a reduced vocabulary (three
-launches, balanced schedule), high_budget (three launches), a small low_budget (two
+launches, balanced schedule), high_budget (two launches, 128-row attention tiles beside
+the scans), a small low_budget (two
 launches), then the fp32 tiny step -- so each call runs on scratch that holds the previous,
 larger call's contents.
 Every output must equal the workspace call's bit for bit.  The call goes through the C

@@ -1627,7 +1627,10 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR)  // 2 waves per SIMD: no AG
 attn_bf16_kernel(AttnArgs a, AttnPlan pl, AttnWs ws)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[AttnLds<D, NWR>::BYTES];
-    if constexpr (NWR == 8) {  // only 8-wave plans take the balanced schedule
+    // Only 8-wave plans take the balanced schedule, and the entry points plan 8-wave
+    // workgroups for nothing else (attn_plan_call turns an unbalanced 8-wave plan into
+    // 128-row 4-wave tiles): with 8 waves the entry points never reach the chunked pass below.
+    if constexpr (NWR == 8) {
         if (pl.bal) {
             // logical share w: XCD (blockIdx & 7) runs shares [x nwg/8, (x + 1) nwg/8)
             const int b = blockIdx.x;
