@@ -129,7 +129,7 @@ constexpr int kF32Rows = 16;
 // anc: the ancestor rows to read; validate: run the argument checks (they write a.err).
 // kPrefetch: issue the next tile's loads before the current tile is computed (measured:
 // the fused step's fp32 phase 2 gains, the standalone pass loses on the short runs it is
-// for -- tiny 11.2 us without, 12.9 us with; 64 more prefix keys, 27.1 against 30.3 us --
+// for -- tiny 11.2 us without, 12.9 us with; with a 300-key prefix 27.1 against 30.3 us --
 // and gains only on long ones, 136 against 130 us over 1,040 keys, so each takes its form).
 template <int D, bool kPrefetch>
 __device__ __forceinline__ void attn_f32_block(const AttnArgs &a, const uint64_t *anc, bool validate,
