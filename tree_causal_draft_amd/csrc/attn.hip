@@ -408,6 +408,8 @@ static AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int max_prefix, int blo
     // fewer, longer chunks cost less in the split-KV merge than they add to the pass
     // (measured on the 16-node, 1024-key shape: 17 one-tile chunks per unit 17.5 us,
     // 9 two-tile chunks 15.8 us), and they leave CUs to the logit scans of the fused step.
+    // Longer ones cost more than they save: with 6 three-tile chunks the low_budget step
+    // took 15.0 us and with 5 four-tile chunks 16.1 us, against 13.7 us with 9.
     const int target = w4_target > 0 ? w4_target : (p.nwr == 8 ? 256 : 128);
     int want = (target + p.units - 1) / p.units;
     if (want > maxc)
